@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of the Block AttnRes hot path on one MI355X.
+
+Default workload: the long-context prefill chunk, T = 262144 tokens, d = 7168,
+S = 9 bf16 sources (~34 GB resident in HBM).  One step = one layer of the hot
+path: ``attnres_accumulate`` adds the layer output into the current block's
+partial sum (read-modify-write), then ``attnres_aggregate`` reads the nine
+sources once and writes the residual and the depth weights.
+
+Prints one JSON line: tokens/s for the whole step, plus a ``roofline`` object
+for the dominant kernel (the aggregation: algorithmic bytes per launch over its
+average launch time, timed with HIP events on the stream it runs on) and a
+``cpu_baseline`` object (the float64 CPU oracle on a bounded token sample).
+
+Other workloads (``--workload``) are for measurement notes, not bench lines.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+METRIC = "Block AttnRes tokens/s and achieved HBM GB/s (% peak), d=7168, S=9, bf16"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
+COUNTERS_FILE = os.path.join(REPO, "profiles", "aggregate_prefill_t262144_counters.json")
+AGG_SOURCE = os.path.join(REPO, "depth_wise_attention_block_amd", "csrc", "aggregate.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="prefill_t262144",
+                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93"])
+    p.add_argument("--decode-T", type=int, default=64)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded oracle timing budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--with-copy", action="store_true",
+                   help="also run one plain copy of T*d bf16 per step outside the timed region "
+                        "(reference kernel for the HBM byte counters)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    with open(AGG_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per aggregation launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("aggregate_source_sha256") != source_digest():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float, seed: int):
+    """The oracle, as it is, on a bounded token sample of the same step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from depth_wise_attention_block_amd import synth
+    from oracle import attnres_oracle as orc
+
+    T = wl.T
+    rows = synth.token_sample(T, 4096, 0, seed=seed + 17)
+    chunk = 128
+    w = wl.w.float().cpu().numpy()
+    done, elapsed, k = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        while elapsed < budget_s and k * chunk < rows.numel():
+            idx = rows[k * chunk:(k + 1) * chunk].to(wl.out.device)
+            k += 1
+            H = wl.store.slots.index_select(1, idx).float().cpu().numpy()
+            F = wl.F.index_select(0, idx).float().cpu().numpy()
+            t0 = time.perf_counter()
+            H[8] = orc.accumulate(H[8], F, "bf16")
+            orc.depth_attention(H, w)
+            elapsed += time.perf_counter() - t0
+            done += idx.numel()
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} tokens of the same step (accumulate + 9-source aggregate), float64 NumPy, "
+                      f"one thread, {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path shards over "
+              "tokens with no communication, so N GPUs would each run this same single-GPU step.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from depth_wise_attention_block_amd import binding, workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    binding.lib()
+
+    t_setup = time.perf_counter()
+    if args.workload == "schedule_93":
+        wl = workloads.Schedule(32768, seed=args.seed, device=dev)
+        T = wl.T
+        step_bytes = wl.step_bytes()
+        cfg = {"workload": "schedule_93", "T": T, "d": wl.d, "layers": wl.layers, "block_size": wl.block_size,
+               "step": "93 x (aggregate + accumulate) + output-layer aggregate"}
+    else:
+        T = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
+        wl = workloads.LayerStep(T, seed=args.seed, device=dev)
+        step_bytes = wl.step_bytes()
+        cfg = {"workload": args.workload, "T": T, "d": wl.d, "S": 9,
+               "step": "accumulate (partial += layer output) + aggregate over 9 sources"}
+    copy_store = None
+    if args.with_copy and args.workload != "schedule_93":
+        copy_store = binding.SourceStore(T, wl.d, s_max=2, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"# setup {setup_s:.1f} s: workload {cfg['workload']} T={T}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    agg_events, acc_events = [], []
+
+    def one_step(timed: bool):
+        if args.workload == "schedule_93":
+            wl.step()
+            return
+        if copy_store is not None:
+            copy_store.reset()
+            copy_store.accumulate(wl.F)   # plain copy of T*d bf16 (first layer of a block)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if ev:
+            ev[0].record(stream)
+        wl.accumulate()
+        if ev:
+            ev[1].record(stream)
+        wl.aggregate()
+        if ev:
+            ev[2].record(stream)
+            acc_events.append((ev[0], ev[1]))
+            agg_events.append((ev[1], ev[2]))
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+
+    if copy_store is None:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            one_step(True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # the copy runs between timed launches: time the step's kernels only
+        wall = 0.0
+        for _ in range(args.steps):
+            one_step(True)
+        torch.cuda.synchronize()
+
+    detail = {"setup_s": round(setup_s, 1)}
+    if args.workload == "schedule_93":
+        ms_step = wall * 1e3 / args.steps
+        roof = {"bound": "hbm", "achieved": step_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "traffic": None, "kernel": "whole schedule (aggregate + accumulate launches)"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        detail["step_gb"] = step_bytes / 1e9
+    else:
+        agg_ms = sum(a.elapsed_time(b) for a, b in agg_events) / len(agg_events)
+        acc_ms = sum(a.elapsed_time(b) for a, b in acc_events) / len(acc_events)
+        if copy_store is not None:
+            ms_step = agg_ms + acc_ms
+        else:
+            ms_step = wall * 1e3 / args.steps
+        agg_bytes = wl.aggregate_bytes()
+        achieved = agg_bytes / (agg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(),
+                "kernel": "attnres aggregate_kernel<bf16, 2 vectors/lane>",
+                "bytes_per_launch": agg_bytes, "avg_launch_ms": round(agg_ms, 4)}
+        detail.update({"aggregate_ms": round(agg_ms, 4), "accumulate_ms": round(acc_ms, 4),
+                       "aggregate_tokens_per_s": round(T / (agg_ms * 1e-3)),
+                       "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1),
+                       "step_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)})
+
+    cpu = None
+    if not args.no_cpu_baseline and args.workload != "schedule_93":
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
+
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu, "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+"""ctypes binding of libattnres.so: argument marshalling only.
+
+Every entry point mirrors a C function of ``include/attnres.h`` and passes torch
+device pointers, sizes and the current HIP stream straight through.  All
+arithmetic happens in the library's HIP kernels; a missing library raises
+``RuntimeError`` -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattnres.so")
+
+BF16, F32 = 0, 1
+MAX_SOURCES = 9
+OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
+_DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+class AttnResError(RuntimeError):
+    """A libattnres call returned a negative status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func}: {strerror(status)} (status {status})")
+
+
+class attnres_store_t(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("T", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+                ("d", ctypes.c_int32), ("s_max", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_completed", ctypes.c_int32), ("partial_valid", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class attnres_launch_t(ctypes.Structure):
+    _fields_ = [("threads", ctypes.c_int32), ("vecs_per_lane", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("tokens_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_SIGNATURES = {
+    "attnres_version": (ctypes.c_int, []),
+    "attnres_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "attnres_aggregate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
+    "attnres_store_init": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
+    "attnres_store_sources": (ctypes.c_int, [ctypes.POINTER(attnres_store_t)]),
+    "attnres_accumulate": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p]),
+    "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.POINTER(attnres_launch_t)]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                       "`python -m depth_wise_attention_block_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().attnres_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().attnres_version())
+
+
+def _check(func: str, status: int) -> int:
+    if status < 0:
+        raise AttnResError(func, status)
+    return status
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32") from None
+
+
+def aggregate_config(S: int, T: int, d: int, dtype=torch.bfloat16, num_cus: int = 256) -> dict:
+    """Launch shape the library picks (host-side query, no GPU needed)."""
+    cfg = attnres_launch_t()
+    _check("attnres_aggregate_config",
+           lib().attnres_aggregate_config(S, T, d, _DTYPE_CODE[dtype], num_cus, ctypes.byref(cfg)))
+    return {"threads": cfg.threads, "vecs_per_lane": cfg.vecs_per_lane, "grid": cfg.grid,
+            "tokens_per_group": cfg.tokens_per_group}
+
+
+def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
+              weights: torch.Tensor | None = None, *, want_weights: bool = True, eps: float = 1e-5,
+              stream=None):
+    """``attnres_aggregate`` on ``sources`` ``[S, T, d]`` (rows contiguous; any
+    source stride), query ``w`` ``[d]`` float32.  Returns ``(out, weights)``;
+    ``weights`` is ``None`` when not wanted."""
+    if sources.dim() != 3:
+        raise ValueError("sources must be [S, T, d]")
+    S, T, d = sources.shape
+    if T > 0 and (sources.stride(2) != 1 or sources.stride(1) != d):
+        raise ValueError("each source must be a contiguous [T, d] block")
+    dev = sources.device
+    if out is None:
+        out = torch.empty((T, d), dtype=sources.dtype, device=dev)
+    if weights is None and want_weights:
+        weights = torch.empty((T, S), dtype=torch.float32, device=dev)
+    for name, t in (("w", w), ("out", out)) + ((("weights", weights),) if weights is not None else ()):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if w.dtype != torch.float32 or w.numel() != d:
+        raise ValueError("w must be float32 with d elements")
+    if out.dtype != sources.dtype or out.numel() != T * d:
+        raise ValueError("out must match the sources' dtype and hold T*d elements")
+    if weights is not None and (weights.dtype != torch.float32 or weights.numel() != T * S):
+        raise ValueError("weights must be float32 with T*S elements")
+    stride = sources.stride(0) if S > 1 else T * d
+    rc = lib().attnres_aggregate(sources.data_ptr(), S, T, d, stride, w.data_ptr(), out.data_ptr(),
+                                 weights.data_ptr() if weights is not None else None, float(eps),
+                                 _dtype_code(sources), _stream(dev, stream))
+    _check("attnres_aggregate", rc)
+    return out, weights
+
+
+class SourceStore:
+    """Device slots ``[s_max, T, d]`` plus the C store bookkeeping.
+
+    Slot 0 is h_0 (fill ``store.h0``); completed block representations and the
+    running partial sum follow.  ``sources()`` is the live ``[S, T, d]`` view the
+    next aggregation reads.
+    """
+
+    def __init__(self, T: int, d: int, *, s_max: int = MAX_SOURCES, dtype=torch.bfloat16,
+                 device="cuda", slots: torch.Tensor | None = None):
+        if slots is None:
+            slots = torch.empty((s_max, T, d), dtype=dtype, device=device)
+        if slots.shape != (s_max, T, d) or not slots.is_contiguous():
+            raise ValueError("slots must be a contiguous [s_max, T, d] tensor")
+        self.slots = slots
+        self.T, self.d, self.s_max = T, d, s_max
+        self._st = attnres_store_t()
+        _check("attnres_store_init",
+               lib().attnres_store_init(ctypes.byref(self._st), slots.data_ptr(), s_max, T, d, 0,
+                                        _dtype_code(slots)))
+
+    @property
+    def h0(self) -> torch.Tensor:
+        return self.slots[0]
+
+    @property
+    def n_completed(self) -> int:
+        return self._st.n_completed
+
+    @property
+    def partial_valid(self) -> bool:
+        return bool(self._st.partial_valid)
+
+    def num_sources(self) -> int:
+        return _check("attnres_store_sources", lib().attnres_store_sources(ctypes.byref(self._st)))
+
+    def sources(self) -> torch.Tensor:
+        return self.slots[: self.num_sources()]
+
+    def reset(self) -> None:
+        """Forget every block (h_0 stays)."""
+        self.set_state(0, False)
+
+    def set_state(self, n_completed: int, partial_valid: bool) -> None:
+        """Declare which slots hold data (for slots filled directly, e.g. with
+        synthetic block representations); checked by the library."""
+        old = (self._st.n_completed, self._st.partial_valid)
+        self._st.n_completed, self._st.partial_valid = int(n_completed), int(bool(partial_valid))
+        try:
+            _check("attnres_store_sources", lib().attnres_store_sources(ctypes.byref(self._st)))
+        except AttnResError:
+            self._st.n_completed, self._st.partial_valid = old
+            raise
+
+    def accumulate(self, layer_out: torch.Tensor, finalize_block: bool = False, stream=None) -> None:
+        if layer_out.dtype != self.slots.dtype or layer_out.device != self.slots.device \
+                or not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d:
+            raise ValueError("layer_out must be a contiguous [T, d] tensor like the store")
+        rc = lib().attnres_accumulate(ctypes.byref(self._st), layer_out.data_ptr(), int(bool(finalize_block)),
+                                      _stream(self.slots.device, stream))
+        _check("attnres_accumulate", rc)
+
+    def aggregate(self, w: torch.Tensor, out=None, weights=None, *, want_weights=True, eps=1e-5, stream=None):
+        return aggregate(self.sources(), w, out, weights, want_weights=want_weights, eps=eps, stream=stream)

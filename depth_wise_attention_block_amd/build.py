@@ -1,0 +1,57 @@
+"""Compile libattnres.so for gfx950 with hipcc (runs on a host without a GPU).
+
+``python -m depth_wise_attention_block_amd.build`` or ``build()``.  Always
+recompiles.  The library lands next to this file, where the binding loads it.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+REPO = os.path.dirname(HERE)
+LIB_NAME = "libattnres.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ("aggregate.hip", "accumulate.hip", "capi.cpp")
+ARCH = "gfx950"
+
+# -packed-fp32-ops: never emit packed fp32 arithmetic; the host pass warns that
+# it does not know the feature, which is harmless.
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP/C++ source into ``libattnres.so``; returns its path."""
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-shared", "-I", os.path.join(REPO, "include"),
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    log = "\n".join(l for l in proc.stdout.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{log}")
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

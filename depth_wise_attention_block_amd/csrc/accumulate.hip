@@ -1,0 +1,89 @@
+// Partial-sum update of the current block (kimi.papertok.ai ch. 4 §4.3 eq 10;
+// "Kimi K3技术详解系列（二）：AttnRes 与 Stable LatentMoE", §3): the block's
+// layer outputs are summed into one block representation; the sum so far
+// (up to the previous layer) is the partial source.
+//
+// partial <- round_bf16(f32(partial) + f32(layer_out)), one read-modify-write
+// pass (3 streams of T*d elements), or partial <- layer_out for the first layer
+// of a block (2 streams).  Closing a block moves no data: the slot simply
+// becomes the block representation (kimi.papertok.ai §4.6: produced once at
+// the boundary, then resident).  Element-wise and HBM-bound: 16-byte vectors,
+// several independent vectors per lane per trip to keep loads in flight.
+#include "internal.h"
+
+namespace attnres {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // independent 16-byte vectors per lane per trip
+
+__device__ __forceinline__ unsigned add_bf16x2(unsigned p, unsigned f) {
+  const float lo = __uint_as_float(p << 16) + __uint_as_float(f << 16);
+  const float hi = __uint_as_float(p & 0xFFFF0000u) + __uint_as_float(f & 0xFFFF0000u);
+  bf16x2 r = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+  return __builtin_bit_cast(unsigned, r);
+}
+
+template <bool kBf16, bool kCopy>
+__global__ void __launch_bounds__(kThreads)
+accumulate_kernel(u32x4* __restrict__ partial, const u32x4* __restrict__ layer_out, int64_t nvec) {
+  const int64_t chunk = (int64_t)kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * chunk; base < nvec; base += (int64_t)gridDim.x * chunk) {
+    u32x4 f[kUnroll], p[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < nvec) {
+        f[u] = __builtin_nontemporal_load(layer_out + i);
+        if constexpr (!kCopy) p[u] = __builtin_nontemporal_load(partial + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < nvec) {
+        u32x4 r;
+        if constexpr (kCopy) {
+          r = f[u];
+        } else if constexpr (kBf16) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) r[k] = add_bf16x2(p[u][k], f[u][k]);
+        } else {
+          const f32x4 s = __builtin_bit_cast(f32x4, p[u]) + __builtin_bit_cast(f32x4, f[u]);
+          r = __builtin_bit_cast(u32x4, s);
+        }
+        __builtin_nontemporal_store(r, partial + i);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream) {
+  const int64_t nvec = a.elems / (a.bf16 ? 8 : 4);
+  const int64_t chunk = (int64_t)kThreads * kUnroll;
+  int64_t grid = (nvec + chunk - 1) / chunk;
+  const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 16;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  u32x4* p = static_cast<u32x4*>(a.partial);
+  const u32x4* f = static_cast<const u32x4*>(a.layer_out);
+  if (a.copy) {
+    hipLaunchKernelGGL((accumulate_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       p, f, nvec);
+  } else if (a.bf16) {
+    hipLaunchKernelGGL((accumulate_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       p, f, nvec);
+  } else {
+    hipLaunchKernelGGL((accumulate_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       p, f, nvec);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attnres

@@ -1,0 +1,302 @@
+// Block AttnRes depth aggregation kernel for gfx950 (MI355X).
+//
+// For one token the method ("Kimi K3技术详解系列（二）：AttnRes 与 Stable
+// LatentMoE", §2; kimi.papertok.ai ch. 4 §4.2 eq 8-9) computes, over S <= 9
+// sources H_s:
+//     z_s = w . H_s / sqrt(mean(H_s^2) + eps),  a = softmax(z),  r = sum_s a_s H_s
+// Per source and token that is two reductions over d and one weighted sum --
+// about 2.7 flop per byte moved, far below the fp32 ridge point, so the kernel
+// is bound by HBM bandwidth and MFMA has nothing to do here.
+//
+// Design (one workgroup = one token at a time, grid-stride over tokens):
+//   * the workgroup's lanes split the d-vector into 16-byte pieces; each lane
+//     loads its V pieces of ALL S sources at once (S*V outstanding 16-byte
+//     loads per lane), so every source row is read from HBM exactly once and
+//     each workgroup keeps ~S*d*2 bytes in flight;
+//   * bf16 statistics use v_dot2_f32_bf16 on the packed pairs straight from
+//     memory: sum of squares as dot2(x, x), and w.x as dot2(x, w_hi) +
+//     dot2(x, w_lo) with the float32 query split into two bf16 halves once per
+//     workgroup -- no unpacking before the reductions;
+//   * 2*S wave sums by DPP (row butterfly, then row_bcast15/31), one LDS
+//     exchange across waves and ONE barrier per token (double-buffered LDS);
+//   * logits, max, exponentials and the normaliser are computed by lanes
+//     0..S-1 of each 16-lane row and broadcast with readlane; the softmax is
+//     exact here because all S scores are known before the weighted sum.  (The
+//     online-softmax merge of separately computed parts belongs to the
+//     two-phase schedule, not to this single pass.);
+//   * the weighted sum of the raw sources is formed in float32 registers and
+//     rounded once to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+#include <math.h>
+
+#include "internal.h"
+
+namespace attnres {
+namespace {
+
+constexpr int kMaxSrc = 9;  // ATTNRES_MAX_SOURCES
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- DPP helpers (GFX9 data-parallel primitives inside one wave) -----------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- 7-i in 8
+constexpr int kDppMirror = 0x140;     // row_mirror: lane i <- 15-i in 16
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15 -> next row
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31 -> rows 2,3
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, src),
+                                         kCtrl, kRowMask, 0xF, false));
+}
+
+// Every lane of each 16-lane row ends with that row's sum (bitwise equal
+// across the row: each step adds the same two operands in either order).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kDppXor1>(v, v);
+  v += dpp<kDppXor2>(v, v);
+  v += dpp<kDppHalfMirror>(v, v);
+  v += dpp<kDppMirror>(v, v);
+  return v;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v, v));
+  v = fmaxf(v, dpp<kDppXor2>(v, v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp<kDppMirror>(v, v));
+  return v;
+}
+
+// Sum over all 64 lanes, returned wave-uniform.  Fixed order: rows, then
+// row 0 + row 1 and row 2 + row 3, then the two halves.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += dpp<kDppBcast15, 0xA>(0.0f, v);  // rows 1,3 += lane 15 of the row below
+  v += dpp<kDppBcast31, 0xC>(0.0f, v);  // rows 2,3 += lane 31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Lane `lane` of every 16-lane row takes v; the other lanes keep old.
+__device__ __forceinline__ float put_lane(float v, int lane, float old, int s16) {
+  return s16 == lane ? v : old;
+}
+
+// ---- bf16 pair helpers -------------------------------------------------------
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  bf16x2 p = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+  return __builtin_bit_cast(unsigned, p);
+}
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// Per-lane slice of the pseudo-query.  bf16 sources: w = hi + lo, both bf16
+// pairs laid out like the source words (element 2i in the low half), so that
+// w.x = dot2(x, hi) + dot2(x, lo) keeps ~16 significant bits of w.
+template <bool kBf16, int kV>
+struct Query {
+  u32x4 hi[kV], lo[kV];  // bf16 path
+  f32x4 f[kV];           // f32 path
+};
+
+template <bool kBf16, int kV>
+__device__ __forceinline__ void load_query(Query<kBf16, kV>& q, const float* __restrict__ w, int nvec,
+                                           int tid, int nthr) {
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int idx = v * nthr + tid;
+    if constexpr (kBf16) {
+      q.hi[v] = u32x4{0, 0, 0, 0};
+      q.lo[v] = u32x4{0, 0, 0, 0};
+      if (idx < nvec) {
+        const f32x4* wp = reinterpret_cast<const f32x4*>(w) + 2 * (int64_t)idx;
+        const f32x4 a = wp[0], b = wp[1];
+        const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const __bf16 h0 = (__bf16)e[2 * k], h1 = (__bf16)e[2 * k + 1];
+          const __bf16 l0 = (__bf16)(e[2 * k] - (float)h0), l1 = (__bf16)(e[2 * k + 1] - (float)h1);
+          q.hi[v][k] = __builtin_bit_cast(unsigned, bf16x2{h0, h1});
+          q.lo[v][k] = __builtin_bit_cast(unsigned, bf16x2{l0, l1});
+        }
+      }
+    } else {
+      q.f[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (idx < nvec) q.f[v] = reinterpret_cast<const f32x4*>(w)[idx];
+    }
+  }
+}
+
+template <bool kBf16, int kV>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+aggregate_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
+                 const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
+                 float eps, float inv_d) {
+  // [buffer][wave][sum of squares | w.x][source]
+  __shared__ float red[2][kMaxWaves][2][16];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int s16 = lane & 15;  // source handled by this lane in the softmax step
+
+  Query<kBf16, kV> q;
+  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
+
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+    const u32x4* tok = src + t * (int64_t)nvec;
+
+    // 1. issue every load of this token: S sources x V vectors per lane
+    u32x4 x[kMaxSrc][kV];
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          const int idx = v * nthr + tid;
+          x[s][v] = u32x4{0, 0, 0, 0};
+          if (idx < nvec) x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
+        }
+      }
+    }
+
+    // 2. per-lane partial statistics, then wave sums
+    float gss = 0.f, gdt = 0.f;  // lane s of the row: source s's wave sums
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+        float ss = 0.f, dt = 0.f;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          if constexpr (kBf16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = dot2(x[s][v][k], x[s][v][k], ss);
+              dt = dot2(x[s][v][k], q.hi[v][k], dt);
+              dt = dot2(x[s][v][k], q.lo[v][k], dt);
+            }
+          } else {
+            const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = fmaf(xf[k], xf[k], ss);
+              dt = fmaf(xf[k], q.f[v][k], dt);
+            }
+          }
+        }
+        gss = put_lane(wave_sum(ss), s, gss, s16);
+        gdt = put_lane(wave_sum(dt), s, gdt, s16);
+      }
+    }
+
+    // 3. combine the waves: one LDS exchange, one barrier
+    if (lane < 16) {
+      red[buf][wave][0][lane] = gss;
+      red[buf][wave][1][lane] = gdt;
+    }
+    __syncthreads();
+
+    // 4. logits and softmax over depth, lanes s16 < S of every row
+    float z = -INFINITY;
+    if (s16 < S) {
+      float ss = 0.f, dt = 0.f;
+      for (int k = 0; k < nwaves; ++k) {
+        ss += red[buf][k][0][s16];
+        dt += red[buf][k][1][s16];
+      }
+      z = dt / sqrtf(ss * inv_d + eps);
+    }
+    const float m = row_max16(z);
+    const float p = (s16 < S) ? expf(z - m) : 0.f;
+    const float l = row_sum16(p);
+    const float a = p / l;
+    if (weights != nullptr && wave == 0 && lane < S) weights[t * S + lane] = a;
+
+    // 5. weighted sum of the raw sources in float32, one rounding to the output
+    float as[kMaxSrc];
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) as[s] = (s < S) ? lane_bcast(a, s) : 0.f;
+
+    u32x4* orow = out + t * (int64_t)nvec;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      if constexpr (kBf16) {
+        float acc[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = as[0] * bf16_lo(x[0][v][k]);
+          acc[2 * k + 1] = as[0] * bf16_hi(x[0][v][k]);
+        }
+#pragma unroll
+        for (int s = 1; s < kMaxSrc; ++s) {
+          if (s < S) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              acc[2 * k] = fmaf(as[s], bf16_lo(x[s][v][k]), acc[2 * k]);
+              acc[2 * k + 1] = fmaf(as[s], bf16_hi(x[s][v][k]), acc[2 * k + 1]);
+            }
+          }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
+        if (idx < nvec) __builtin_nontemporal_store(o, orow + idx);
+      } else {
+        f32x4 acc = as[0] * __builtin_bit_cast(f32x4, x[0][v]);
+#pragma unroll
+        for (int s = 1; s < kMaxSrc; ++s) {
+          if (s < S) {
+            const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = fmaf(as[s], xf[k], acc[k]);
+          }
+        }
+        if (idx < nvec) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, acc), orow + idx);
+      }
+    }
+  }
+}
+
+template <bool kBf16, int kV>
+hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
+  const int epv = kBf16 ? 8 : 4;
+  const int nvec = a.d / epv;
+  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                     static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / epv, a.w,
+                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream) {
+  switch ((a.bf16 ? 0 : 8) + a.vecs_per_lane) {
+    case 1: return launch<true, 1>(a, stream);
+    case 2: return launch<true, 2>(a, stream);
+    case 3: return launch<true, 3>(a, stream);
+    case 4: return launch<true, 4>(a, stream);
+    case 9: return launch<false, 1>(a, stream);
+    case 10: return launch<false, 2>(a, stream);
+    case 11: return launch<false, 3>(a, stream);
+    case 12: return launch<false, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attnres

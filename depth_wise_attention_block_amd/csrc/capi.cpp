@@ -1,0 +1,235 @@
+// C ABI of libattnres.so: host-side argument checks, launch-shape policy and
+// source-store bookkeeping.  Every check runs before any HIP call, so a
+// rejected call has no side effect at all (and the checks work without a GPU).
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attnres.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int elem_bytes(int32_t dtype) { return dtype == ATTNRES_BF16 ? 2 : 4; }
+int elems_per_vec(int32_t dtype) { return attnres::kVecBytes / elem_bytes(dtype); }
+bool known_dtype(int32_t dtype) { return dtype == ATTNRES_BF16 || dtype == ATTNRES_F32; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Shape checks shared by aggregate, its config query and the store.
+int check_shape(int64_t T, int32_t d, int32_t dtype) {
+  if (!known_dtype(dtype)) return ATTNRES_EUNSUPPORTED;
+  if (T < 0 || d <= 0) return ATTNRES_EINVAL;
+  if (d % elems_per_vec(dtype) != 0) return ATTNRES_EUNSUPPORTED;
+  if (d > (dtype == ATTNRES_BF16 ? ATTNRES_MAX_D_BF16 : ATTNRES_MAX_D_F32)) return ATTNRES_EUNSUPPORTED;
+  // keep every element offset far inside int64
+  if (T > (INT64_C(1) << 40) / d) return ATTNRES_EINVAL;
+  return ATTNRES_OK;
+}
+
+// Launch shape: each lane holds V 16-byte vectors of every source row; V is
+// the smallest value that keeps the workgroup within kMaxWaves waves.  One
+// token per workgroup per trip; the grid covers every token up to a cap, past
+// which workgroups loop over tokens.
+int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus, attnres_launch_t* cfg) {
+  const int nvec = d / elems_per_vec(dtype);
+  const int max_threads = 64 * attnres::kMaxWaves;
+  const int v = (nvec + max_threads - 1) / max_threads;
+  if (v < 1 || v > attnres::kMaxVecsPerLane) return ATTNRES_EUNSUPPORTED;
+  const int lanes = (nvec + v - 1) / v;
+  cfg->threads = (lanes + 63) / 64 * 64;
+  cfg->vecs_per_lane = v;
+  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 4096;
+  cfg->grid = T < cap ? T : cap;
+  cfg->tokens_per_group = 1;
+  cfg->reserved = 0;
+  (void)S;
+  return ATTNRES_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTNRES_ELAUNCH;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return ATTNRES_OK;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return ATTNRES_ELAUNCH;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return ATTNRES_OK;
+}
+
+int check_store(const attnres_store_t* st) {
+  if (st == nullptr) return ATTNRES_EINVAL;
+  int rc = check_shape(st->T, st->d, st->dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (st->base == nullptr) return ATTNRES_EINVAL;
+  if (!aligned16(st->base)) return ATTNRES_EUNSUPPORTED;
+  if (st->s_max < 2 || st->s_max > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  if (st->slot_stride < st->T * st->d) return ATTNRES_EINVAL;
+  if (st->slot_stride % elems_per_vec(st->dtype) != 0) return ATTNRES_EUNSUPPORTED;
+  if (st->slot_stride > (INT64_C(1) << 40)) return ATTNRES_EINVAL;
+  if (st->n_completed < 0 || (st->partial_valid != 0 && st->partial_valid != 1)) return ATTNRES_ESTATE;
+  if (1 + st->n_completed + st->partial_valid > st->s_max) return ATTNRES_ESTATE;
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ATTNRES_API int attnres_version(void) { return kVersion; }
+
+ATTNRES_API const char* attnres_strerror(int status) {
+  switch (status) {
+    case ATTNRES_OK: return "success";
+    case ATTNRES_EINVAL: return "invalid argument (count, size, null pointer or flag)";
+    case ATTNRES_EUNSUPPORTED: return "unsupported layout (alignment, vector multiple, hidden size or dtype)";
+    case ATTNRES_EALIAS: return "an output buffer overlaps an input buffer";
+    case ATTNRES_ELAUNCH: return "the HIP runtime refused the kernel launch";
+    case ATTNRES_ESTATE: return "source store full or inconsistent";
+    default: return "unknown status";
+  }
+}
+
+ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus,
+                                         attnres_launch_t* cfg) {
+  if (cfg == nullptr) return ATTNRES_EINVAL;
+  if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  const int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  return pick_config(S, T, d, dtype, num_cus, cfg);
+}
+
+ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
+                                  const float* w, void* out, float* weights, float eps, int32_t dtype,
+                                  void* stream) {
+  if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;
+  const int64_t row = T * (int64_t)d;
+  if (src_stride == 0) src_stride = row;
+  if (src_stride < 0 || src_stride > (INT64_C(1) << 40)) return ATTNRES_EINVAL;
+  if (S > 1 && src_stride < row) return ATTNRES_EINVAL;
+  if (src_stride % elems_per_vec(dtype) != 0) return ATTNRES_EUNSUPPORTED;
+  if (T == 0) return ATTNRES_OK;
+  if (sources == nullptr || w == nullptr || out == nullptr) return ATTNRES_EINVAL;
+  if (!aligned16(sources) || !aligned16(w) || !aligned16(out)) return ATTNRES_EUNSUPPORTED;
+  if (weights != nullptr && (reinterpret_cast<uintptr_t>(weights) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+
+  const int es = elem_bytes(dtype);
+  const Range r_src = range(sources, ((int64_t)(S - 1) * src_stride + row) * es);
+  const Range r_w = range(w, (int64_t)d * 4);
+  const Range r_out = range(out, row * es);
+  if (overlap(r_out, r_src) || overlap(r_out, r_w)) return ATTNRES_EALIAS;
+  if (weights != nullptr) {
+    const Range r_wt = range(weights, T * (int64_t)S * 4);
+    if (overlap(r_wt, r_src) || overlap(r_wt, r_w) || overlap(r_wt, r_out)) return ATTNRES_EALIAS;
+  }
+
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  attnres_launch_t cfg;
+  rc = pick_config(S, T, d, dtype, cus, &cfg);
+  if (rc != ATTNRES_OK) return rc;
+
+  attnres::AggregateArgs a;
+  a.sources = sources;
+  a.S = S;
+  a.T = T;
+  a.d = d;
+  a.src_stride = src_stride;
+  a.w = w;
+  a.out = out;
+  a.weights = weights;
+  a.eps = eps;
+  a.bf16 = dtype == ATTNRES_BF16;
+  a.threads = cfg.threads;
+  a.vecs_per_lane = cfg.vecs_per_lane;
+  a.grid = cfg.grid;
+  (void)hipGetLastError();  // start from a clean error state
+  return attnres::launch_aggregate(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                      : ATTNRES_ELAUNCH;
+}
+
+ATTNRES_API int attnres_store_init(attnres_store_t* st, void* base, int32_t s_max, int64_t T, int32_t d,
+                                   int64_t slot_stride, int32_t dtype) {
+  if (st == nullptr) return ATTNRES_EINVAL;
+  attnres_store_t s;
+  s.base = base;
+  s.T = T;
+  s.d = d;
+  s.slot_stride = slot_stride == 0 ? T * (int64_t)d : slot_stride;
+  s.s_max = s_max;
+  s.dtype = dtype;
+  s.n_completed = 0;
+  s.partial_valid = 0;
+  s.reserved = 0;
+  const int rc = check_store(&s);
+  if (rc != ATTNRES_OK) return rc;
+  *st = s;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_store_sources(const attnres_store_t* st) {
+  const int rc = check_store(st);
+  if (rc != ATTNRES_OK) return rc;
+  return 1 + st->n_completed + st->partial_valid;
+}
+
+ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
+                                   void* stream) {
+  int rc = check_store(st);
+  if (rc != ATTNRES_OK) return rc;
+  if (finalize_block != 0 && finalize_block != 1) return ATTNRES_EINVAL;
+  const int slot = 1 + st->n_completed;
+  if (slot >= st->s_max) return ATTNRES_ESTATE;
+  const int es = elem_bytes(st->dtype);
+  const int64_t row = st->T * (int64_t)st->d;
+  if (row > 0) {
+    if (layer_out == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(layer_out)) return ATTNRES_EUNSUPPORTED;
+    const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * es);
+    if (overlap(range(layer_out, row * es), r_store)) return ATTNRES_EALIAS;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != ATTNRES_OK) return rc;
+    attnres::AccumulateArgs a;
+    a.partial = static_cast<char*>(st->base) + (int64_t)slot * st->slot_stride * es;
+    a.layer_out = layer_out;
+    a.elems = row;
+    a.bf16 = st->dtype == ATTNRES_BF16;
+    a.copy = st->partial_valid == 0;
+    a.num_cus = cus;
+    (void)hipGetLastError();
+    if (attnres::launch_accumulate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
+  }
+  st->partial_valid = 1;
+  if (finalize_block) {
+    st->n_completed += 1;
+    st->partial_valid = 0;
+  }
+  return ATTNRES_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI layer (capi.cpp) and the HIP kernels.
+// Arguments reaching these launchers have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+// Bytes per load/store vector: every global access is a 16-byte vector.
+constexpr int kVecBytes = 16;
+// Most waves (64 lanes each) one aggregation workgroup uses.
+constexpr int kMaxWaves = 8;
+// Most 16-byte vectors of one source row a lane holds.
+constexpr int kMaxVecsPerLane = 4;
+
+struct AggregateArgs {
+  const void* sources;  // [S][T][d], source s at element offset s*src_stride
+  int S;
+  int64_t T;
+  int d;
+  int64_t src_stride;   // elements between sources
+  const float* w;       // [d]
+  void* out;            // [T][d]
+  float* weights;       // [T][S] or nullptr
+  float eps;
+  bool bf16;
+  int threads;          // multiple of 64, <= 64*kMaxWaves
+  int vecs_per_lane;    // 1..kMaxVecsPerLane
+  int64_t grid;
+};
+
+// Enqueue one aggregation; returns the hipError_t of the launch.
+hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream);
+
+struct AccumulateArgs {
+  void* partial;        // [T][d] slot, updated in place
+  const void* layer_out;// [T][d]
+  int64_t elems;        // T*d
+  bool bf16;
+  bool copy;            // true: partial = layer_out (first layer of a block)
+  int num_cus;
+};
+
+hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream);
+
+}  // namespace attnres

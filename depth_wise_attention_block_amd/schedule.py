@@ -1,0 +1,63 @@
+"""Per-layer depth schedule of a Block AttnRes stack (host bookkeeping only).
+
+kimi.papertok.ai ch. 4 §4.3 (eq 10) and §4.5: layers are grouped into blocks of
+``block_size``; layer i of block n aggregates over h_0, b_1..b_{n-1} and, from
+i = 2 on, the block's partial sum; after the layer its output is added to the
+partial, and the block's last layer closes it (§4.6: the representation is
+produced once at the boundary and then stays resident).  The output layer
+aggregates h_0 and every block representation (§4.3, last paragraph).
+
+Each step is one ``attnres_aggregate`` and one ``attnres_accumulate`` call;
+the only host work is deciding the finalize flag.
+"""
+
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence
+
+import torch
+
+from .binding import SourceStore, aggregate
+
+
+def closes_block(layer: int, num_layers: int, block_size: int) -> bool:
+    """True if 1-based ``layer`` is the last layer of its block."""
+    return layer % block_size == 0 or layer == num_layers
+
+
+def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], queries: Sequence[torch.Tensor],
+                 block_size: int, *, out: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
+                 final_query: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
+                 final_weights: Optional[torch.Tensor] = None,
+                 on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
+                 eps: float = 1e-5) -> None:
+    """Run every layer's aggregate + accumulate on the store's stream order.
+
+    ``store`` must hold h_0 in slot 0 and no blocks yet.  ``out`` is either one
+    ``[T, d]`` buffer reused by every layer or ``[L, T, d]``; ``weights``
+    likewise ``[T, 9]`` (only the first S_l columns' worth is written, as a
+    ``[T, S_l]`` block) or ``[L, T, 9]``.  ``on_layer(l, r_l, a_l)`` runs after
+    layer l's aggregation is enqueued (1-based l), before its accumulate.
+    """
+    num_layers = len(layer_outputs)
+    if len(queries) != num_layers:
+        raise ValueError("one query per layer")
+    if store.n_completed != 0 or store.partial_valid:
+        raise ValueError("store must start with only h_0 live")
+    T, d = store.T, store.d
+    if out is None:
+        out = torch.empty((T, d), dtype=store.slots.dtype, device=store.slots.device)
+    for l in range(1, num_layers + 1):
+        S = store.num_sources()
+        r = out[l - 1] if out.dim() == 3 else out
+        a = None
+        if weights is not None:
+            wbuf = weights[l - 1] if weights.dim() == 3 else weights
+            a = wbuf.view(-1)[: T * S].view(T, S)
+        aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+        if on_layer is not None:
+            on_layer(l, r, a)
+        store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
+    if final_query is not None:
+        return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
+    return None

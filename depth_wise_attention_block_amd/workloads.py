@@ -1,0 +1,102 @@
+"""Synthetic workloads and their steps, shared by the bench and the parity tests
+so both time and check exactly the same launches.
+
+* ``LayerStep``: one layer of the hot path at S = 9 -- the store holds h_0,
+  seven completed block representations and the current block's partial sum
+  (K3's last block: kimi.papertok.ai ch. 4 §4.5); a step adds the layer's
+  output into the partial (``attnres_accumulate``, read-modify-write) and then
+  aggregates the nine sources (``attnres_aggregate``).  Used at T = 4096
+  (single layer), T in {1, 8, 64, 256} (decode batches) and T = 262144
+  (long-context prefill chunk).
+* ``Schedule``: the whole 93-layer depth path at one batch of tokens -- every
+  layer's aggregate + accumulate with block closing every 12 layers, then the
+  output layer's aggregate over h_0 and the 8 block representations.
+
+Inputs come from :mod:`.synth` (seeded, generated on the device).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import synth
+from .binding import MAX_SOURCES, SourceStore
+from .schedule import closes_block, run_schedule
+
+
+class LayerStep:
+    def __init__(self, T: int, d: int = 7168, *, seed: int = 0, device="cuda", scale=(0.5, 50.0),
+                 layer_out_std: float = 1.0):
+        self.T, self.d = T, d
+        self.store = SourceStore(T, d, s_max=MAX_SOURCES, dtype=torch.bfloat16, device=device)
+        synth.sources(MAX_SOURCES, T, d, scale=scale, seed=seed, out=self.store.slots)
+        self.store.set_state(MAX_SOURCES - 2, True)   # h0, b1..b7, partial
+        self.F = synth.layer_output(T, d, std=layer_out_std, seed=seed, tag=1, device=device)
+        self.w = synth.query(d, seed=seed, device=device)
+        self.out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
+        self.weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
+
+    def accumulate(self):
+        self.store.accumulate(self.F, finalize_block=False)
+
+    def aggregate(self):
+        self.store.aggregate(self.w, self.out, self.weights)
+
+    def step(self):
+        self.accumulate()
+        self.aggregate()
+
+    # Algorithmic HBM bytes (each stream read or written once).
+    def aggregate_bytes(self) -> int:
+        S, T, d = MAX_SOURCES, self.T, self.d
+        return T * (2 * S * d + 2 * d + 4 * S) + 4 * d
+
+    def accumulate_bytes(self) -> int:
+        return 3 * 2 * self.T * self.d
+
+    def step_bytes(self) -> int:
+        return self.aggregate_bytes() + self.accumulate_bytes()
+
+
+class Schedule:
+    def __init__(self, T: int, d: int = 7168, *, layers: int = 93, block_size: int = 12, seed: int = 0,
+                 device="cuda", h0_scale: float = 1.0, layer_out_std: float = 0.1):
+        self.T, self.d, self.layers, self.block_size = T, d, layers, block_size
+        self.store = SourceStore(T, d, s_max=MAX_SOURCES, dtype=torch.bfloat16, device=device)
+        synth.fill_normal_(self.store.h0, h0_scale, seed=seed, tag=1)
+        self.F = [synth.layer_output(T, d, std=layer_out_std, seed=seed, tag=l, device=device)
+                  for l in range(layers)]
+        self.W = [synth.query(d, seed=seed, device=device, tag=l) for l in range(layers)]
+        self.w_out = synth.query(d, seed=seed, device=device, tag=10_000)
+        self.out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
+        self.weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
+        self.final_out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
+        self.final_weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
+
+    def step(self, on_layer=None):
+        self.store.reset()
+        run_schedule(self.store, self.F, self.W, self.block_size, out=self.out, weights=self.weights,
+                     final_query=self.w_out, final_out=self.final_out, final_weights=self.final_weights,
+                     on_layer=on_layer)
+
+    def source_counts(self):
+        """S of every layer, then of the output layer."""
+        counts, n_done, partial = [], 0, False
+        for l in range(1, self.layers + 1):
+            counts.append(1 + n_done + int(partial))
+            partial = True
+            if closes_block(l, self.layers, self.block_size):
+                n_done, partial = n_done + 1, False
+        return counts + [1 + n_done]
+
+    def step_bytes(self) -> int:
+        """Algorithmic bytes of one full pass: every aggregate, every accumulate
+        (copy for a block's first layer, read-modify-write otherwise)."""
+        T, d = self.T, self.d
+        total = 0
+        for S in self.source_counts():
+            total += T * (2 * S * d + 2 * d + 4 * S) + 4 * d
+        for l in range(1, self.layers + 1):
+            first = (l - 1) % self.block_size == 0
+            total += (2 if first else 3) * 2 * T * d
+        return total

@@ -1,0 +1,177 @@
+/*
+ * attnres.h -- C ABI of libattnres.so: Block Attention-Residuals (Block AttnRes)
+ * depth aggregation for AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages cited by title and section):
+ *   - "Kimi K3技术详解系列（二）：AttnRes 与 Stable LatentMoE", §2: a layer's
+ *     residual is a softmax-weighted sum over depth sources, scored by a learned
+ *     per-layer pseudo-query against RMS-normalised sources; §3: Block AttnRes
+ *     keeps the embedding, one summary per completed block and the current
+ *     block's partial sum.
+ *   - kimi.papertok.ai tutorial, ch. 4 "Attention Residuals", §4.2 (eq 8-9:
+ *     phi(q,k) = exp(q^T RMSNorm(k)), no temperature), §4.3 (eq 10: block
+ *     representations and the partial sum; no partial entry for the first
+ *     layer of a block), §4.6 (a block representation is produced once at the
+ *     block boundary and then stays resident).
+ *   - "Kimi K3 模型结构（6）：输入端与零件", loose model facts: RMSNorm eps 1e-5.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are device memory on the current HIP device;
+ *     the caller allocates and frees all of it.  The library never allocates,
+ *     frees or synchronises, and keeps no pointer after a call returns.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; buffers must stay alive until it ends.
+ *   - Return value: ATTNRES_OK or a negative status.  All argument checks run
+ *     on the host before anything is enqueued; a failed check enqueues nothing
+ *     and makes no HIP call.  Nothing is thrown across the ABI.
+ *   - Element layout is row-major; bf16 is IEEE binary32's top 16 bits.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNRES_API __attribute__((visibility("default")))
+
+/* Most sources one aggregation takes: embedding + 8 block representations,
+ * or embedding + 7 + the partial sum (kimi.papertok.ai ch. 4 §4.5). */
+#define ATTNRES_MAX_SOURCES 9
+/* Largest hidden size: 4 vectors of 16 bytes per lane, 512 lanes per token. */
+#define ATTNRES_MAX_D_BF16 16384
+#define ATTNRES_MAX_D_F32 8192
+
+typedef enum { ATTNRES_BF16 = 0, ATTNRES_F32 = 1 } attnres_dtype;
+
+enum {
+  ATTNRES_OK = 0,
+  ATTNRES_EINVAL = -1,       /* bad count, size, null pointer or flag        */
+  ATTNRES_EUNSUPPORTED = -2, /* misaligned pointer/stride, d not a multiple of
+                                the 16-byte vector, d above the maximum, or an
+                                unknown dtype                                 */
+  ATTNRES_EALIAS = -3,       /* an output overlaps an input                   */
+  ATTNRES_ELAUNCH = -4,      /* the HIP runtime refused a launch              */
+  ATTNRES_ESTATE = -5        /* source store full or its fields inconsistent  */
+};
+
+/* Library version, major*10000 + minor*100 + patch. */
+ATTNRES_API int attnres_version(void);
+
+/* Static text for a status code (never NULL). */
+ATTNRES_API const char* attnres_strerror(int status);
+
+/*
+ * attnres_aggregate -- one depth aggregation for T tokens.
+ *
+ * For every token t:  k_s = H_s[t] / sqrt(mean_j H_s[t][j]^2 + eps)
+ *                     z_s = w . k_s,    a_s = exp(z_s) / sum_s' exp(z_s')
+ *                     out[t] = sum_s a_s H_s[t]          (raw sources as values)
+ * ("Kimi K3技术详解系列（二）" §2 and its listing; kimi.papertok.ai §4.2 eq 8-9;
+ * llm-atlas.k1412.top/k3 card 07.)  Each source row is read from HBM once;
+ * sums, softmax and the weighted sum are formed in float32.
+ *
+ *   sources     device, [S][T][d] of dtype, source-major: source s, token t
+ *               starts at element s*src_stride + t*d.  16-byte aligned.
+ *   S           number of sources, 1..ATTNRES_MAX_SOURCES.
+ *   T           tokens, >= 0.  T == 0 returns ATTNRES_OK with nothing enqueued.
+ *   d           hidden size: a multiple of 8 (bf16) or 4 (f32), at most
+ *               ATTNRES_MAX_D_BF16 / ATTNRES_MAX_D_F32.
+ *   src_stride  elements between consecutive sources; 0 means T*d.  Must be a
+ *               multiple of the 16-byte vector and >= T*d when S > 1.
+ *   w           device, [d] float32 pseudo-query of the layer.
+ *   out         device, [T][d] of dtype (bf16 rounded to nearest even).
+ *   weights     device, [T][S] float32 depth weights, or NULL to skip them.
+ *   eps         RMSNorm epsilon (the model uses 1e-5); finite and >= 0.
+ *   dtype       ATTNRES_BF16 or ATTNRES_F32 (sources and out).
+ *   stream      hipStream_t.
+ * out and weights must not overlap sources, w or each other (ATTNRES_EALIAS).
+ * Bitwise deterministic for a given device, shape and input.
+ */
+ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d,
+                                  int64_t src_stride, const float* w, void* out,
+                                  float* weights, float eps, int32_t dtype, void* stream);
+
+/*
+ * Source store: host-side bookkeeping for device slots [s_max][T][d].
+ * Slot 0 holds the embedding h_0 (written by the caller); slot n holds block
+ * representation b_n once block n is complete; slot 1 + n_completed holds the
+ * running partial sum of the current block when partial_valid is set
+ * ("Kimi K3技术详解系列（二）" §3 diagram order; kimi.papertok.ai §4.3 eq 10).
+ * The live sources of the next aggregation are slots
+ * [0, 1 + n_completed + partial_valid), contiguous at stride slot_stride.
+ */
+typedef struct attnres_store {
+  void* base;            /* device, slot 0; 16-byte aligned                  */
+  int64_t T;             /* tokens per slot                                  */
+  int64_t slot_stride;   /* elements between slots, >= T*d                   */
+  int32_t d;             /* hidden size                                      */
+  int32_t s_max;         /* slots allocated, 2..ATTNRES_MAX_SOURCES          */
+  int32_t dtype;         /* attnres_dtype                                    */
+  int32_t n_completed;   /* completed block representations b_1..b_n         */
+  int32_t partial_valid; /* 1 if slot 1 + n_completed holds a partial sum    */
+  int32_t reserved;      /* zero                                             */
+} attnres_store_t;
+
+/*
+ * attnres_store_init -- fill *st for caller-owned slots (host only, no HIP
+ * call).  slot_stride 0 means T*d.  Counters start at zero: only h_0 is live.
+ * Same size/alignment rules as attnres_aggregate; ATTNRES_EINVAL for s_max
+ * outside 2..ATTNRES_MAX_SOURCES.
+ */
+ATTNRES_API int attnres_store_init(attnres_store_t* st, void* base, int32_t s_max, int64_t T,
+                                   int32_t d, int64_t slot_stride, int32_t dtype);
+
+/* Number of live sources, 1 + n_completed + partial_valid, or a negative status
+ * if *st is inconsistent (host only). */
+ATTNRES_API int attnres_store_sources(const attnres_store_t* st);
+
+/*
+ * attnres_accumulate -- add one layer's output to the current block's partial
+ * sum, and optionally close the block (kimi.papertok.ai §4.3 eq 10 and §4.6;
+ * "Kimi K3技术详解系列（二）" §3).
+ *
+ *   slot = 1 + n_completed
+ *   partial_valid ? slot = round(f32(slot) + f32(layer_out))   (one pass, RMW)
+ *                 : slot = layer_out                           (first layer: copy)
+ *   partial_valid = 1
+ *   finalize_block: n_completed += 1, partial_valid = 0  -- the partial slot
+ *                   becomes b_n in place; no data moves.
+ * bf16: the sum is one float32 add rounded to bf16 (nearest even); f32: one
+ * float32 add.  Bit-exact.
+ *
+ *   st             store (host struct, updated on success only).
+ *   layer_out      device, [T][d] of st->dtype, 16-byte aligned; must not
+ *                  overlap the store's slots (ATTNRES_EALIAS).
+ *   finalize_block 0 or 1.
+ * ATTNRES_ESTATE if slot would be >= s_max.  T == 0 updates the bookkeeping
+ * and enqueues nothing.
+ */
+ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out,
+                                   int32_t finalize_block, void* stream);
+
+/* Launch shape the library picks for an aggregation (host only, no HIP call). */
+typedef struct attnres_launch {
+  int32_t threads;          /* threads per workgroup (multiple of 64)         */
+  int32_t vecs_per_lane;    /* 16-byte vectors of one source row per lane     */
+  int64_t grid;             /* workgroups                                     */
+  int32_t tokens_per_group; /* tokens a workgroup handles per loop trip       */
+  int32_t reserved;
+} attnres_launch_t;
+
+/*
+ * attnres_aggregate_config -- the launch attnres_aggregate would use for this
+ * shape on a device with num_cus compute units (host only).  Same argument
+ * checks as attnres_aggregate (without pointers).
+ */
+ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_t dtype,
+                                         int32_t num_cus, attnres_launch_t* cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

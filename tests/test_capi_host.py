@@ -1,0 +1,160 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol the
+header declares, and its host-side logic (argument checks, launch-shape policy,
+source-store state machine) behaves as documented.  No kernel is launched:
+every call here fails its checks before the first HIP call, or has T = 0."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from depth_wise_attention_block_amd import binding as B
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "attnres.h")
+
+# Fake, 16-byte aligned, non-overlapping device addresses: never dereferenced,
+# because every call below is rejected on the host (or has nothing to do).
+SRC, W, OUT, WTS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libattnres.so is not built; run python -m depth_wise_attention_block_amd.build")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"ATTNRES_API\s+[\w\s\*]+?\b(attnres_\w+)\s*\(", text)
+
+
+def test_header_symbols_are_exported(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(B._SIGNATURES)
+
+
+def test_version_and_strerror(lib):
+    assert B.version() == 10000
+    codes = [B.OK, B.EINVAL, B.EUNSUPPORTED, B.EALIAS, B.ELAUNCH, B.ESTATE]
+    texts = [B.strerror(c) for c in codes]
+    assert len(set(texts)) == len(codes)
+    assert B.strerror(-99) == "unknown status"
+
+
+def agg(S=9, T=4, d=7168, stride=0, src=SRC, w=W, out=OUT, wts=WTS, eps=1e-5, dtype=B.BF16):
+    return B.lib().attnres_aggregate(src, S, T, d, stride, w, out, wts, eps, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(S=0), B.EINVAL), (dict(S=10), B.EINVAL), (dict(S=-1), B.EINVAL),
+    (dict(T=-1), B.EINVAL), (dict(d=0), B.EINVAL),
+    (dict(d=7164), B.EUNSUPPORTED), (dict(d=6, dtype=B.F32), B.EUNSUPPORTED),
+    (dict(d=16392), B.EUNSUPPORTED), (dict(d=8196, dtype=B.F32), B.EUNSUPPORTED),
+    (dict(dtype=2), B.EUNSUPPORTED),
+    (dict(eps=float("nan")), B.EINVAL), (dict(eps=-1e-5), B.EINVAL), (dict(eps=float("inf")), B.EINVAL),
+    (dict(stride=4 * 7168 - 8), B.EINVAL), (dict(stride=-8), B.EINVAL), (dict(stride=4 * 7168 + 4), B.EUNSUPPORTED),
+    (dict(src=None), B.EINVAL), (dict(w=None), B.EINVAL), (dict(out=None), B.EINVAL),
+    (dict(src=SRC + 8), B.EUNSUPPORTED), (dict(w=W + 4), B.EUNSUPPORTED), (dict(out=OUT + 2), B.EUNSUPPORTED),
+    (dict(wts=WTS + 2), B.EUNSUPPORTED),
+    (dict(out=SRC + 16), B.EALIAS), (dict(out=SRC + 8 * 4 * 7168 * 2), B.EALIAS),
+    (dict(out=W - 16), B.EALIAS), (dict(wts=SRC + 64), B.EALIAS), (dict(wts=OUT + 4 * 7168 * 2 - 4), B.EALIAS),
+    (dict(wts=W + 16), B.EALIAS),
+])
+def test_aggregate_rejects_before_any_launch(lib, kwargs, status):
+    assert agg(**kwargs) == status
+
+
+def test_aggregate_empty_batch_is_ok_without_pointers(lib):
+    assert agg(T=0, src=None, w=None, out=None, wts=None) == B.OK
+    assert agg(T=0, S=0) == B.EINVAL  # shape checks still apply
+
+
+def test_last_source_end_is_the_alias_boundary(lib):
+    # sources end exactly where out begins: touching, not overlapping -> only the
+    # launch would remain, which needs a GPU; so check the neighbour byte instead
+    end = SRC + (8 * 4 * 7168 + 4 * 7168) * 2
+    assert agg(out=end - 16) == B.EALIAS
+
+
+@pytest.mark.parametrize("S,T,d,dtype,threads,vpl", [
+    (9, 262144, 7168, B.BF16, 448, 2),
+    (9, 4096, 7168, B.BF16, 448, 2),
+    (4, 64, 256, B.F32, 64, 1),
+    (9, 5, 264, B.BF16, 64, 1),
+    (9, 5, 7176, B.BF16, 512, 2),
+    (9, 5, 4096, B.BF16, 512, 1),
+    (9, 5, 7168, B.F32, 448, 4),
+    (1, 1, 16384, B.BF16, 512, 4),
+    (2, 3, 8, B.BF16, 64, 1),
+])
+def test_launch_shape_policy(lib, S, T, d, dtype, threads, vpl):
+    cfg = B.aggregate_config(S, T, d, {B.BF16: B.torch.bfloat16, B.F32: B.torch.float32}[dtype], 256)
+    assert cfg["threads"] == threads and cfg["vecs_per_lane"] == vpl
+    epv = 8 if dtype == B.BF16 else 4
+    assert cfg["threads"] * cfg["vecs_per_lane"] >= d // epv  # every vector has a lane
+    assert cfg["threads"] % 64 == 0 and cfg["threads"] <= 512
+    assert cfg["grid"] == min(T, 256 * 4096) and cfg["tokens_per_group"] == 1
+
+
+def test_launch_grid_caps_and_loops(lib):
+    cfg = B.aggregate_config(2, 5_000_000, 8, B.torch.bfloat16, 256)
+    assert cfg["grid"] == 256 * 4096
+
+
+def _store(T=0, d=8, s_max=9, base=SRC, stride=0, dtype=B.BF16):
+    st = B.attnres_store_t()
+    rc = B.lib().attnres_store_init(ctypes.byref(st), base, s_max, T, d, stride, dtype)
+    return rc, st
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(s_max=1), B.EINVAL), (dict(s_max=10), B.EINVAL), (dict(base=None), B.EINVAL),
+    (dict(base=SRC + 2), B.EUNSUPPORTED), (dict(d=12), B.EUNSUPPORTED), (dict(dtype=7), B.EUNSUPPORTED),
+    (dict(T=4, d=8, stride=24), B.EINVAL), (dict(T=4, d=8, stride=36), B.EUNSUPPORTED),
+])
+def test_store_init_checks(lib, kwargs, status):
+    assert _store(**kwargs)[0] == status
+
+
+def test_store_state_machine_follows_the_block_rule(lib):
+    """93 layers in blocks of 12 through the C bookkeeping (T = 0, so nothing is
+    enqueued): live-source counts before each layer, and the full store."""
+    rc, st = _store(T=0)
+    assert rc == B.OK
+    counts = []
+    for l in range(1, 94):
+        counts.append(B.lib().attnres_store_sources(ctypes.byref(st)))
+        finalize = l % 12 == 0 or l == 93
+        assert B.lib().attnres_accumulate(ctypes.byref(st), None, int(finalize), None) == B.OK
+    hist = {s: counts.count(s) for s in sorted(set(counts))}
+    assert counts[0] == 1 and hist == {1: 1, 2: 12, 3: 12, 4: 12, 5: 12, 6: 12, 7: 12, 8: 12, 9: 8}
+    assert st.n_completed == 8 and st.partial_valid == 0
+    assert B.lib().attnres_store_sources(ctypes.byref(st)) == 9
+    # no slot left for a ninth block
+    before = (st.n_completed, st.partial_valid)
+    assert B.lib().attnres_accumulate(ctypes.byref(st), None, 0, None) == B.ESTATE
+    assert (st.n_completed, st.partial_valid) == before
+
+
+def test_accumulate_argument_checks(lib):
+    rc, st = _store(T=4, d=8)
+    assert rc == B.OK
+    acc = lambda ptr, fin=0: B.lib().attnres_accumulate(ctypes.byref(st), ptr, fin, None)
+    assert acc(None) == B.EINVAL
+    assert acc(OUT, fin=2) == B.EINVAL
+    assert acc(OUT + 8) == B.EUNSUPPORTED
+    assert acc(SRC + 16) == B.EALIAS
+    assert acc(SRC + 9 * 4 * 8 * 2 - 16) == B.EALIAS
+    assert (st.n_completed, st.partial_valid) == (0, 0)
+    st.partial_valid = 3
+    assert acc(OUT) == B.ESTATE
+    st.partial_valid, st.n_completed = 1, 8
+    assert acc(OUT) == B.ESTATE
+    assert B.lib().attnres_accumulate(None, OUT, 0, None) == B.EINVAL
