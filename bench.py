@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded oracle timing budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-pattern-probe", action="store_true",
+                   help="skip the trivial-arithmetic probe of the same HBM access pattern")
     p.add_argument("--with-copy", action="store_true",
                    help="also run one plain copy of T*d bf16 per step outside the timed region "
                         "(reference kernel for the HBM byte counters)")
@@ -78,7 +80,8 @@ def cpu_baseline(wl, budget_s: float, seed: int):
     from oracle import attnres_oracle as orc
 
     T = wl.T
-    rows = synth.token_sample(T, 4096, 0, seed=seed + 17)
+    rows = synth.token_sample(T, 65536, 0, seed=seed + 17)
+    rows = rows[torch.randperm(rows.numel(), generator=torch.Generator().manual_seed(seed))]
     chunk = 128
     w = wl.w.float().cpu().numpy()
     done, elapsed, k = 0, 0.0, 0
@@ -99,6 +102,25 @@ def cpu_baseline(wl, budget_s: float, seed: int):
                       f"one thread, {elapsed:.1f} s"}
 
 
+def pattern_ceiling(T: int, d: int):
+    """Run the access-pattern probe (trivial arithmetic, same reads and writes)
+    in a child process; None if it is not built or fails."""
+    import subprocess
+
+    exe = os.path.join(REPO, "depth_wise_attention_block_amd", "pattern_bench")
+    if not os.path.exists(exe):
+        return None
+    try:
+        proc = subprocess.run([exe, str(T), str(d), "5"], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                              text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return None
+    if proc.returncode != 0:
+        print(f"# pattern probe failed: {proc.stderr.strip()}", file=sys.stderr)
+        return None
+    return json.loads(proc.stdout.strip().splitlines()[-1])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -106,6 +128,11 @@ def main():
               "tokens with no communication, so N GPUs would each run this same single-GPU step.",
               file=sys.stderr)
         sys.exit(2)
+
+    ceiling = None
+    if args.workload != "schedule_93" and not args.no_pattern_probe:
+        T_probe = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
+        ceiling = pattern_ceiling(T_probe, 7168)
 
     import torch
 
@@ -196,6 +223,10 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(),
                 "kernel": "attnres aggregate_kernel<bf16, 2 vectors/lane>",
                 "bytes_per_launch": agg_bytes, "avg_launch_ms": round(agg_ms, 4)}
+        if ceiling is not None:
+            roof["pattern_ceiling"] = ceiling["token_pattern_9r1w_gbps"]
+            roof["frac_of_pattern_ceiling"] = round(achieved / ceiling["token_pattern_9r1w_gbps"], 4)
+            detail["pattern_probe"] = ceiling
         detail.update({"aggregate_ms": round(agg_ms, 4), "accumulate_ms": round(acc_ms, 4),
                        "aggregate_tokens_per_s": round(T / (agg_ms * 1e-3)),
                        "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1),

@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 REPO = os.path.dirname(HERE)
 LIB_NAME = "libattnres.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+PATTERN_BENCH = os.path.join(HERE, "pattern_bench")
 SOURCES = ("aggregate.hip", "accumulate.hip", "capi.cpp")
 ARCH = "gfx950"
 
@@ -50,7 +51,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if verbose and log.strip():
         print(log)
     os.replace(tmp, LIB_PATH)
+    _compile([hipcc(), *HIP_FLAGS, *extra_flags, os.path.join(CSRC, "pattern_bench.hip")], PATTERN_BENCH, verbose)
     return LIB_PATH
+
+
+def _compile(cmd, target: str, verbose: bool) -> None:
+    tmp = target + f".tmp{os.getpid()}"
+    cmd = [*cmd, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    log = "\n".join(l for l in proc.stdout.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{log}")
+    os.replace(tmp, target)
 
 
 if __name__ == "__main__":

@@ -25,6 +25,7 @@ def test_accumulate_copy_then_add_is_bit_exact(dtype, T, d):
     store = B.SourceStore(T, d, s_max=3, dtype=_tdt(dtype), device=dev)
     F1 = synth.layer_output(T, d, std=3.0, seed=T, tag=1, dtype=dtype, device=dev)
     F2 = synth.layer_output(T, d, std=0.01, seed=T, tag=2, dtype=dtype, device=dev)
+    store.slots[2].fill_(7.0)                 # must stay untouched
     sentinel = store.slots[2].clone()
     store.accumulate(F1)                      # first layer of the block: copy
     torch.cuda.synchronize()
