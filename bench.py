@@ -3,14 +3,15 @@
 
 Default workload: the long-context prefill chunk, T = 262144 tokens, d = 7168,
 S = 9 bf16 sources (~34 GB resident in HBM).  One step = one layer of the hot
-path: ``attnres_accumulate`` adds the layer output into the current block's
-partial sum (read-modify-write), then ``attnres_aggregate`` reads the nine
-sources once and writes the residual and the depth weights.
+path: the previous layer's output is added into the current block's partial
+sum (read-modify-write) and the nine sources are aggregated into the residual
+and the depth weights -- one ``attnres_accumulate_aggregate`` launch (or, with
+``--unfused``, ``attnres_accumulate`` then ``attnres_aggregate``).
 
 Prints one JSON line: tokens/s for the whole step, plus a ``roofline`` object
-for the dominant kernel (the aggregation: algorithmic bytes per launch over its
-average launch time, timed with HIP events on the stream it runs on) and a
-``cpu_baseline`` object (the float64 CPU oracle on a bounded token sample).
+for the dominant kernel (algorithmic bytes per launch over its average launch
+time, timed with HIP events on the stream it runs on) and a ``cpu_baseline``
+object (the float64 CPU oracle on a bounded token sample of the same step).
 
 Other workloads (``--workload``) are for measurement notes, not bench lines.
 """
@@ -46,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pattern-probe", action="store_true",
                    help="skip the trivial-arithmetic probe of the same HBM access pattern")
+    p.add_argument("--unfused", action="store_true",
+                   help="time attnres_accumulate + attnres_aggregate as two launches instead of the fused one")
     p.add_argument("--with-copy", action="store_true",
                    help="also run one plain copy of T*d bf16 per step outside the timed region "
                         "(reference kernel for the HBM byte counters)")
@@ -57,17 +60,18 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per aggregation launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+def counter_traffic(kernel: str, T: int):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, if
+    it was taken on the current kernel source at this T; else None."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("aggregate_source_sha256") != source_digest():
+    if c.get("aggregate_source_sha256") != source_digest() or c.get("workload", {}).get("T") != T:
         return None
-    return c.get("traffic_bytes_per_launch")
+    k = c.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(wl, budget_s: float, seed: int):
@@ -144,32 +148,35 @@ def main():
     dev = torch.device("cuda:0")
     binding.lib()
 
+    fused = not args.unfused
     t_setup = time.perf_counter()
     if args.workload == "schedule_93":
         wl = workloads.Schedule(32768, seed=args.seed, device=dev)
         T = wl.T
-        step_bytes = wl.step_bytes()
+        step_bytes = wl.step_bytes(fused)
         cfg = {"workload": "schedule_93", "T": T, "d": wl.d, "layers": wl.layers, "block_size": wl.block_size,
-               "step": "93 x (aggregate + accumulate) + output-layer aggregate"}
+               "step": ("layer 1 aggregate + 93 fused (partial update + next aggregate) launches" if fused else
+                        "93 x (aggregate + partial update) + output-layer aggregate")}
     else:
         T = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
         wl = workloads.LayerStep(T, seed=args.seed, device=dev)
-        step_bytes = wl.step_bytes()
+        step_bytes = wl.step_bytes(fused)
         cfg = {"workload": args.workload, "T": T, "d": wl.d, "S": 9,
-               "step": "accumulate (partial += layer output) + aggregate over 9 sources"}
+               "step": ("one fused launch: partial += layer output, then aggregate over 9 sources" if fused else
+                        "attnres_accumulate (partial += layer output), then attnres_aggregate over 9 sources")}
     copy_store = None
     if args.with_copy and args.workload != "schedule_93":
         copy_store = binding.SourceStore(T, wl.d, s_max=2, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
-    print(f"# setup {setup_s:.1f} s: workload {cfg['workload']} T={T}", file=sys.stderr, flush=True)
+    print(f"# setup {setup_s:.1f} s: workload {cfg['workload']} T={T} fused={fused}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    agg_events, acc_events = [], []
+    dom_events, acc_events = [], []   # dominant kernel; stand-alone update (unfused only)
 
     def one_step(timed: bool):
         if args.workload == "schedule_93":
-            wl.step()
+            wl.step(fused=fused)
             return
         if copy_store is not None:
             copy_store.reset()
@@ -177,6 +184,12 @@ def main():
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
         if ev:
             ev[0].record(stream)
+        if fused:
+            wl.fused()
+            if ev:
+                ev[1].record(stream)
+                dom_events.append((ev[0], ev[1]))
+            return
         wl.accumulate()
         if ev:
             ev[1].record(stream)
@@ -184,53 +197,50 @@ def main():
         if ev:
             ev[2].record(stream)
             acc_events.append((ev[0], ev[1]))
-            agg_events.append((ev[1], ev[2]))
+            dom_events.append((ev[1], ev[2]))
 
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
 
-    if copy_store is None:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            one_step(True)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        # the copy runs between timed launches: time the step's kernels only
-        wall = 0.0
-        for _ in range(args.steps):
-            one_step(True)
-        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
 
-    detail = {"setup_s": round(setup_s, 1)}
+    detail = {"setup_s": round(setup_s, 1), "fused": fused}
     if args.workload == "schedule_93":
         ms_step = wall * 1e3 / args.steps
-        roof = {"bound": "hbm", "achieved": step_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "traffic": None, "kernel": "whole schedule (aggregate + accumulate launches)"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
+        achieved = step_bytes / (ms_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "kernel": "whole schedule (all launches of one pass)", "bytes_per_launch": step_bytes}
         detail["step_gb"] = step_bytes / 1e9
     else:
-        agg_ms = sum(a.elapsed_time(b) for a, b in agg_events) / len(agg_events)
-        acc_ms = sum(a.elapsed_time(b) for a, b in acc_events) / len(acc_events)
+        dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
         if copy_store is not None:
-            ms_step = agg_ms + acc_ms
+            # the copy sits between the timed launches: count the step's kernels only
+            ms_step = dom_ms + (sum(a.elapsed_time(b) for a, b in acc_events) / len(acc_events) if acc_events else 0)
         else:
             ms_step = wall * 1e3 / args.steps
-        agg_bytes = wl.aggregate_bytes()
-        achieved = agg_bytes / (agg_ms * 1e-3) / 1e9
+        dom_bytes = wl.fused_bytes() if fused else wl.aggregate_bytes()
+        kernel = "aggregate_kernel<true, 2, 2>" if fused else "aggregate_kernel<true, 2, 0>"
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(),
-                "kernel": "attnres aggregate_kernel<bf16, 2 vectors/lane>",
-                "bytes_per_launch": agg_bytes, "avg_launch_ms": round(agg_ms, 4)}
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(kernel, T),
+                "kernel": kernel, "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 4)}
         if ceiling is not None:
-            roof["pattern_ceiling"] = ceiling["token_pattern_9r1w_gbps"]
-            roof["frac_of_pattern_ceiling"] = round(achieved / ceiling["token_pattern_9r1w_gbps"], 4)
+            key = "fused_pattern_10r2w_gbps" if fused else "token_pattern_9r1w_gbps"
+            roof["pattern_ceiling"] = ceiling[key]
+            roof["frac_of_pattern_ceiling"] = round(achieved / ceiling[key], 4)
             detail["pattern_probe"] = ceiling
-        detail.update({"aggregate_ms": round(agg_ms, 4), "accumulate_ms": round(acc_ms, 4),
-                       "aggregate_tokens_per_s": round(T / (agg_ms * 1e-3)),
-                       "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1),
+        detail.update({"dominant_ms": round(dom_ms, 4), "dominant_tokens_per_s": round(T / (dom_ms * 1e-3)),
                        "step_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)})
+        if acc_events:
+            acc_ms = sum(a.elapsed_time(b) for a, b in acc_events) / len(acc_events)
+            detail.update({"accumulate_ms": round(acc_ms, 4),
+                           "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1)})
 
     cpu = None
     if not args.no_cpu_baseline and args.workload != "schedule_93":

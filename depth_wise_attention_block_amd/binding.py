@@ -54,6 +54,9 @@ _SIGNATURES = {
     "attnres_store_sources": (ctypes.c_int, [ctypes.POINTER(attnres_store_t)]),
     "attnres_accumulate": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_void_p]),
+    "attnres_accumulate_aggregate": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
+                                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                                    ctypes.c_void_p]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(attnres_launch_t)]),
 }
@@ -213,3 +216,31 @@ class SourceStore:
 
     def aggregate(self, w: torch.Tensor, out=None, weights=None, *, want_weights=True, eps=1e-5, stream=None):
         return aggregate(self.sources(), w, out, weights, want_weights=want_weights, eps=eps, stream=stream)
+
+    def accumulate_aggregate(self, layer_out: torch.Tensor, finalize_block: bool, w: torch.Tensor, out=None,
+                             weights=None, *, want_weights=True, eps=1e-5, stream=None):
+        """``attnres_accumulate_aggregate``: add ``layer_out`` into the current
+        block (closing it if asked), then aggregate the live sources with the
+        next layer's query ``w`` -- one kernel.  Returns ``(out, weights)``."""
+        if layer_out.dtype != self.slots.dtype or layer_out.device != self.slots.device \
+                or not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d:
+            raise ValueError("layer_out must be a contiguous [T, d] tensor like the store")
+        S = 1 + self.n_completed + (1 if finalize_block else 0) + (0 if finalize_block else 1)
+        dev = self.slots.device
+        if out is None:
+            out = torch.empty((self.T, self.d), dtype=self.slots.dtype, device=dev)
+        if weights is None and want_weights:
+            weights = torch.empty((self.T, S), dtype=torch.float32, device=dev)
+        if w.dtype != torch.float32 or w.numel() != self.d or w.device != dev or not w.is_contiguous():
+            raise ValueError("w must be a contiguous float32 [d] tensor on the store's device")
+        if out.dtype != self.slots.dtype or out.numel() != self.T * self.d or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [T, d] tensor of the store's dtype")
+        if weights is not None and (weights.dtype != torch.float32 or weights.numel() != self.T * S
+                                    or not weights.is_contiguous()):
+            raise ValueError("weights must be a contiguous float32 tensor with T*S elements")
+        rc = lib().attnres_accumulate_aggregate(ctypes.byref(self._st), layer_out.data_ptr(), int(bool(finalize_block)),
+                                                w.data_ptr(), out.data_ptr(),
+                                                weights.data_ptr() if weights is not None else None, float(eps),
+                                                _stream(dev, stream))
+        _check("attnres_accumulate_aggregate", rc)
+        return out, weights

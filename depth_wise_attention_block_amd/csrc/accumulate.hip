@@ -9,24 +9,14 @@
 // becomes the block representation (kimi.papertok.ai §4.6: produced once at
 // the boundary, then resident).  Element-wise and HBM-bound: 16-byte vectors,
 // several independent vectors per lane per trip to keep loads in flight.
+#include "device_common.h"
 #include "internal.h"
 
 namespace attnres {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;  // independent 16-byte vectors per lane per trip
-
-__device__ __forceinline__ unsigned add_bf16x2(unsigned p, unsigned f) {
-  const float lo = __uint_as_float(p << 16) + __uint_as_float(f << 16);
-  const float hi = __uint_as_float(p & 0xFFFF0000u) + __uint_as_float(f & 0xFFFF0000u);
-  bf16x2 r = {(__bf16)lo, (__bf16)hi};  // round to nearest even
-  return __builtin_bit_cast(unsigned, r);
-}
 
 template <bool kBf16, bool kCopy>
 __global__ void __launch_bounds__(kThreads)
@@ -46,17 +36,11 @@ accumulate_kernel(u32x4* __restrict__ partial, const u32x4* __restrict__ layer_o
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
       if (i < nvec) {
-        u32x4 r;
         if constexpr (kCopy) {
-          r = f[u];
-        } else if constexpr (kBf16) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) r[k] = add_bf16x2(p[u][k], f[u][k]);
+          __builtin_nontemporal_store(f[u], partial + i);
         } else {
-          const f32x4 s = __builtin_bit_cast(f32x4, p[u]) + __builtin_bit_cast(f32x4, f[u]);
-          r = __builtin_bit_cast(u32x4, s);
+          __builtin_nontemporal_store(add_rows(p[u], f[u], kBf16), partial + i);
         }
-        __builtin_nontemporal_store(r, partial + i);
       }
     }
   }

@@ -26,18 +26,24 @@
 //     two-phase schedule, not to this single pass.);
 //   * the weighted sum of the raw sources is formed in float32 registers and
 //     rounded once to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+//
+// Fused update (kUpdate != 0): the last source is the current block's slot
+// after this layer's output has been added to it (kimi.papertok.ai §4.3 eq 10:
+// the next layer attends over the partial sum up to the previous layer, or over
+// the block representation just closed).  The kernel reads the old slot row and
+// the layer output, forms the new slot row exactly as the stand-alone partial
+// update does, writes it back and uses it from registers -- one HBM pass less
+// than update-then-aggregate, bit-identical results.
 #include <math.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace attnres {
 namespace {
 
 constexpr int kMaxSrc = 9;  // ATTNRES_MAX_SOURCES
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr int kUpdateNone = 0, kUpdateCopy = 1, kUpdateAdd = 2;
 
 // ---- DPP helpers (GFX9 data-parallel primitives inside one wave) -----------
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -92,12 +98,6 @@ __device__ __forceinline__ float put_lane(float v, int lane, float old, int s16)
 
 // ---- bf16 pair helpers -------------------------------------------------------
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
-__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  bf16x2 p = {(__bf16)lo, (__bf16)hi};  // round to nearest even
-  return __builtin_bit_cast(unsigned, p);
-}
 __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
@@ -139,11 +139,16 @@ __device__ __forceinline__ void load_query(Query<kBf16, kV>& q, const float* __r
   }
 }
 
-template <bool kBf16, int kV>
-__global__ void __launch_bounds__(64 * kMaxWaves)
-aggregate_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
+// Waves per SIMD each instance is built for: two 7-wave workgroups per CU for
+// the d = 7168 shape (V = 2), i.e. at most 128 VGPRs; wider rows get fewer.
+template <int kV>
+constexpr int waves_per_simd() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
+
+template <bool kBf16, int kV, int kUpdate>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kV>())))
+aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
-                 float eps, float inv_d) {
+                 float eps, float inv_d, const u32x4* __restrict__ layer_out) {
   // [buffer][wave][sum of squares | w.x][source]
   __shared__ float red[2][kMaxWaves][2][16];
 
@@ -159,10 +164,13 @@ aggregate_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int6
 
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
-    const u32x4* tok = src + t * (int64_t)nvec;
+    u32x4* tok = src + t * (int64_t)nvec;
+    const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxSrc;  // the updated slot, if any
 
-    // 1. issue every load of this token: S sources x V vectors per lane
+    // 1. issue every load of this token: S sources x V vectors per lane (for
+    //    the updated slot: the layer output, and the old slot row when adding)
     u32x4 x[kMaxSrc][kV];
+    u32x4 f[kV];
 #pragma unroll
     for (int s = 0; s < kMaxSrc; ++s) {
       if (s < S) {
@@ -170,7 +178,33 @@ aggregate_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int6
         for (int v = 0; v < kV; ++v) {
           const int idx = v * nthr + tid;
           x[s][v] = u32x4{0, 0, 0, 0};
-          if (idx < nvec) x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
+          if (s == s_upd) {
+            if constexpr (kUpdate == kUpdateCopy) {
+              if (idx < nvec) x[s][v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
+            } else {
+              f[v] = u32x4{0, 0, 0, 0};
+              if (idx < nvec) {
+                f[v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
+                x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
+              }
+            }
+          } else if (idx < nvec) {
+            x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
+          }
+        }
+      }
+    }
+    if constexpr (kUpdate != kUpdateNone) {
+      // new slot row = old + layer output (or the layer output), written back
+#pragma unroll
+      for (int s = 0; s < kMaxSrc; ++s) {
+        if (s == s_upd) {
+#pragma unroll
+          for (int v = 0; v < kV; ++v) {
+            const int idx = v * nthr + tid;
+            if constexpr (kUpdate == kUpdateAdd) x[s][v] = add_rows(x[s][v], f[v], kBf16);
+            if (idx < nvec) __builtin_nontemporal_store(x[s][v], tok + s * src_stride_v + idx);
+          }
         }
       }
     }
@@ -273,28 +307,39 @@ aggregate_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int6
   }
 }
 
-template <bool kBf16, int kV>
+template <bool kBf16, int kV, int kUpdate>
 hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
   const int epv = kBf16 ? 8 : 4;
   const int nvec = a.d / epv;
-  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
-                     static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / epv, a.w,
-                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d);
+  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                     static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec, a.src_stride / epv, a.w,
+                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
+                     static_cast<const u32x4*>(a.layer_out));
   return hipGetLastError();
+}
+
+template <int kUpdate>
+hipError_t launch_v(const AggregateArgs& a, hipStream_t stream) {
+  switch ((a.bf16 ? 0 : 8) + a.vecs_per_lane) {
+    case 1: return launch<true, 1, kUpdate>(a, stream);
+    case 2: return launch<true, 2, kUpdate>(a, stream);
+    case 3: return launch<true, 3, kUpdate>(a, stream);
+    case 4: return launch<true, 4, kUpdate>(a, stream);
+    case 9: return launch<false, 1, kUpdate>(a, stream);
+    case 10: return launch<false, 2, kUpdate>(a, stream);
+    case 11: return launch<false, 3, kUpdate>(a, stream);
+    case 12: return launch<false, 4, kUpdate>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream) {
-  switch ((a.bf16 ? 0 : 8) + a.vecs_per_lane) {
-    case 1: return launch<true, 1>(a, stream);
-    case 2: return launch<true, 2>(a, stream);
-    case 3: return launch<true, 3>(a, stream);
-    case 4: return launch<true, 4>(a, stream);
-    case 9: return launch<false, 1>(a, stream);
-    case 10: return launch<false, 2>(a, stream);
-    case 11: return launch<false, 3>(a, stream);
-    case 12: return launch<false, 4>(a, stream);
+  switch (a.update) {
+    case AggregateArgs::kNoUpdate: return launch_v<kUpdateNone>(a, stream);
+    case AggregateArgs::kCopyUpdate: return launch_v<kUpdateCopy>(a, stream);
+    case AggregateArgs::kAddUpdate: return launch_v<kUpdateAdd>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

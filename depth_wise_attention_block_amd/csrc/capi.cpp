@@ -172,6 +172,68 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
                                                                                       : ATTNRES_ELAUNCH;
 }
 
+ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
+                                             const float* w, void* out, float* weights, float eps, void* stream) {
+  int rc = check_store(st);
+  if (rc != ATTNRES_OK) return rc;
+  if (finalize_block != 0 && finalize_block != 1) return ATTNRES_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;
+  const int slot = 1 + st->n_completed;
+  if (slot >= st->s_max) return ATTNRES_ESTATE;
+  // bookkeeping after the update; the updated slot is the last live source
+  const int n_after = st->n_completed + (finalize_block ? 1 : 0);
+  const int p_after = finalize_block ? 0 : 1;
+  const int S = 1 + n_after + p_after;
+  const int64_t T = st->T;
+  const int d = st->d;
+  const int64_t row = T * (int64_t)d;
+  if (row > 0) {
+    if (layer_out == nullptr || w == nullptr || out == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(layer_out) || !aligned16(w) || !aligned16(out)) return ATTNRES_EUNSUPPORTED;
+    if (weights != nullptr && (reinterpret_cast<uintptr_t>(weights) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    const int es = elem_bytes(st->dtype);
+    const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * es);
+    const Range r_f = range(layer_out, row * es);
+    const Range r_w = range(w, (int64_t)d * 4);
+    const Range r_out = range(out, row * es);
+    if (overlap(r_f, r_store) || overlap(r_out, r_store) || overlap(r_out, r_f) || overlap(r_out, r_w) ||
+        overlap(r_w, r_store))
+      return ATTNRES_EALIAS;
+    if (weights != nullptr) {
+      const Range r_wt = range(weights, T * (int64_t)S * 4);
+      if (overlap(r_wt, r_store) || overlap(r_wt, r_f) || overlap(r_wt, r_w) || overlap(r_wt, r_out))
+        return ATTNRES_EALIAS;
+    }
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != ATTNRES_OK) return rc;
+    attnres_launch_t cfg;
+    rc = pick_config(S, T, d, st->dtype, cus, &cfg);
+    if (rc != ATTNRES_OK) return rc;
+    attnres::AggregateArgs a;
+    a.sources = st->base;
+    a.S = S;
+    a.T = T;
+    a.d = d;
+    a.src_stride = st->slot_stride;
+    a.w = w;
+    a.out = out;
+    a.weights = weights;
+    a.eps = eps;
+    a.bf16 = st->dtype == ATTNRES_BF16;
+    a.threads = cfg.threads;
+    a.vecs_per_lane = cfg.vecs_per_lane;
+    a.grid = cfg.grid;
+    a.update = st->partial_valid ? attnres::AggregateArgs::kAddUpdate : attnres::AggregateArgs::kCopyUpdate;
+    a.layer_out = layer_out;
+    (void)hipGetLastError();
+    if (attnres::launch_aggregate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
+  }
+  st->n_completed = n_after;
+  st->partial_valid = p_after;
+  return ATTNRES_OK;
+}
+
 ATTNRES_API int attnres_store_init(attnres_store_t* st, void* base, int32_t s_max, int64_t T, int32_t d,
                                    int64_t slot_stride, int32_t dtype) {
   if (st == nullptr) return ATTNRES_EINVAL;

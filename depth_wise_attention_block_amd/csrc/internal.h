@@ -28,6 +28,11 @@ struct AggregateArgs {
   int threads;          // multiple of 64, <= 64*kMaxWaves
   int vecs_per_lane;    // 1..kMaxVecsPerLane
   int64_t grid;
+  // Fused partial-sum update of the last source (index S-1) before use:
+  // kCopyUpdate: slot = layer_out; kAddUpdate: slot = slot + layer_out.
+  enum Update { kNoUpdate = 0, kCopyUpdate = 1, kAddUpdate = 2 };
+  Update update = kNoUpdate;
+  const void* layer_out = nullptr;  // [T][d], with update only
 };
 
 // Enqueue one aggregation; returns the hipError_t of the launch.

@@ -54,6 +54,35 @@ token_pattern(const u32x4* __restrict__ src, int64_t T, int nvec, u32x4* __restr
   }
 }
 
+// The fused step's pattern: 8 source rows + the partial row + the layer-output
+// row in, the partial row written back in place and one output row out.
+__global__ void __launch_bounds__(kThreads)
+fused_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ layer_out, int64_t T, int nvec,
+              u32x4* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  u32x4 x[10][2];
+#pragma unroll
+  for (int s = 0; s < 10; ++s)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int idx = v * kThreads + threadIdx.x;
+      const u32x4* row = s < 9 ? src + (s * T + t) * nvec : layer_out + t * nvec;
+      x[s][v] = idx < nvec ? __builtin_nontemporal_load(row + idx) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int idx = v * kThreads + threadIdx.x;
+    const u32x4 p = x[8][v] ^ x[9][v];
+    u32x4 o = p;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o ^= x[s][v];
+    if (idx < nvec) {
+      __builtin_nontemporal_store(p, src + (8 * T + t) * nvec + idx);
+      __builtin_nontemporal_store(o, out + t * nvec + idx);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) stream_read(const u32x4* __restrict__ a, int64_t n, unsigned* sink) {
   unsigned acc = 0;
   for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 1024) {
@@ -87,10 +116,12 @@ int main(int argc, char** argv) {
   }
   const int nvec = (int)(d / 8);
   const int64_t src_vecs = 9 * T * nvec, out_vecs = T * nvec;
-  u32x4 *src = nullptr, *out = nullptr;
+  u32x4 *src = nullptr, *out = nullptr, *lout = nullptr;
   unsigned* sink = nullptr;
   CHECK(hipMalloc(&src, src_vecs * 16));
   CHECK(hipMalloc(&out, out_vecs * 16));
+  CHECK(hipMalloc(&lout, out_vecs * 16));
+  CHECK(hipMemset(lout, 2, out_vecs * 16));
   CHECK(hipMalloc(&sink, 64));
   CHECK(hipMemset(src, 1, src_vecs * 16));
   CHECK(hipMemset(out, 0, out_vecs * 16));
@@ -115,11 +146,14 @@ int main(int argc, char** argv) {
   const int64_t grid = (int64_t)cus * 64;
   const double mixed = gbps(10 * row, [&] { token_pattern<true><<<T, kThreads>>>(src, T, nvec, out, sink); });
   const double ronly = gbps(9 * row, [&] { token_pattern<false><<<T, kThreads>>>(src, T, nvec, out, sink); });
+  const double fused = gbps(12 * row, [&] { fused_pattern<<<T, kThreads>>>(src, lout, T, nvec, out); });
   const double rstream = gbps(9 * row, [&] { stream_read<<<grid, 256>>>(src, src_vecs, sink); });
   const double wstream = gbps(row, [&] { stream_write<<<grid, 256>>>(out, out_vecs); });
   std::printf("{\"T\": %lld, \"d\": %lld, \"reps\": %d, \"token_pattern_9r1w_gbps\": %.1f, "
-              "\"token_pattern_9r_gbps\": %.1f, \"stream_read_gbps\": %.1f, \"stream_write_gbps\": %.1f}\n",
-              (long long)T, (long long)d, reps, mixed, ronly, rstream, wstream);
+              "\"token_pattern_9r_gbps\": %.1f, \"fused_pattern_10r2w_gbps\": %.1f, \"stream_read_gbps\": %.1f, "
+              "\"stream_write_gbps\": %.1f}\n",
+              (long long)T, (long long)d, reps, mixed, ronly, fused, rstream, wstream);
+  CHECK(hipFree(lout));
   CHECK(hipFree(src));
   CHECK(hipFree(out));
   CHECK(hipFree(sink));

@@ -26,8 +26,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 AGG_SOURCE = os.path.join(HERE, "csrc", "aggregate.hip")
 
 COPY_KERNEL = "accumulate_kernel<true, true>"
-RMW_KERNEL = "accumulate_kernel<true, false>"
-AGG_KERNEL = "aggregate_kernel<true, 2>"
+
+
+def algorithmic_bytes(kernel: str, T: int, d: int, S: int):
+    """(read, write) bytes each kernel must move at S sources, bf16, or None."""
+    row = 2 * T * d
+    table = {
+        "aggregate_kernel<true, 2, 0>": (S * row + 4 * d, row + 4 * T * S),
+        "aggregate_kernel<true, 2, 1>": ((S - 1) * row + row + 4 * d, 2 * row + 4 * T * S),
+        "aggregate_kernel<true, 2, 2>": ((S - 1) * row + 2 * row + 4 * d, 2 * row + 4 * T * S),
+        "accumulate_kernel<true, false>": (2 * row, row),
+        "accumulate_kernel<true, true>": (row, row),
+    }
+    return table.get(kernel)
 
 
 def _short(name: str) -> str:
@@ -72,30 +83,32 @@ def counters_summary(fetch_csv: str, write_csv: str, T: int, d: int, S: int, cmd
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
     write = _per_kernel(write_csv, "WRITE_SIZE")
     kib = 1024.0
+    mean = lambda v: sum(v) / len(v)
     copy_bytes = 2 * T * d                       # the copy reads and writes T*d bf16
-    f_copy = sum(fetch[COPY_KERNEL]) / len(fetch[COPY_KERNEL]) * kib
-    w_copy = sum(write[COPY_KERNEL]) / len(write[COPY_KERNEL]) * kib
-    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
-    agg_f = sum(fetch[AGG_KERNEL]) / len(fetch[AGG_KERNEL]) * kib * f_scale
-    agg_w = sum(write[AGG_KERNEL]) / len(write[AGG_KERNEL]) * kib * w_scale
-    alg_read = 2 * S * T * d + 4 * d
-    alg_write = 2 * T * d + 4 * T * S
-    out = {
-        "kernel": AGG_KERNEL, "workload": {"T": T, "d": d, "S": S},
+    f_scale = copy_bytes / (mean(fetch[COPY_KERNEL]) * kib)
+    w_scale = copy_bytes / (mean(write[COPY_KERNEL]) * kib)
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if not name.startswith(("aggregate_kernel", "accumulate_kernel")):
+            continue
+        fb = mean(fetch[name]) * kib * f_scale
+        wb = mean(write[name]) * kib * w_scale
+        entry = {"fetch_kib_raw": mean(fetch[name]), "write_kib_raw": mean(write[name]),
+                 "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb,
+                 "launches": len(fetch[name])}
+        alg = algorithmic_bytes(name, T, d, S)
+        if alg is not None:
+            entry.update({"algorithmic_read_bytes": alg[0], "algorithmic_write_bytes": alg[1],
+                          "traffic_over_algorithmic": (fb + wb) / (alg[0] + alg[1])})
+        kernels[name] = entry
+    return {
+        "workload": {"T": T, "d": d, "S": S},
         "commands": {"FETCH_SIZE": cmd_fetch, "WRITE_SIZE": cmd_write},
-        "copy_calibration": {"bytes_moved_each_way": copy_bytes, "fetch_kib": f_copy / kib, "write_kib": w_copy / kib,
+        "copy_calibration": {"kernel": COPY_KERNEL, "bytes_moved_each_way": copy_bytes,
                              "fetch_scale": f_scale, "write_scale": w_scale},
-        "fetch_kib_per_launch_raw": agg_f / kib / f_scale, "write_kib_per_launch_raw": agg_w / kib / w_scale,
-        "fetch_bytes_per_launch": agg_f, "write_bytes_per_launch": agg_w,
-        "traffic_bytes_per_launch": agg_f + agg_w,
-        "algorithmic_read_bytes": alg_read, "algorithmic_write_bytes": alg_write,
-        "traffic_over_algorithmic": (agg_f + agg_w) / (alg_read + alg_write),
+        "kernels": kernels,
         "aggregate_source_sha256": hashlib.sha256(open(AGG_SOURCE, "rb").read()).hexdigest(),
     }
-    if RMW_KERNEL in fetch and RMW_KERNEL in write:
-        out["accumulate_rmw_bytes_per_launch"] = (sum(fetch[RMW_KERNEL]) / len(fetch[RMW_KERNEL]) * kib * f_scale
-                                                  + sum(write[RMW_KERNEL]) / len(write[RMW_KERNEL]) * kib * w_scale)
-    return out
 
 
 def main():

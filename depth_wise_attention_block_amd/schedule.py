@@ -30,34 +30,67 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                  final_query: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
                  final_weights: Optional[torch.Tensor] = None,
                  on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
-                 eps: float = 1e-5) -> None:
-    """Run every layer's aggregate + accumulate on the store's stream order.
+                 fused: bool = True, eps: float = 1e-5):
+    """Run every layer's aggregation and partial-sum update in stream order.
+
+    ``fused=True`` (default): layer 1 aggregates h_0 alone; every later layer l
+    is one ``attnres_accumulate_aggregate`` that adds F_{l-1} (closing its block
+    if it was the block's last layer) and aggregates with w_l; the output layer's
+    aggregation is fused with the last update the same way -- 1 + L launches.
+    ``fused=False``: separate ``attnres_aggregate`` and ``attnres_accumulate``
+    per layer -- 2L (+1) launches.  Both give bit-identical results.
 
     ``store`` must hold h_0 in slot 0 and no blocks yet.  ``out`` is either one
     ``[T, d]`` buffer reused by every layer or ``[L, T, d]``; ``weights``
-    likewise ``[T, 9]`` (only the first S_l columns' worth is written, as a
-    ``[T, S_l]`` block) or ``[L, T, 9]``.  ``on_layer(l, r_l, a_l)`` runs after
-    layer l's aggregation is enqueued (1-based l), before its accumulate.
+    likewise ``[T, 9]`` (each layer writes a ``[T, S_l]`` block at its start) or
+    ``[L, T, 9]``.  ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation
+    is enqueued (1-based l).  Returns the output layer's ``(out, weights)``
+    when ``final_query`` is given, else None.
     """
     num_layers = len(layer_outputs)
-    if len(queries) != num_layers:
-        raise ValueError("one query per layer")
+    if len(queries) != num_layers or num_layers == 0:
+        raise ValueError("one query per layer, at least one layer")
     if store.n_completed != 0 or store.partial_valid:
         raise ValueError("store must start with only h_0 live")
     T, d = store.T, store.d
     if out is None:
         out = torch.empty((T, d), dtype=store.slots.dtype, device=store.slots.device)
-    for l in range(1, num_layers + 1):
-        S = store.num_sources()
+
+    def buffers(l: int, S: int):
         r = out[l - 1] if out.dim() == 3 else out
         a = None
         if weights is not None:
             wbuf = weights[l - 1] if weights.dim() == 3 else weights
             a = wbuf.view(-1)[: T * S].view(T, S)
-        aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+        return r, a
+
+    def sources_after(l_done: int) -> int:
+        """Live sources once layer l_done's output has been added."""
+        closes = closes_block(l_done, num_layers, block_size)
+        return 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
+
+    if not fused:
+        for l in range(1, num_layers + 1):
+            r, a = buffers(l, store.num_sources())
+            aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+            if on_layer is not None:
+                on_layer(l, r, a)
+            store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
+        if final_query is not None:
+            return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
+        return None
+
+    r, a = buffers(1, store.num_sources())
+    aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
+    if on_layer is not None:
+        on_layer(1, r, a)
+    for l in range(2, num_layers + 1):
+        r, a = buffers(l, sources_after(l - 1))
+        store.accumulate_aggregate(layer_outputs[l - 2], closes_block(l - 1, num_layers, block_size),
+                                   queries[l - 1], r, a, want_weights=a is not None, eps=eps)
         if on_layer is not None:
             on_layer(l, r, a)
-        store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
     if final_query is not None:
-        return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
+        return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps)
+    store.accumulate(layer_outputs[-1], True)
     return None

@@ -3,14 +3,16 @@ so both time and check exactly the same launches.
 
 * ``LayerStep``: one layer of the hot path at S = 9 -- the store holds h_0,
   seven completed block representations and the current block's partial sum
-  (K3's last block: kimi.papertok.ai ch. 4 §4.5); a step adds the layer's
-  output into the partial (``attnres_accumulate``, read-modify-write) and then
-  aggregates the nine sources (``attnres_aggregate``).  Used at T = 4096
-  (single layer), T in {1, 8, 64, 256} (decode batches) and T = 262144
-  (long-context prefill chunk).
+  (K3's last block: kimi.papertok.ai ch. 4 §4.5); a step adds the previous
+  layer's output into the partial (read-modify-write) and aggregates the nine
+  sources -- one ``attnres_accumulate_aggregate`` launch, or (``fused=False``)
+  ``attnres_accumulate`` then ``attnres_aggregate``.  Used at T = 4096 (single
+  layer), T in {1, 8, 64, 256} (decode batches) and T = 262144 (long-context
+  prefill chunk).
 * ``Schedule``: the whole 93-layer depth path at one batch of tokens -- every
-  layer's aggregate + accumulate with block closing every 12 layers, then the
-  output layer's aggregate over h_0 and the 8 block representations.
+  layer's aggregation and partial-sum update with block closing every 12
+  layers, then the output layer's aggregation over h_0 and the 8 block
+  representations.
 
 Inputs come from :mod:`.synth` (seeded, generated on the device).
 """
@@ -42,9 +44,15 @@ class LayerStep:
     def aggregate(self):
         self.store.aggregate(self.w, self.out, self.weights)
 
-    def step(self):
-        self.accumulate()
-        self.aggregate()
+    def fused(self):
+        self.store.accumulate_aggregate(self.F, False, self.w, self.out, self.weights)
+
+    def step(self, fused: bool = True):
+        if fused:
+            self.fused()
+        else:
+            self.accumulate()
+            self.aggregate()
 
     # Algorithmic HBM bytes (each stream read or written once).
     def aggregate_bytes(self) -> int:
@@ -54,8 +62,14 @@ class LayerStep:
     def accumulate_bytes(self) -> int:
         return 3 * 2 * self.T * self.d
 
-    def step_bytes(self) -> int:
-        return self.aggregate_bytes() + self.accumulate_bytes()
+    def fused_bytes(self) -> int:
+        """One fused launch: 8 untouched sources + old partial + layer output in,
+        new partial + residual + weights out."""
+        S, T, d = MAX_SOURCES, self.T, self.d
+        return T * (2 * (S + 1) * d + 2 * 2 * d + 4 * S) + 4 * d
+
+    def step_bytes(self, fused: bool = True) -> int:
+        return self.fused_bytes() if fused else self.aggregate_bytes() + self.accumulate_bytes()
 
 
 class Schedule:
@@ -73,11 +87,11 @@ class Schedule:
         self.final_out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
         self.final_weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
 
-    def step(self, on_layer=None):
+    def step(self, on_layer=None, fused: bool = True):
         self.store.reset()
         run_schedule(self.store, self.F, self.W, self.block_size, out=self.out, weights=self.weights,
                      final_query=self.w_out, final_out=self.final_out, final_weights=self.final_weights,
-                     on_layer=on_layer)
+                     on_layer=on_layer, fused=fused)
 
     def source_counts(self):
         """S of every layer, then of the output layer."""
@@ -89,14 +103,22 @@ class Schedule:
                 n_done, partial = n_done + 1, False
         return counts + [1 + n_done]
 
-    def step_bytes(self) -> int:
-        """Algorithmic bytes of one full pass: every aggregate, every accumulate
-        (copy for a block's first layer, read-modify-write otherwise)."""
+    def step_bytes(self, fused: bool = True) -> int:
+        """Algorithmic bytes of one full pass.  Unfused: every aggregation plus
+        every update (copy for a block's first layer, read-modify-write
+        otherwise).  Fused: each update's slot is not read back by the next
+        aggregation, and a copy's source row is not read at all."""
         T, d = self.T, self.d
         total = 0
         for S in self.source_counts():
             total += T * (2 * S * d + 2 * d + 4 * S) + 4 * d
         for l in range(1, self.layers + 1):
             first = (l - 1) % self.block_size == 0
-            total += (2 if first else 3) * 2 * T * d
+            if fused:
+                # layer output (and, after a block's first layer, the old partial)
+                # read + slot written, while the next aggregation no longer reads
+                # the slot: net one slab for a copy, two for an addition
+                total += (1 if first else 2) * 2 * T * d
+            else:
+                total += (2 if first else 3) * 2 * T * d
         return total

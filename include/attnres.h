@@ -153,6 +153,28 @@ ATTNRES_API int attnres_store_sources(const attnres_store_t* st);
 ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out,
                                    int32_t finalize_block, void* stream);
 
+/*
+ * attnres_accumulate_aggregate -- attnres_accumulate(st, layer_out,
+ * finalize_block) followed by attnres_aggregate over the store's live sources
+ * with the next layer's query w, in ONE kernel: the updated slot is formed in
+ * registers from the old slot row and the layer output, written back, and used
+ * as the last source without being read again (kimi.papertok.ai §4.3 eq 10: the
+ * next layer sees the partial sum up to the previous layer, or the block
+ * representation just closed).  Results (slot contents, out, weights, store
+ * bookkeeping) are bit-identical to the two separate calls.
+ *
+ *   st, layer_out, finalize_block   as for attnres_accumulate.
+ *   w, out, weights, eps            as for attnres_aggregate; the sources are
+ *                                   slots [0, S) after the update, S =
+ *                                   1 + n_completed + partial_valid (new values);
+ *                                   weights is [T][S] or NULL.
+ * out and weights must not overlap the store, layer_out, w or each other
+ * (ATTNRES_EALIAS).  ATTNRES_ESTATE if the store has no slot left.  T == 0
+ * updates the bookkeeping and enqueues nothing.  *st changes on success only.
+ */
+ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
+                                             const float* w, void* out, float* weights, float eps, void* stream);
+
 /* Launch shape the library picks for an aggregation (host only, no HIP call). */
 typedef struct attnres_launch {
   int32_t threads;          /* threads per workgroup (multiple of 64)         */

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -158,3 +158,46 @@ def test_accumulate_argument_checks(lib):
     st.partial_valid, st.n_completed = 1, 8
     assert acc(OUT) == B.ESTATE
     assert B.lib().attnres_accumulate(None, OUT, 0, None) == B.EINVAL
+
+
+def test_fused_update_aggregate_checks(lib):
+    """attnres_accumulate_aggregate rejects bad arguments before any HIP call and
+    leaves the store untouched."""
+    rc, st = _store(T=4, d=8)
+    assert rc == B.OK
+    F, Wq, O, A = OUT, W, 0x50000000, WTS
+
+    def call(f=F, fin=0, w=Wq, out=O, wts=A, eps=1e-5):
+        return B.lib().attnres_accumulate_aggregate(ctypes.byref(st), f, fin, w, out, wts, eps, None)
+
+    assert call(f=None) == B.EINVAL
+    assert call(w=None) == B.EINVAL
+    assert call(out=None) == B.EINVAL
+    assert call(fin=3) == B.EINVAL
+    assert call(eps=float("nan")) == B.EINVAL
+    assert call(f=F + 8) == B.EUNSUPPORTED
+    assert call(out=O + 4) == B.EUNSUPPORTED
+    assert call(wts=A + 1) == B.EUNSUPPORTED
+    assert call(out=SRC + 32) == B.EALIAS          # residual into the store
+    assert call(wts=SRC + 64) == B.EALIAS          # weights into the store
+    assert call(out=F + 16) == B.EALIAS            # residual over the layer output
+    assert call(wts=O + 16) == B.EALIAS            # weights over the residual
+    assert call(w=SRC + 16) == B.EALIAS            # query inside the store
+    assert (st.n_completed, st.partial_valid) == (0, 0)
+    st.n_completed, st.partial_valid = 8, 0
+    assert call() == B.ESTATE
+    assert (st.n_completed, st.partial_valid) == (8, 0)
+
+
+def test_fused_update_aggregate_bookkeeping_without_tokens(lib):
+    """With T = 0 the fused call only advances the store, exactly like
+    attnres_accumulate."""
+    rc, st = _store(T=0)
+    assert rc == B.OK
+    counts = []
+    for l in range(1, 94):
+        fin = int(l % 12 == 0 or l == 93)
+        assert B.lib().attnres_accumulate_aggregate(ctypes.byref(st), None, fin, None, None, None, 1e-5, None) == B.OK
+        counts.append(B.lib().attnres_store_sources(ctypes.byref(st)))
+    # sources seen by layers 2..93 and the output layer
+    assert counts[-1] == 9 and st.n_completed == 8 and counts[0] == 2

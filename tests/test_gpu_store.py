@@ -59,12 +59,40 @@ def test_accumulate_rounding_ties_and_wide_range():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_small_schedule_matches_oracle_everywhere(dtype):
+@pytest.mark.parametrize("T,d", [(5, 7168), (129, 264), (1000, 7176), (3, 8)])
+@pytest.mark.parametrize("state,finalize", [((0, 0), 0), ((0, 1), 0), ((2, 1), 1), ((3, 0), 1), ((7, 1), 0)])
+def test_fused_update_aggregate_is_bit_identical_to_two_calls(dtype, T, d, state, finalize):
+    """attnres_accumulate_aggregate == attnres_accumulate + attnres_aggregate:
+    slot contents, residual, weights and bookkeeping, bit for bit."""
+    dev = device()
+    note(f"fused vs separate {dtype} T={T} d={d} state={state} finalize={finalize}")
+    a_store = B.SourceStore(T, d, dtype=_tdt(dtype), device=dev)
+    synth.sources(9, T, d, scale=(0.5, 50.0), seed=T + d, dtype=dtype, out=a_store.slots)
+    b_store = B.SourceStore(T, d, dtype=_tdt(dtype), device=dev, slots=a_store.slots.clone())
+    for st in (a_store, b_store):
+        st.set_state(*state)
+    F = synth.layer_output(T, d, std=2.0, seed=T, tag=3, dtype=dtype, device=dev)
+    w = synth.query(d, seed=d, device=dev)
+    a_store.accumulate(F, bool(finalize))
+    out_a, wts_a = a_store.aggregate(w)
+    out_b, wts_b = b_store.accumulate_aggregate(F, bool(finalize), w)
+    torch.cuda.synchronize()
+    assert (a_store.n_completed, a_store.partial_valid) == (b_store.n_completed, b_store.partial_valid)
+    assert torch.equal(a_store.slots.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       b_store.slots.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(out_a.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       out_b.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(wts_a.view(torch.int32), wts_b.view(torch.int32))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_schedule_matches_oracle_everywhere(dtype, fused):
     """30 layers in blocks of 4 (8 blocks, so up to 9 sources), ragged T and d,
     every layer's output and weights compared in full, block sums bit-exact."""
     dev = device()
     L, Bsz, T, d = 30, 4, 300, 520
-    note(f"small schedule {dtype} L={L} block={Bsz} T={T} d={d}")
+    note(f"small schedule {dtype} fused={fused} L={L} block={Bsz} T={T} d={d}")
     store = B.SourceStore(T, d, dtype=_tdt(dtype), device=dev)
     synth.fill_normal_(store.h0, 1.0, seed=1, tag=1)
     Fs = [synth.layer_output(T, d, std=0.1, seed=1, tag=l, dtype=dtype, device=dev) for l in range(L)]
@@ -72,7 +100,8 @@ def test_small_schedule_matches_oracle_everywhere(dtype):
     w_out = synth.query(d, seed=1, device=dev, tag=999)
     outs = torch.empty((L, T, d), dtype=_tdt(dtype), device=dev)
     wts = torch.zeros((L, T, 9), dtype=torch.float32, device=dev)
-    final_r, final_a = schedule.run_schedule(store, Fs, Ws, Bsz, out=outs, weights=wts, final_query=w_out)
+    final_r, final_a = schedule.run_schedule(store, Fs, Ws, Bsz, out=outs, weights=wts, final_query=w_out,
+                                             fused=fused)
     torch.cuda.synchronize()
     ref = orc.run_schedule(host(store.h0), [host(F) for F in Fs], [host(w) for w in Ws], Bsz, dtype,
                            final_query=host(w_out))

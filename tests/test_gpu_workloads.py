@@ -34,13 +34,13 @@ def test_fp32_small():
     compare(host(out), host(a), r_ref, a_ref, False, "fp32_small")
 
 
-def _check_layer_step(wl: workloads.LayerStep, rows: torch.Tensor, what: str):
+def _check_layer_step(wl: workloads.LayerStep, rows: torch.Tensor, what: str, fused: bool = True):
     """Snapshot sampled rows, run one step, compare with the oracle's
     accumulate + aggregate on the same rows."""
     idx = rows.to(wl.out.device)
     H = host(wl.store.slots.index_select(1, idx))         # [9, n, d] before the step
     F = host(wl.F.index_select(0, idx))
-    wl.step()
+    wl.step(fused=fused)
     torch.cuda.synchronize()
     new_partial = orc.accumulate(H[8], F, "bf16")
     assert same_bits(wl.store.slots[8].index_select(0, idx), new_partial), f"{what}: partial sum"
@@ -49,21 +49,23 @@ def _check_layer_step(wl: workloads.LayerStep, rows: torch.Tensor, what: str):
     compare(host(wl.out.index_select(0, idx)), host(wl.weights.index_select(0, idx)), r_ref, a_ref, True, what)
 
 
-def test_single_layer_t4096_full():
+@pytest.mark.parametrize("fused", [True, False])
+def test_single_layer_t4096_full(fused):
     dev = device()
-    note("layer_t4096 full compare")
+    note(f"layer_t4096 full compare fused={fused}")
     wl = workloads.LayerStep(4096, seed=0, device=dev)
-    _check_layer_step(wl, torch.arange(4096), "layer_t4096")
+    _check_layer_step(wl, torch.arange(4096), f"layer_t4096 fused={fused}", fused)
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("T", [1, 8, 64, 256])
-def test_decode_batches_full(T):
+def test_decode_batches_full(T, fused):
     dev = device()
-    note(f"decode T={T}")
+    note(f"decode T={T} fused={fused}")
     wl = workloads.LayerStep(T, seed=T, device=dev)
-    _check_layer_step(wl, torch.arange(T), f"decode T={T}")
+    _check_layer_step(wl, torch.arange(T), f"decode T={T}", fused)
     # a second step keeps accumulating into the same partial
-    _check_layer_step(wl, torch.arange(T), f"decode T={T} second step")
+    _check_layer_step(wl, torch.arange(T), f"decode T={T} second step", fused)
 
 
 def test_prefill_t262144_sampled():
