@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="prefill_t262144",
-                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93"])
+                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93", "full_s94"])
     p.add_argument("--decode-T", type=int, default=64)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded oracle timing budget")
@@ -134,7 +134,7 @@ def main():
         sys.exit(2)
 
     ceiling = None
-    if args.workload != "schedule_93" and not args.no_pattern_probe:
+    if args.workload not in ("schedule_93", "full_s94") and not args.no_pattern_probe:
         T_probe = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
         ceiling = pattern_ceiling(T_probe, 7168)
 
@@ -150,7 +150,13 @@ def main():
 
     fused = not args.unfused
     t_setup = time.perf_counter()
-    if args.workload == "schedule_93":
+    if args.workload == "full_s94":
+        wl = workloads.ManySources(32768, 94, seed=args.seed, device=dev)
+        T = wl.T
+        step_bytes = wl.step_bytes()
+        cfg = {"workload": "full_s94", "T": T, "d": wl.d, "S": wl.S,
+               "step": "one aggregation over 94 sources (batched online softmax)"}
+    elif args.workload == "schedule_93":
         wl = workloads.Schedule(32768, seed=args.seed, device=dev)
         T = wl.T
         step_bytes = wl.step_bytes(fused)
@@ -165,7 +171,7 @@ def main():
                "step": ("one fused launch: partial += layer output, then aggregate over 9 sources" if fused else
                         "attnres_accumulate (partial += layer output), then attnres_aggregate over 9 sources")}
     copy_store = None
-    if args.with_copy and args.workload != "schedule_93":
+    if args.with_copy and args.workload not in ("schedule_93", "full_s94"):
         copy_store = binding.SourceStore(T, wl.d, s_max=2, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -177,6 +183,15 @@ def main():
     def one_step(timed: bool):
         if args.workload == "schedule_93":
             wl.step(fused=fused)
+            return
+        if args.workload == "full_s94":
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
+            if ev:
+                ev[0].record(stream)
+            wl.step()
+            if ev:
+                ev[1].record(stream)
+                dom_events.append((ev[0], ev[1]))
             return
         if copy_store is not None:
             copy_store.reset()
@@ -217,6 +232,14 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                 "kernel": "whole schedule (all launches of one pass)", "bytes_per_launch": step_bytes}
         detail["step_gb"] = step_bytes / 1e9
+    elif args.workload == "full_s94":
+        dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
+        ms_step = wall * 1e3 / args.steps
+        achieved = step_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "kernel": "aggregate_many_kernel<true, 2>", "bytes_per_launch": step_bytes,
+                "avg_launch_ms": round(dom_ms, 4)}
     else:
         dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
         if copy_store is not None:
@@ -243,7 +266,7 @@ def main():
                            "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1)})
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload != "schedule_93":
+    if not args.no_cpu_baseline and args.workload not in ("schedule_93", "full_s94"):
         cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
 
     line = {

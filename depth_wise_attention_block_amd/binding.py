@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattnres.so")
 
 BF16, F32 = 0, 1
-MAX_SOURCES = 9
+MAX_SOURCES = 9            # Block AttnRes store slots
+MAX_SOURCES_FULL = 256     # one aggregation (Full AttnRes / sublayer granularity)
 OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
 

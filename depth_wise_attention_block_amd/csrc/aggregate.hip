@@ -307,6 +307,164 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   }
 }
 
+// ---- more than 9 sources: online softmax over batches of 9 ------------------
+//
+// Full AttnRes (kimi.papertok.ai ch. 4 §4.2: every earlier layer output is a
+// source, S up to L + 1) or sublayer granularity needs more rows than fit in
+// registers at once.  The sources are taken in batches of 9; after each batch
+// the running maximum m, normaliser l and float32 accumulator are rescaled by
+// exp(m_old - m_new) before the batch's terms are added ([TUT] §4.4: online
+// softmax merges partial results computed separately).  One barrier per batch.
+// The logits are kept in LDS so the weights can be written once m and l are
+// final.
+template <bool kBf16, int kV>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kV>())))
+aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
+                      const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
+                      float eps, float inv_d) {
+  __shared__ float red[2][kMaxWaves][2][16];
+  __shared__ float zbuf[kMaxSourcesMany];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int s16 = lane & 15;
+
+  Query<kBf16, kV> q;
+  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
+  constexpr int kE = kBf16 ? 8 : 4;  // elements per 16-byte vector
+
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const u32x4* tok = src + t * (int64_t)nvec;
+    float m = -INFINITY, l = 0.f;
+    float acc[kV][kE];
+#pragma unroll
+    for (int v = 0; v < kV; ++v)
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[v][e] = 0.f;
+
+    for (int s0 = 0; s0 < S; s0 += kMaxSrc, buf ^= 1) {
+      const int nb = min(kMaxSrc, S - s0);
+      u32x4 x[kMaxSrc][kV];
+#pragma unroll
+      for (int s = 0; s < kMaxSrc; ++s) {
+        if (s < nb) {
+#pragma unroll
+          for (int v = 0; v < kV; ++v) {
+            const int idx = v * nthr + tid;
+            x[s][v] = u32x4{0, 0, 0, 0};
+            if (idx < nvec) x[s][v] = __builtin_nontemporal_load(tok + (int64_t)(s0 + s) * src_stride_v + idx);
+          }
+        }
+      }
+      float gss = 0.f, gdt = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSrc; ++s) {
+        if (s < nb) {
+          float ss = 0.f, dt = 0.f;
+#pragma unroll
+          for (int v = 0; v < kV; ++v) {
+            if constexpr (kBf16) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                ss = dot2(x[s][v][k], x[s][v][k], ss);
+                dt = dot2(x[s][v][k], q.hi[v][k], dt);
+                dt = dot2(x[s][v][k], q.lo[v][k], dt);
+              }
+            } else {
+              const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                ss = fmaf(xf[k], xf[k], ss);
+                dt = fmaf(xf[k], q.f[v][k], dt);
+              }
+            }
+          }
+          gss = put_lane(wave_sum(ss), s, gss, s16);
+          gdt = put_lane(wave_sum(dt), s, gdt, s16);
+        }
+      }
+      if (lane < 16) {
+        red[buf][wave][0][lane] = gss;
+        red[buf][wave][1][lane] = gdt;
+      }
+      __syncthreads();
+      float z = -INFINITY;
+      if (s16 < nb) {
+        float ss = 0.f, dt = 0.f;
+        for (int k = 0; k < nwaves; ++k) {
+          ss += red[buf][k][0][s16];
+          dt += red[buf][k][1][s16];
+        }
+        z = dt / sqrtf(ss * inv_d + eps);
+        if (wave == 0 && lane < 16) zbuf[s0 + s16] = z;
+      }
+      // online merge of this batch into (m, l, acc)
+      const float m_new = fmaxf(m, row_max16(z));
+      const float c = expf(m - m_new);  // 0 on the first batch (m = -inf)
+      const float p = (s16 < nb) ? expf(z - m_new) : 0.f;
+      l = l * c + row_sum16(p);
+      m = m_new;
+      float ps[kMaxSrc];
+#pragma unroll
+      for (int s = 0; s < kMaxSrc; ++s) ps[s] = (s < nb) ? lane_bcast(p, s) : 0.f;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[v][e] *= c;
+#pragma unroll
+        for (int s = 0; s < kMaxSrc; ++s) {
+          if (s < nb) {
+            if constexpr (kBf16) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                acc[v][2 * k] = fmaf(ps[s], bf16_lo(x[s][v][k]), acc[v][2 * k]);
+                acc[v][2 * k + 1] = fmaf(ps[s], bf16_hi(x[s][v][k]), acc[v][2 * k + 1]);
+              }
+            } else {
+              const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) acc[v][k] = fmaf(ps[s], xf[k], acc[v][k]);
+            }
+          }
+        }
+      }
+    }
+
+    const float inv_l = 1.0f / l;
+    u32x4* orow = out + t * (int64_t)nvec;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      u32x4 o;
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[v][2 * k] * inv_l, acc[v][2 * k + 1] * inv_l);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(acc[v][k] * inv_l);
+      }
+      if (idx < nvec) __builtin_nontemporal_store(o, orow + idx);
+    }
+    if (weights != nullptr && wave == 0) {
+      for (int s = lane; s < S; s += 64) weights[t * S + s] = expf(zbuf[s] - m) * inv_l;
+    }
+  }
+}
+
+template <bool kBf16, int kV>
+hipError_t launch_many(const AggregateArgs& a, hipStream_t stream) {
+  const int epv = kBf16 ? 8 : 4;
+  const int nvec = a.d / epv;
+  hipLaunchKernelGGL((aggregate_many_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                     static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / epv, a.w,
+                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d);
+  return hipGetLastError();
+}
+
 template <bool kBf16, int kV, int kUpdate>
 hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
   const int epv = kBf16 ? 8 : 4;
@@ -316,6 +474,20 @@ hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
                      static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
                      static_cast<const u32x4*>(a.layer_out));
   return hipGetLastError();
+}
+
+hipError_t launch_many_v(const AggregateArgs& a, hipStream_t stream) {
+  switch ((a.bf16 ? 0 : 8) + a.vecs_per_lane) {
+    case 1: return launch_many<true, 1>(a, stream);
+    case 2: return launch_many<true, 2>(a, stream);
+    case 3: return launch_many<true, 3>(a, stream);
+    case 4: return launch_many<true, 4>(a, stream);
+    case 9: return launch_many<false, 1>(a, stream);
+    case 10: return launch_many<false, 2>(a, stream);
+    case 11: return launch_many<false, 3>(a, stream);
+    case 12: return launch_many<false, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int kUpdate>
@@ -336,6 +508,10 @@ hipError_t launch_v(const AggregateArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream) {
+  if (a.S > kMaxSrc) {
+    if (a.update != AggregateArgs::kNoUpdate || a.S > kMaxSourcesMany) return hipErrorInvalidValue;
+    return launch_many_v(a, stream);
+  }
   switch (a.update) {
     case AggregateArgs::kNoUpdate: return launch_v<kUpdateNone>(a, stream);
     case AggregateArgs::kCopyUpdate: return launch_v<kUpdateCopy>(a, stream);

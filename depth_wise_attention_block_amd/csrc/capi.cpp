@@ -8,6 +8,8 @@
 #include "../../include/attnres.h"
 #include "internal.h"
 
+static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
+
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
@@ -113,7 +115,7 @@ ATTNRES_API const char* attnres_strerror(int status) {
 ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus,
                                          attnres_launch_t* cfg) {
   if (cfg == nullptr) return ATTNRES_EINVAL;
-  if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  if (S < 1 || S > ATTNRES_MAX_SOURCES_FULL) return ATTNRES_EINVAL;
   const int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
   return pick_config(S, T, d, dtype, num_cus, cfg);
@@ -122,7 +124,7 @@ ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_
 ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
                                   const float* w, void* out, float* weights, float eps, int32_t dtype,
                                   void* stream) {
-  if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  if (S < 1 || S > ATTNRES_MAX_SOURCES_FULL) return ATTNRES_EINVAL;
   int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;

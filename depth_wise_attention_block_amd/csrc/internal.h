@@ -13,6 +13,8 @@ constexpr int kVecBytes = 16;
 constexpr int kMaxWaves = 8;
 // Most 16-byte vectors of one source row a lane holds.
 constexpr int kMaxVecsPerLane = 4;
+// Most sources one aggregation takes (batched online softmax beyond 9).
+constexpr int kMaxSourcesMany = 256;
 
 struct AggregateArgs {
   const void* sources;  // [S][T][d], source s at element offset s*src_stride

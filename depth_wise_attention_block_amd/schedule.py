@@ -94,3 +94,36 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
         return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps)
     store.accumulate(layer_outputs[-1], True)
     return None
+
+
+def run_full_schedule(sources: torch.Tensor, queries: Sequence[torch.Tensor], *, out: Optional[torch.Tensor] = None,
+                      weights: Optional[torch.Tensor] = None, final_query: Optional[torch.Tensor] = None,
+                      final_out: Optional[torch.Tensor] = None, final_weights: Optional[torch.Tensor] = None,
+                      on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
+                      eps: float = 1e-5):
+    """Full AttnRes (kimi.papertok.ai ch. 4 §4.2): layer l aggregates h_0 and the
+    outputs of every earlier layer.  ``sources`` is ``[L + 1, T, d]`` with h_0 in
+    row 0 and layer l's output in row l (a layer writes its output straight
+    into its row, so nothing is copied); layer l reads rows ``[0, l)`` -- one
+    ``attnres_aggregate`` with S = l, batched online softmax beyond 9 rows.
+    ``out``/``weights`` as in :func:`run_schedule` (``weights`` rows hold up to
+    L + 1 columns).  Returns the output layer's ``(out, weights)`` over all
+    L + 1 rows when ``final_query`` is given."""
+    num_layers = len(queries)
+    if sources.dim() != 3 or sources.shape[0] < num_layers + (1 if final_query is not None else 0):
+        raise ValueError("sources must be [L + 1, T, d]")
+    T, d = sources.shape[1], sources.shape[2]
+    if out is None:
+        out = torch.empty((T, d), dtype=sources.dtype, device=sources.device)
+    for l in range(1, num_layers + 1):
+        r = out[l - 1] if out.dim() == 3 else out
+        a = None
+        if weights is not None:
+            wbuf = weights[l - 1] if weights.dim() == 3 else weights
+            a = wbuf.view(-1)[: T * l].view(T, l)
+        aggregate(sources[:l], queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+        if on_layer is not None:
+            on_layer(l, r, a)
+    if final_query is not None:
+        return aggregate(sources[: num_layers + 1], final_query, final_out, final_weights, eps=eps)
+    return None

@@ -122,3 +122,24 @@ class Schedule:
             else:
                 total += (2 if first else 3) * 2 * T * d
         return total
+
+
+class ManySources:
+    """One aggregation over S > 9 sources (Full AttnRes: h_0 and every earlier
+    layer output; S = 94 is K3's output layer) -- the batched online-softmax
+    path.  Sources are N(0,1) * log-uniform scale like the other workloads."""
+
+    def __init__(self, T: int, S: int = 94, d: int = 7168, *, seed: int = 0, device="cuda", scale=(0.5, 50.0)):
+        self.T, self.S, self.d = T, S, d
+        self.H = synth.sources(S, T, d, scale=scale, seed=seed, device=device)
+        self.w = synth.query(d, seed=seed, device=device)
+        self.out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
+        self.weights = torch.empty((T, S), dtype=torch.float32, device=device)
+
+    def step(self):
+        from .binding import aggregate
+        aggregate(self.H, self.w, self.out, self.weights)
+
+    def step_bytes(self) -> int:
+        S, T, d = self.S, self.T, self.d
+        return T * (2 * S * d + 2 * d + 4 * S) + 4 * d

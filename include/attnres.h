@@ -41,6 +41,10 @@ extern "C" {
 /* Most sources one aggregation takes: embedding + 8 block representations,
  * or embedding + 7 + the partial sum (kimi.papertok.ai ch. 4 §4.5). */
 #define ATTNRES_MAX_SOURCES 9
+/* Most sources attnres_aggregate takes in one call: Full AttnRes keeps every
+ * earlier layer output as a source (kimi.papertok.ai ch. 4 §4.2), up to 94 for
+ * K3's 93 layers, or about twice that at sublayer granularity. */
+#define ATTNRES_MAX_SOURCES_FULL 256
 /* Largest hidden size: 4 vectors of 16 bytes per lane, 512 lanes per token. */
 #define ATTNRES_MAX_D_BF16 16384
 #define ATTNRES_MAX_D_F32 8192
@@ -72,11 +76,15 @@ ATTNRES_API const char* attnres_strerror(int status);
  *                     out[t] = sum_s a_s H_s[t]          (raw sources as values)
  * ("Kimi K3技术详解系列（二）" §2 and its listing; kimi.papertok.ai §4.2 eq 8-9;
  * llm-atlas.k1412.top/k3 card 07.)  Each source row is read from HBM once;
- * sums, softmax and the weighted sum are formed in float32.
+ * sums, softmax and the weighted sum are formed in float32.  Up to 9 sources
+ * are held in registers at once and the softmax is exact; beyond 9 (Full
+ * AttnRes, kimi.papertok.ai §4.2) the sources are taken in batches of 9 and
+ * merged by an online softmax (running max and normaliser, rescaled float32
+ * accumulator; §4.4).
  *
  *   sources     device, [S][T][d] of dtype, source-major: source s, token t
  *               starts at element s*src_stride + t*d.  16-byte aligned.
- *   S           number of sources, 1..ATTNRES_MAX_SOURCES.
+ *   S           number of sources, 1..ATTNRES_MAX_SOURCES_FULL.
  *   T           tokens, >= 0.  T == 0 returns ATTNRES_OK with nothing enqueued.
  *   d           hidden size: a multiple of 8 (bf16) or 4 (f32), at most
  *               ATTNRES_MAX_D_BF16 / ATTNRES_MAX_D_F32.

@@ -6,4 +6,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 from .attnres_oracle import (EPS, accumulate, bf16_bits_to_f32, bf16_round,  # noqa: F401
                              block_layout, depth_attention, f32_to_bf16_bits,
-                             layer_source_names, rmsnorm, run_schedule, softmax)
+                             layer_source_names, rmsnorm, run_full_schedule, run_schedule,
+                             softmax)

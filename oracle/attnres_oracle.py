@@ -31,11 +31,12 @@ with round-to-nearest-even.
 
 Parity pins (tests that fix this oracle to something other than itself):
 every function below is pinned -- the worked example of [BLOG2] §2.1, a
-library reduction (torch ``rms_norm`` + ``scaled_dot_product_attention``),
-closed forms (S=1, zero query, equal sources, S=2 logistic), invariants,
-50-digit brute force, bf16 rounding against torch and hand-made ties, and the
-schedule's source counts from [TUT] §4.5 / [ATLAS]'s widget.  None is marked
-"parity unpinned".
+library reduction (torch ``rms_norm`` + ``scaled_dot_product_attention``, up to
+94 sources), closed forms (S=1, zero query, equal sources, S=2 logistic),
+invariants, 50-digit brute force, bf16 rounding against torch and hand-made
+ties, the schedule's source counts from [TUT] §4.5 / [ATLAS]'s widget, and
+([TUT] §4.3) Block AttnRes with one layer per block being Full AttnRes.  None
+is marked "parity unpinned".
 """
 
 from __future__ import annotations
@@ -232,3 +233,18 @@ def run_schedule(h0, layer_outputs, queries, block_size: int, dtype: str,
         H = np.stack([h0] + blocks)
         out["final_r"], out["final_a"] = depth_attention(H, final_query, eps)
     return out
+
+
+def run_full_schedule(h0, layer_outputs, queries, final_query=None, eps: float = EPS):
+    """Full AttnRes ([TUT] §4.2): layer l aggregates h_0 and the outputs of every
+    earlier layer, h_1..h_{l-1}, with its own query; the output layer (if
+    ``final_query`` is given) aggregates all L + 1.  Sources are kept at their
+    given precision.  Returns the list of ``(r_l, a_l)`` and, optionally, the
+    output layer's pair."""
+    sources = [np.asarray(h0, dtype=np.float32)]
+    per_layer = []
+    for F, w in zip(layer_outputs, queries):
+        per_layer.append(depth_attention(np.stack(sources), w, eps))
+        sources.append(np.asarray(F, dtype=np.float32))
+    final = depth_attention(np.stack(sources), final_query, eps) if final_query is not None else None
+    return per_layer, final

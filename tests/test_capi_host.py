@@ -53,7 +53,7 @@ def agg(S=9, T=4, d=7168, stride=0, src=SRC, w=W, out=OUT, wts=WTS, eps=1e-5, dt
 
 
 @pytest.mark.parametrize("kwargs,status", [
-    (dict(S=0), B.EINVAL), (dict(S=10), B.EINVAL), (dict(S=-1), B.EINVAL),
+    (dict(S=0), B.EINVAL), (dict(S=257), B.EINVAL), (dict(S=-1), B.EINVAL),
     (dict(T=-1), B.EINVAL), (dict(d=0), B.EINVAL),
     (dict(d=7164), B.EUNSUPPORTED), (dict(d=6, dtype=B.F32), B.EUNSUPPORTED),
     (dict(d=16392), B.EUNSUPPORTED), (dict(d=8196, dtype=B.F32), B.EUNSUPPORTED),
@@ -64,6 +64,7 @@ def agg(S=9, T=4, d=7168, stride=0, src=SRC, w=W, out=OUT, wts=WTS, eps=1e-5, dt
     (dict(src=SRC + 8), B.EUNSUPPORTED), (dict(w=W + 4), B.EUNSUPPORTED), (dict(out=OUT + 2), B.EUNSUPPORTED),
     (dict(wts=WTS + 2), B.EUNSUPPORTED),
     (dict(out=SRC + 16), B.EALIAS), (dict(out=SRC + 8 * 4 * 7168 * 2), B.EALIAS),
+    (dict(S=94, out=SRC + 93 * 4 * 7168 * 2), B.EALIAS), (dict(S=256, stride=4 * 7168 - 8), B.EINVAL),
     (dict(out=W - 16), B.EALIAS), (dict(wts=SRC + 64), B.EALIAS), (dict(wts=OUT + 4 * 7168 * 2 - 4), B.EALIAS),
     (dict(wts=W + 16), B.EALIAS),
 ])

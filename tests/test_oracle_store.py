@@ -123,3 +123,33 @@ def test_schedule_with_integer_outputs_is_exact(dtype):
         assert np.array_equal(out["r"][l - 1], r) and np.array_equal(out["a"][l - 1], a)
     r, a = orc.depth_attention(np.stack([h0] + blocks), w_out)
     assert np.array_equal(out["final_r"], r)
+
+
+def test_full_attnres_is_block_attnres_with_one_layer_per_block():
+    """kimi.papertok.ai ch. 4 §4.3: the L layers are cut into N blocks of L/N
+    layers; with N = L every block is one layer, its representation is that
+    layer's output, and Block AttnRes reduces to Full AttnRes (§4.2)."""
+    rng = np.random.default_rng(5)
+    L, T, d = 11, 4, 16
+    h0 = orc.bf16_round(rng.normal(size=(T, d)).astype(np.float32))
+    Fs = orc.bf16_round(rng.normal(size=(L, T, d)).astype(np.float32))
+    Ws = rng.normal(scale=0.5, size=(L, d))
+    w_out = rng.normal(scale=0.5, size=d)
+    full, final = orc.run_full_schedule(h0, Fs, Ws, final_query=w_out)
+    block = orc.run_schedule(h0, Fs, Ws, 1, "bf16", final_query=w_out)
+    assert [a.shape[1] for _, a in full] == list(range(1, L + 1)) == block["num_sources"]
+    for l in range(L):
+        assert np.array_equal(full[l][0], block["r"][l]) and np.array_equal(full[l][1], block["a"][l])
+    assert np.array_equal(final[0], block["final_r"]) and final[1].shape == (T, L + 1)
+
+
+def test_many_sources_match_the_library_reduction():
+    """94 sources (Full AttnRes at K3's depth) against torch's RMSNorm + SDPA."""
+    from tests.oracle_pins import library_reference
+    rng = np.random.default_rng(6)
+    H = rng.normal(size=(94, 5, 32)) * rng.uniform(0.1, 10, size=(94, 1, 1))
+    w = rng.normal(scale=0.3, size=32)
+    r, a = orc.depth_attention(H, w)
+    r_lib, a_lib = library_reference(H, w)
+    assert np.max(np.abs(a - a_lib)) < 1e-12
+    assert np.max(np.abs(r - r_lib)) < 1e-12 * np.max(np.abs(r_lib))
