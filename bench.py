@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pattern-probe", action="store_true",
                    help="skip the trivial-arithmetic probe of the same HBM access pattern")
+    p.add_argument("--schedule-mode", default="two_phase", choices=["two_phase", "fused", "unfused"],
+                   help="schedule_93 only: per-layer launches (unfused / fused) or the two-phase schedule")
     p.add_argument("--unfused", action="store_true",
                    help="time attnres_accumulate + attnres_aggregate as two launches instead of the fused one")
     p.add_argument("--with-copy", action="store_true",
@@ -159,10 +161,14 @@ def main():
     elif args.workload == "schedule_93":
         wl = workloads.Schedule(32768, seed=args.seed, device=dev)
         T = wl.T
-        step_bytes = wl.step_bytes(fused)
+        sched_mode = "unfused" if args.unfused else args.schedule_mode
+        step_bytes = wl.step_bytes(sched_mode)
         cfg = {"workload": "schedule_93", "T": T, "d": wl.d, "layers": wl.layers, "block_size": wl.block_size,
-               "step": ("layer 1 aggregate + 93 fused (partial update + next aggregate) launches" if fused else
-                        "93 x (aggregate + partial update) + output-layer aggregate")}
+               "mode": sched_mode,
+               "step": {"two_phase": "blocks 1-2 one launch per layer; blocks 3-8 one inter-block pass per block "
+                                     "+ one merge per later layer; output-layer aggregate",
+                        "fused": "layer 1 aggregate + 93 fused (partial update + next aggregate) launches",
+                        "unfused": "93 x (aggregate + partial update) + output-layer aggregate"}[sched_mode]}
     else:
         T = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
         wl = workloads.LayerStep(T, seed=args.seed, device=dev)
@@ -182,7 +188,7 @@ def main():
 
     def one_step(timed: bool):
         if args.workload == "schedule_93":
-            wl.step(fused=fused)
+            wl.step(mode=sched_mode)
             return
         if args.workload == "full_s94":
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None

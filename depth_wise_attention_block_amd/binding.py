@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(HERE, "libattnres.so")
 BF16, F32 = 0, 1
 MAX_SOURCES = 9            # Block AttnRes store slots
 MAX_SOURCES_FULL = 256     # one aggregation (Full AttnRes / sublayer granularity)
+MAX_INTER_SOURCES = 8      # two-phase: inter-block sources per pass
+MAX_BLOCK_QUERIES = 16     # two-phase: layer queries per pass
 OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
 
@@ -58,6 +60,12 @@ _SIGNATURES = {
     "attnres_accumulate_aggregate": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                                     ctypes.c_void_p]),
+    "attnres_block_prepare": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]),
+    "attnres_block_merge": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_float, ctypes.c_void_p]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(attnres_launch_t)]),
 }
@@ -244,4 +252,65 @@ class SourceStore:
                                                 weights.data_ptr() if weights is not None else None, float(eps),
                                                 _stream(dev, stream))
         _check("attnres_accumulate_aggregate", rc)
+        return out, weights
+
+    # ---- two-phase schedule -------------------------------------------------
+
+    def block_prepare(self, layer_out, close_block: bool, w: torch.Tensor, inter: torch.Tensor,
+                      logits: torch.Tensor, weights0=None, *, eps=1e-5, stream=None):
+        """``attnres_block_prepare``: optionally close the open block with
+        ``layer_out``, then one pass over the K inter-block sources for the B
+        queries ``w`` ``[B, d]``.  ``inter`` is ``[B, T, d]`` (rows may be strided
+        along dim 0), ``logits`` ``[B, T, K]`` float32 with ``K = 1 +
+        n_completed`` after the close; ``weights0`` optional ``[T, K]``."""
+        dev = self.slots.device
+        B = w.shape[0]
+        if w.dtype != torch.float32 or w.dim() != 2 or w.shape[1] != self.d or not w.is_contiguous():
+            raise ValueError("w must be a contiguous float32 [B, d] tensor")
+        if inter.dim() != 3 or inter.shape[0] != B or inter.shape[1:] != (self.T, self.d) or \
+                inter.dtype != self.slots.dtype or (self.T > 0 and (inter.stride(2) != 1 or inter.stride(1) != self.d)):
+            raise ValueError("inter must be [B, T, d] of the store dtype with contiguous rows")
+        K = 1 + self.n_completed + (1 if close_block else 0)
+        if logits.dtype != torch.float32 or logits.numel() != B * self.T * K or not logits.is_contiguous():
+            raise ValueError("logits must be a contiguous float32 tensor with B*T*K elements")
+        if weights0 is not None and (weights0.dtype != torch.float32 or weights0.numel() != self.T * K
+                                     or not weights0.is_contiguous()):
+            raise ValueError("weights0 must be a contiguous float32 tensor with T*K elements")
+        if close_block and (layer_out is None or layer_out.dtype != self.slots.dtype or
+                            not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d):
+            raise ValueError("closing needs a contiguous [T, d] layer_out like the store")
+        stride = inter.stride(0) if B > 1 else self.T * self.d
+        rc = lib().attnres_block_prepare(ctypes.byref(self._st), layer_out.data_ptr() if close_block else None,
+                                         int(bool(close_block)), w.data_ptr(), B, inter.data_ptr(), stride,
+                                         logits.data_ptr(), weights0.data_ptr() if weights0 is not None else None,
+                                         float(eps), _stream(dev, stream))
+        _check("attnres_block_prepare", rc)
+
+    def block_merge(self, layer_out: torch.Tensor, w: torch.Tensor, inter: torch.Tensor, logits: torch.Tensor,
+                    out=None, weights=None, *, want_weights=True, eps=1e-5, stream=None):
+        """``attnres_block_merge``: add ``layer_out`` into the partial and merge it
+        with the inter-block part (``inter`` row ``[T, d]`` and its ``logits``
+        ``[T, K]``) for this layer's query ``w``.  ``out`` may be ``inter``
+        itself.  Returns ``(out, weights)``, weights ``[T, K + 1]``."""
+        dev = self.slots.device
+        K = 1 + self.n_completed
+        for name, t, dt, n in (("layer_out", layer_out, self.slots.dtype, self.T * self.d),
+                               ("w", w, torch.float32, self.d), ("inter", inter, self.slots.dtype, self.T * self.d),
+                               ("logits", logits, torch.float32, self.T * K)):
+            if t.dtype != dt or t.numel() != n or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"{name} must be a contiguous {dt} tensor with {n} elements on {dev}")
+        if out is None:
+            out = torch.empty((self.T, self.d), dtype=self.slots.dtype, device=dev)
+        if weights is None and want_weights:
+            weights = torch.empty((self.T, K + 1), dtype=torch.float32, device=dev)
+        if out.dtype != self.slots.dtype or out.numel() != self.T * self.d or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [T, d] tensor of the store dtype")
+        if weights is not None and (weights.dtype != torch.float32 or weights.numel() != self.T * (K + 1)
+                                    or not weights.is_contiguous()):
+            raise ValueError("weights must be a contiguous float32 tensor with T*(K+1) elements")
+        rc = lib().attnres_block_merge(ctypes.byref(self._st), layer_out.data_ptr(), w.data_ptr(), inter.data_ptr(),
+                                       logits.data_ptr(), out.data_ptr(),
+                                       weights.data_ptr() if weights is not None else None, float(eps),
+                                       _stream(dev, stream))
+        _check("attnres_block_merge", rc)
         return out, weights

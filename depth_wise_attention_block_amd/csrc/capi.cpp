@@ -9,6 +9,8 @@
 #include "internal.h"
 
 static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
+static_assert(ATTNRES_MAX_INTER_SOURCES == attnres::kMaxInterSources, "inter-source limits disagree");
+static_assert(ATTNRES_MAX_BLOCK_QUERIES == attnres::kMaxBlockQueries, "query limits disagree");
 
 namespace {
 
@@ -233,6 +235,141 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
   }
   st->n_completed = n_after;
   st->partial_valid = p_after;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out, int32_t close_block,
+                                      const float* w, int32_t B, void* inter, int64_t inter_stride, float* logits,
+                                      float* weights0, float eps, void* stream) {
+  int rc = check_store(st);
+  if (rc != ATTNRES_OK) return rc;
+  if (st->dtype != ATTNRES_BF16) return ATTNRES_EUNSUPPORTED;
+  if (close_block != 0 && close_block != 1) return ATTNRES_EINVAL;
+  if (B < 1 || B > attnres::kMaxBlockQueries) return ATTNRES_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;
+  if (close_block) {
+    if (1 + st->n_completed >= st->s_max) return ATTNRES_ESTATE;
+  } else if (st->partial_valid) {
+    return ATTNRES_ESTATE;  // an open partial must be closed first
+  }
+  const int n_after = st->n_completed + close_block;
+  const int K = 1 + n_after;
+  if (K > attnres::kMaxInterSources) return ATTNRES_EUNSUPPORTED;
+  const int64_t T = st->T;
+  const int d = st->d;
+  const int64_t row = T * (int64_t)d;
+  if (inter_stride == 0) inter_stride = row;
+  if (inter_stride < row || inter_stride % 8 != 0 || inter_stride > (INT64_C(1) << 40)) return ATTNRES_EINVAL;
+  if (row > 0) {
+    if (w == nullptr || inter == nullptr || logits == nullptr) return ATTNRES_EINVAL;
+    if (close_block && layer_out == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(w) || !aligned16(inter) || (close_block && !aligned16(layer_out))) return ATTNRES_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    if (weights0 != nullptr && (reinterpret_cast<uintptr_t>(weights0) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * 2);
+    const Range r_w = range(w, (int64_t)B * d * 4);
+    const Range r_in = range(inter, ((int64_t)(B - 1) * inter_stride + row) * 2);
+    const Range r_lg = range(logits, (int64_t)B * T * K * 4);
+    const Range r_f = close_block ? range(layer_out, row * 2) : Range{0, 0};
+    const Range r_w0 = weights0 != nullptr ? range(weights0, T * (int64_t)K * 4) : Range{0, 0};
+    if (overlap(r_f, r_store) || overlap(r_w, r_store) || overlap(r_in, r_store) || overlap(r_in, r_w) ||
+        overlap(r_in, r_f) || overlap(r_lg, r_store) || overlap(r_lg, r_w) || overlap(r_lg, r_in) ||
+        overlap(r_lg, r_f) || overlap(r_w0, r_store) || overlap(r_w0, r_w) || overlap(r_w0, r_in) ||
+        overlap(r_w0, r_lg) || overlap(r_w0, r_f))
+      return ATTNRES_EALIAS;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != ATTNRES_OK) return rc;
+    attnres_launch_t cfg;
+    rc = pick_config(K, T, d, st->dtype, cus, &cfg);
+    if (rc != ATTNRES_OK) return rc;
+    attnres::PrepareArgs a;
+    a.store = st->base;
+    a.slot_stride = st->slot_stride;
+    a.K = K;
+    a.B = B;
+    a.T = T;
+    a.d = d;
+    a.w = w;
+    a.inter = inter;
+    a.inter_stride = inter_stride;
+    a.logits = logits;
+    a.weights0 = weights0;
+    a.eps = eps;
+    a.close = !close_block ? attnres::PrepareArgs::kNone
+                           : (st->partial_valid ? attnres::PrepareArgs::kAdd : attnres::PrepareArgs::kCopy);
+    a.layer_out = layer_out;
+    a.threads = cfg.threads;
+    a.vecs_per_lane = cfg.vecs_per_lane;
+    a.grid = cfg.grid;
+    (void)hipGetLastError();
+    if (attnres::launch_block_prepare(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
+  }
+  st->n_completed = n_after;
+  st->partial_valid = 0;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_block_merge(attnres_store_t* st, const void* layer_out, const float* w, const void* inter,
+                                    const float* logits, void* out, float* weights, float eps, void* stream) {
+  int rc = check_store(st);
+  if (rc != ATTNRES_OK) return rc;
+  if (st->dtype != ATTNRES_BF16) return ATTNRES_EUNSUPPORTED;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;
+  const int slot = 1 + st->n_completed;
+  if (slot >= st->s_max) return ATTNRES_ESTATE;
+  const int K = 1 + st->n_completed;
+  if (K > attnres::kMaxInterSources) return ATTNRES_EUNSUPPORTED;
+  const int64_t T = st->T;
+  const int d = st->d;
+  const int64_t row = T * (int64_t)d;
+  if (row > 0) {
+    if (layer_out == nullptr || w == nullptr || inter == nullptr || logits == nullptr || out == nullptr)
+      return ATTNRES_EINVAL;
+    if (!aligned16(layer_out) || !aligned16(w) || !aligned16(inter) || !aligned16(out)) return ATTNRES_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    if (weights != nullptr && (reinterpret_cast<uintptr_t>(weights) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * 2);
+    const Range r_f = range(layer_out, row * 2);
+    const Range r_w = range(w, (int64_t)d * 4);
+    const Range r_in = range(inter, row * 2);
+    const Range r_lg = range(logits, T * (int64_t)K * 4);
+    const Range r_out = range(out, row * 2);
+    const Range r_wt = weights != nullptr ? range(weights, T * (int64_t)(K + 1) * 4) : Range{0, 0};
+    // out may be the inter row itself (the merge is in place per element);
+    // any other overlap is an error
+    const bool in_place = out == inter;
+    if (overlap(r_f, r_store) || overlap(r_w, r_store) || overlap(r_in, r_store) || overlap(r_lg, r_store) ||
+        overlap(r_out, r_store) || overlap(r_out, r_f) || overlap(r_out, r_w) || overlap(r_out, r_lg) ||
+        (!in_place && overlap(r_out, r_in)) || overlap(r_wt, r_store) || overlap(r_wt, r_f) ||
+        overlap(r_wt, r_w) || overlap(r_wt, r_in) || overlap(r_wt, r_lg) || overlap(r_wt, r_out))
+      return ATTNRES_EALIAS;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != ATTNRES_OK) return rc;
+    attnres_launch_t cfg;
+    rc = pick_config(2, T, d, st->dtype, cus, &cfg);
+    if (rc != ATTNRES_OK) return rc;
+    attnres::MergeArgs a;
+    a.slot = static_cast<char*>(st->base) + (int64_t)slot * st->slot_stride * 2;
+    a.layer_out = layer_out;
+    a.add = st->partial_valid != 0;
+    a.inter = inter;
+    a.logits = logits;
+    a.K = K;
+    a.T = T;
+    a.d = d;
+    a.w = w;
+    a.out = out;
+    a.weights = weights;
+    a.eps = eps;
+    a.threads = cfg.threads;
+    a.vecs_per_lane = cfg.vecs_per_lane;
+    a.grid = cfg.grid;
+    (void)hipGetLastError();
+    if (attnres::launch_block_merge(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
+  }
+  st->partial_valid = 1;
   return ATTNRES_OK;
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 
 namespace attnres {
 
@@ -31,6 +32,115 @@ __device__ __forceinline__ u32x4 add_rows(u32x4 p, u32x4 f, bool bf16) {
     for (int k = 0; k < 4; ++k) r[k] = __float_as_uint(__uint_as_float(p[k]) + __uint_as_float(f[k]));
   }
   return r;
+}
+
+// ---- DPP helpers (GFX9 data-parallel primitives inside one wave) -----------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- 7-i in 8
+constexpr int kDppMirror = 0x140;     // row_mirror: lane i <- 15-i in 16
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15 -> next row
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31 -> rows 2,3
+
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, src),
+                                         kCtrl, kRowMask, 0xF, false));
+}
+
+// Every lane of each 16-lane row ends with that row's sum (bitwise equal
+// across the row: each step adds the same two operands in either order).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kDppXor1>(v, v);
+  v += dpp<kDppXor2>(v, v);
+  v += dpp<kDppHalfMirror>(v, v);
+  v += dpp<kDppMirror>(v, v);
+  return v;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v, v));
+  v = fmaxf(v, dpp<kDppXor2>(v, v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp<kDppMirror>(v, v));
+  return v;
+}
+
+// Every lane of each 8-lane group ends with that group's sum / maximum.
+__device__ __forceinline__ float group_sum8(float v) {
+  v += dpp<kDppXor1>(v, v);
+  v += dpp<kDppXor2>(v, v);
+  v += dpp<kDppHalfMirror>(v, v);
+  return v;
+}
+
+__device__ __forceinline__ float group_max8(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v, v));
+  v = fmaxf(v, dpp<kDppXor2>(v, v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v, v));
+  return v;
+}
+
+// Sum over all 64 lanes, returned wave-uniform.  Fixed order: rows, then
+// row 0 + row 1 and row 2 + row 3, then the two halves.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += dpp<kDppBcast15, 0xA>(0.0f, v);  // rows 1,3 += lane 15 of the row below
+  v += dpp<kDppBcast31, 0xC>(0.0f, v);  // rows 2,3 += lane 31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Lane `lane` of every 16-lane row takes v; the other lanes keep old.
+__device__ __forceinline__ float put_lane(float v, int lane, float old, int s16) {
+  return s16 == lane ? v : old;
+}
+
+// ---- bf16 pair helpers -------------------------------------------------------
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// Per-lane slice of the pseudo-query.  bf16 sources: w = hi + lo, both bf16
+// pairs laid out like the source words (element 2i in the low half), so that
+// w.x = dot2(x, hi) + dot2(x, lo) keeps ~16 significant bits of w.
+template <bool kBf16, int kV>
+struct Query {
+  u32x4 hi[kV], lo[kV];  // bf16 path
+  f32x4 f[kV];           // f32 path
+};
+
+template <bool kBf16, int kV>
+__device__ __forceinline__ void load_query(Query<kBf16, kV>& q, const float* __restrict__ w, int nvec,
+                                           int tid, int nthr) {
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int idx = v * nthr + tid;
+    if constexpr (kBf16) {
+      q.hi[v] = u32x4{0, 0, 0, 0};
+      q.lo[v] = u32x4{0, 0, 0, 0};
+      if (idx < nvec) {
+        const f32x4* wp = reinterpret_cast<const f32x4*>(w) + 2 * (int64_t)idx;
+        const f32x4 a = wp[0], b = wp[1];
+        const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const __bf16 h0 = (__bf16)e[2 * k], h1 = (__bf16)e[2 * k + 1];
+          const __bf16 l0 = (__bf16)(e[2 * k] - (float)h0), l1 = (__bf16)(e[2 * k + 1] - (float)h1);
+          q.hi[v][k] = __builtin_bit_cast(unsigned, bf16x2{h0, h1});
+          q.lo[v][k] = __builtin_bit_cast(unsigned, bf16x2{l0, l1});
+        }
+      }
+    } else {
+      q.f[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (idx < nvec) q.f[v] = reinterpret_cast<const f32x4*>(w)[idx];
+    }
+  }
 }
 
 }  // namespace attnres

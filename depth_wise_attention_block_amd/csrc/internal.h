@@ -15,6 +15,9 @@ constexpr int kMaxWaves = 8;
 constexpr int kMaxVecsPerLane = 4;
 // Most sources one aggregation takes (batched online softmax beyond 9).
 constexpr int kMaxSourcesMany = 256;
+// Two-phase schedule: inter-block sources and layer queries per pass.
+constexpr int kMaxInterSources = 8;
+constexpr int kMaxBlockQueries = 16;
 
 struct AggregateArgs {
   const void* sources;  // [S][T][d], source s at element offset s*src_stride
@@ -50,5 +53,49 @@ struct AccumulateArgs {
 };
 
 hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream);
+
+// Phase 1 of the two-phase schedule: one pass over a block's inter-block
+// sources (bf16 store) for B layer queries.
+struct PrepareArgs {
+  void* store;          // slot 0
+  int64_t slot_stride;  // elements
+  int K;                // inter-block sources, slots [0, K)
+  int B;                // queries
+  int64_t T;
+  int d;
+  const float* w;       // [B][d]
+  void* inter;          // [B] rows of [T][d] bf16 at inter_stride elements
+  int64_t inter_stride;
+  float* logits;        // [B][T][K]
+  float* weights0;      // [T][K] or nullptr
+  float eps;
+  enum Close { kNone = 0, kCopy = 1, kAdd = 2 };
+  Close close;          // form slot K-1 from layer_out first (closing a block)
+  const void* layer_out;
+  int threads, vecs_per_lane;
+  int64_t grid;
+};
+
+hipError_t launch_block_prepare(const PrepareArgs& a, hipStream_t stream);
+
+// Phase 2: one later layer of the block.
+struct MergeArgs {
+  void* slot;           // the partial slot [T][d]
+  const void* layer_out;
+  bool add;             // slot = slot + layer_out (else slot = layer_out)
+  const void* inter;    // R row [T][d]
+  const float* logits;  // [T][K]
+  int K;
+  int64_t T;
+  int d;
+  const float* w;       // [d]
+  void* out;            // [T][d]; may be `inter` itself
+  float* weights;       // [T][K+1] or nullptr
+  float eps;
+  int threads, vecs_per_lane;
+  int64_t grid;
+};
+
+hipError_t launch_block_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace attnres

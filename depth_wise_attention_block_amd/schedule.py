@@ -17,7 +17,7 @@ from typing import Callable, Optional, Sequence
 
 import torch
 
-from .binding import SourceStore, aggregate
+from .binding import MAX_BLOCK_QUERIES, MAX_INTER_SOURCES, SourceStore, aggregate
 
 
 def closes_block(layer: int, num_layers: int, block_size: int) -> bool:
@@ -30,22 +30,35 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                  final_query: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
                  final_weights: Optional[torch.Tensor] = None,
                  on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
-                 fused: bool = True, eps: float = 1e-5):
+                 fused: bool = True, two_phase_from: Optional[int] = None,
+                 inter: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                 eps: float = 1e-5):
     """Run every layer's aggregation and partial-sum update in stream order.
 
-    ``fused=True`` (default): layer 1 aggregates h_0 alone; every later layer l
-    is one ``attnres_accumulate_aggregate`` that adds F_{l-1} (closing its block
-    if it was the block's last layer) and aggregates with w_l; the output layer's
-    aggregation is fused with the last update the same way -- 1 + L launches.
-    ``fused=False``: separate ``attnres_aggregate`` and ``attnres_accumulate``
-    per layer -- 2L (+1) launches.  Both give bit-identical results.
+    Per layer one of:
+      * ``fused=False``: ``attnres_aggregate`` then ``attnres_accumulate`` (2L+1
+        launches);
+      * default: layer 1 aggregates h_0 alone; every later layer l is one
+        ``attnres_accumulate_aggregate`` that adds F_{l-1} (closing its block
+        when it was the block's last layer) and aggregates with w_l;
+      * ``two_phase_from=n0``: blocks n >= n0 run the two-phase schedule --
+        one ``attnres_block_prepare`` (closing the previous block, then one pass
+        over h_0, b_1..b_{n-1} for all the block's queries; its first query's
+        result is the block's first residual) and one ``attnres_block_merge``
+        per later layer; other blocks run as in the default.
+    The output layer's aggregation is fused with the last update.  All modes
+    agree with the oracle; the fused and unfused ones bit for bit with each
+    other.
 
     ``store`` must hold h_0 in slot 0 and no blocks yet.  ``out`` is either one
     ``[T, d]`` buffer reused by every layer or ``[L, T, d]``; ``weights``
     likewise ``[T, 9]`` (each layer writes a ``[T, S_l]`` block at its start) or
-    ``[L, T, 9]``.  ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation
-    is enqueued (1-based l).  Returns the output layer's ``(out, weights)``
-    when ``final_query`` is given, else None.
+    ``[L, T, 9]``.  Two-phase blocks need ``inter`` ``[block_size, T, d]`` (store
+    dtype) and ``logits`` (float32, ``block_size * T * 8`` elements) unless
+    ``out`` is ``[L, T, d]``, whose rows then hold the pass's results directly.
+    ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation is enqueued
+    (1-based l).  Returns the output layer's ``(out, weights)`` when
+    ``final_query`` is given, else None.
     """
     num_layers = len(layer_outputs)
     if len(queries) != num_layers or num_layers == 0:
@@ -53,25 +66,22 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     if store.n_completed != 0 or store.partial_valid:
         raise ValueError("store must start with only h_0 live")
     T, d = store.T, store.d
+    dev = store.slots.device
     if out is None:
-        out = torch.empty((T, d), dtype=store.slots.dtype, device=store.slots.device)
+        out = torch.empty((T, d), dtype=store.slots.dtype, device=dev)
 
-    def buffers(l: int, S: int):
-        r = out[l - 1] if out.dim() == 3 else out
-        a = None
-        if weights is not None:
-            wbuf = weights[l - 1] if weights.dim() == 3 else weights
-            a = wbuf.view(-1)[: T * S].view(T, S)
-        return r, a
+    def wview(l: int, S: int):
+        if weights is None:
+            return None
+        wbuf = weights[l - 1] if weights.dim() == 3 else weights
+        return wbuf.view(-1)[: T * S].view(T, S)
 
-    def sources_after(l_done: int) -> int:
-        """Live sources once layer l_done's output has been added."""
-        closes = closes_block(l_done, num_layers, block_size)
-        return 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
+    def rbuf(l: int):
+        return out[l - 1] if out.dim() == 3 else out
 
     if not fused:
         for l in range(1, num_layers + 1):
-            r, a = buffers(l, store.num_sources())
+            r, a = rbuf(l), wview(l, store.num_sources())
             aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
             if on_layer is not None:
                 on_layer(l, r, a)
@@ -80,14 +90,48 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
             return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
         return None
 
-    r, a = buffers(1, store.num_sources())
-    aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
-    if on_layer is not None:
-        on_layer(1, r, a)
-    for l in range(2, num_layers + 1):
-        r, a = buffers(l, sources_after(l - 1))
-        store.accumulate_aggregate(layer_outputs[l - 2], closes_block(l - 1, num_layers, block_size),
-                                   queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+    num_blocks = (num_layers + block_size - 1) // block_size
+    two_phase = set()
+    if two_phase_from is not None:
+        two_phase = {n for n in range(max(1, two_phase_from), num_blocks + 1) if n <= MAX_INTER_SOURCES}
+        if block_size > MAX_BLOCK_QUERIES:
+            raise ValueError(f"two-phase blocks hold at most {MAX_BLOCK_QUERIES} layers")
+        if two_phase and out.dim() != 3 and (inter is None or logits is None):
+            inter = torch.empty((block_size, T, d), dtype=store.slots.dtype, device=dev)
+            logits = torch.empty(block_size * T * MAX_INTER_SOURCES, dtype=torch.float32, device=dev)
+
+    block_rows = None   # R rows of the current two-phase block
+    block_logits = None
+    for l in range(1, num_layers + 1):
+        n, i = (l - 1) // block_size + 1, (l - 1) % block_size + 1
+        last = min(n * block_size, num_layers)
+        if n in two_phase and i == 1:
+            B = last - l + 1
+            K = n  # h_0 and b_1..b_{n-1} once the previous block is closed
+            W = torch.stack([queries[j] for j in range(l - 1, last)])
+            block_rows = out[l - 1:last] if out.dim() == 3 else inter[:B]
+            lg_buf = logits if out.dim() != 3 else None
+            if lg_buf is None:
+                lg_buf = torch.empty(B * T * K, dtype=torch.float32, device=dev)
+            block_logits = lg_buf[: B * T * K].view(B, T, K)
+            a = wview(l, K)
+            store.block_prepare(layer_outputs[l - 2] if l > 1 else None, l > 1, W, block_rows, block_logits, a,
+                                eps=eps)
+            r = block_rows[0]
+        elif n in two_phase:
+            a = wview(l, n + 1)
+            r = rbuf(l)
+            store.block_merge(layer_outputs[l - 2], queries[l - 1], block_rows[i - 1], block_logits[i - 1],
+                              out=r, weights=a, want_weights=a is not None, eps=eps)
+        elif l == 1:
+            r, a = rbuf(l), wview(l, store.num_sources())
+            aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
+        else:
+            closes = closes_block(l - 1, num_layers, block_size)
+            S = 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
+            r, a = rbuf(l), wview(l, S)
+            store.accumulate_aggregate(layer_outputs[l - 2], closes, queries[l - 1], r, a,
+                                       want_weights=a is not None, eps=eps)
         if on_layer is not None:
             on_layer(l, r, a)
     if final_query is not None:

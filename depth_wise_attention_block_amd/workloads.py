@@ -73,6 +73,10 @@ class LayerStep:
 
 
 class Schedule:
+    #: two-phase blocks start here: block n's one pass reads n inter-block rows
+    #: and writes 12, which beats 12 one-pass layers from about n = 3 on
+    TWO_PHASE_FROM = 3
+
     def __init__(self, T: int, d: int = 7168, *, layers: int = 93, block_size: int = 12, seed: int = 0,
                  device="cuda", h0_scale: float = 1.0, layer_out_std: float = 0.1):
         self.T, self.d, self.layers, self.block_size = T, d, layers, block_size
@@ -86,12 +90,27 @@ class Schedule:
         self.weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
         self.final_out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
         self.final_weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
+        self._inter = None
+        self._logits = None
 
-    def step(self, on_layer=None, fused: bool = True):
+    def step(self, on_layer=None, mode: str = "fused"):
+        """One pass of the depth path.  ``mode``: ``"unfused"`` (aggregate +
+        update per layer), ``"fused"`` (one launch per layer), ``"two_phase"``
+        (blocks from ``TWO_PHASE_FROM`` on: one inter-block pass per block, one
+        merge per later layer)."""
         self.store.reset()
+        kw = {}
+        if mode == "two_phase":
+            if self._inter is None:
+                dev = self.out.device
+                self._inter = torch.empty((self.block_size, self.T, self.d), dtype=torch.bfloat16, device=dev)
+                self._logits = torch.empty(self.block_size * self.T * 8, dtype=torch.float32, device=dev)
+            kw = dict(two_phase_from=self.TWO_PHASE_FROM, inter=self._inter, logits=self._logits)
+        elif mode not in ("fused", "unfused"):
+            raise ValueError(f"unknown mode {mode!r}")
         run_schedule(self.store, self.F, self.W, self.block_size, out=self.out, weights=self.weights,
                      final_query=self.w_out, final_out=self.final_out, final_weights=self.final_weights,
-                     on_layer=on_layer, fused=fused)
+                     on_layer=on_layer, fused=mode != "unfused", **kw)
 
     def source_counts(self):
         """S of every layer, then of the output layer."""
@@ -103,24 +122,46 @@ class Schedule:
                 n_done, partial = n_done + 1, False
         return counts + [1 + n_done]
 
-    def step_bytes(self, fused: bool = True) -> int:
+    def step_bytes(self, mode: str = "fused") -> int:
         """Algorithmic bytes of one full pass.  Unfused: every aggregation plus
         every update (copy for a block's first layer, read-modify-write
         otherwise).  Fused: each update's slot is not read back by the next
-        aggregation, and a copy's source row is not read at all."""
+        aggregation, and a copy's source row is not read at all.  Two-phase
+        blocks: one pass reading the n inter-block rows (and the closing
+        update's rows) and writing B result rows + B*T*n logits, then per later
+        layer the merge's rows (result row, layer output, old partial in;
+        partial, residual out) and logits."""
         T, d = self.T, self.d
+        row = 2 * T * d
+        counts = self.source_counts()
         total = 0
-        for S in self.source_counts():
-            total += T * (2 * S * d + 2 * d + 4 * S) + 4 * d
         for l in range(1, self.layers + 1):
-            first = (l - 1) % self.block_size == 0
-            if fused:
-                # layer output (and, after a block's first layer, the old partial)
-                # read + slot written, while the next aggregation no longer reads
-                # the slot: net one slab for a copy, two for an addition
-                total += (1 if first else 2) * 2 * T * d
-            else:
-                total += (2 if first else 3) * 2 * T * d
+            n, i = (l - 1) // self.block_size + 1, (l - 1) % self.block_size + 1
+            S = counts[l - 1]
+            if mode == "two_phase" and n >= self.TWO_PHASE_FROM:
+                if i == 1:
+                    B = min(self.block_size, self.layers - l + 1)
+                    prev_first = ((l - 2) % self.block_size == 0)   # closing a 1-layer partial: copy
+                    total += (n - 1) * row                          # b's already complete + h_0
+                    total += (1 if prev_first else 2) * row + row   # layer output (+ old partial) in, b_{n-1} out
+                    total += B * row + B * T * n * 4 + B * d * 4 + T * n * 4
+                else:
+                    total += (2 if i >= 3 else 1) * row             # layer output (+ old partial) in
+                    total += row + row + row                        # R in, partial out, residual out
+                    total += T * n * 4 + T * (n + 1) * 4 + 4 * d
+                continue
+            total += T * (2 * S * d + 2 * d + 4 * S) + 4 * d
+            if l > 1:
+                first = (l - 2) % self.block_size == 0   # the update this launch fuses is a copy
+                if mode == "unfused":
+                    total += (2 if first else 3) * row
+                else:
+                    total += (1 if first else 2) * row
+        # output layer (always fused with the last update, or an extra update)
+        S = counts[-1]
+        total += T * (2 * S * d + 2 * d + 4 * S) + 4 * d
+        last_first = (self.layers - 1) % self.block_size == 0
+        total += ((2 if last_first else 3) if mode == "unfused" else (1 if last_first else 2)) * row
         return total
 
 

@@ -183,6 +183,61 @@ ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out,
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                              const float* w, void* out, float* weights, float eps, void* stream);
 
+/*
+ * Two-phase schedule (kimi.papertok.ai ch. 4 §4.4, third benefit, and §4.6,
+ * inference): inside block n the inter-block sources h_0, b_1 .. b_{n-1} stay
+ * fixed, so one batched pass reads them once for all the block's layer
+ * queries (attnres_block_prepare), and each later layer merges its partial
+ * sum in by online softmax (attnres_block_merge).  bf16 stores only; at most
+ * ATTNRES_MAX_INTER_SOURCES inter-block sources and ATTNRES_MAX_BLOCK_QUERIES
+ * queries per pass.  Results equal attnres_aggregate over the same sources up
+ * to one extra bf16 rounding of the inter-block part (the stored R rows).
+ */
+#define ATTNRES_MAX_INTER_SOURCES 8
+#define ATTNRES_MAX_BLOCK_QUERIES 16
+
+/*
+ * attnres_block_prepare -- phase 1 for one block.
+ *
+ * If close_block, layer_out (the previous block's last layer output) is first
+ * added into the partial slot and the block is closed, exactly as
+ * attnres_accumulate(st, layer_out, 1) (copy when no partial is open);
+ * otherwise no partial may be open (ATTNRES_ESTATE).  Then with K = 1 +
+ * n_completed inter-block sources (slots [0, K)) and the B queries w[b]:
+ *   z[b][t][s] = w_b . RMSNorm(H_s[t])          -> logits, float32 [B][T][K]
+ *   R_b[t]     = sum_s softmax_s(z[b][t]) H_s[t] -> inter row b, bf16 [T][d]
+ *   weights0[t][s] = softmax_s(z[0][t])         (optional, float32 [T][K])
+ * R_0 is the residual of the block's first layer.
+ *
+ *   w             device, [B][d] float32, 16-byte aligned.
+ *   B             1..ATTNRES_MAX_BLOCK_QUERIES.
+ *   inter         device, B rows of [T][d] bf16, row b at element b*inter_stride
+ *                 (0 means T*d); 16-byte aligned.
+ *   logits        device, [B][T][K] float32.
+ * No output may overlap the store, layer_out, w or another output
+ * (ATTNRES_EALIAS).  *st is updated on success only.
+ */
+ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out, int32_t close_block,
+                                      const float* w, int32_t B, void* inter, int64_t inter_stride,
+                                      float* logits, float* weights0, float eps, void* stream);
+
+/*
+ * attnres_block_merge -- phase 2 for one later layer of the block.
+ *
+ * Adds layer_out (the previous layer's output) into the partial slot (copy if
+ * none is open; partial_valid becomes 1), scores the new partial with this
+ * layer's query w, and merges it with the inter-block part of prepare's query
+ * for this layer (inter row R and its logits [T][K], K = 1 + n_completed):
+ *   M = max(max_s z_s, z_p),  A = sum_s e^(z_s - M),  P = e^(z_p - M)
+ *   out = (A R + P x_p) / (A + P);  weights[t] = [e^(z_s - M), P] / (A + P)
+ *
+ *   out       device, [T][d] bf16; may be the inter row itself (in place).
+ *   weights   device, [T][K+1] float32 (inter sources, then the partial), or NULL.
+ */
+ATTNRES_API int attnres_block_merge(attnres_store_t* st, const void* layer_out, const float* w,
+                                    const void* inter, const float* logits, void* out, float* weights,
+                                    float eps, void* stream);
+
 /* Launch shape the library picks for an aggregation (host only, no HIP call). */
 typedef struct attnres_launch {
   int32_t threads;          /* threads per workgroup (multiple of 64)         */

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -202,3 +202,47 @@ def test_fused_update_aggregate_bookkeeping_without_tokens(lib):
         counts.append(B.lib().attnres_store_sources(ctypes.byref(st)))
     # sources seen by layers 2..93 and the output layer
     assert counts[-1] == 9 and st.n_completed == 8 and counts[0] == 2
+
+
+def test_two_phase_checks_and_bookkeeping(lib):
+    """attnres_block_prepare / attnres_block_merge argument checks (no launch) and
+    their effect on the store with T = 0."""
+    rc, st = _store(T=4, d=8)
+    assert rc == B.OK
+    INTER, LOG, W0 = 0x60000000, 0x70000000, 0x78000000
+
+    def prep(f=OUT, close=0, w=W, nb=12, inter=INTER, stride=0, lg=LOG, w0=W0, eps=1e-5):
+        return B.lib().attnres_block_prepare(ctypes.byref(st), f, close, w, nb, inter, stride, lg, w0, eps, None)
+
+    assert prep(nb=0) == B.EINVAL and prep(nb=17) == B.EINVAL
+    assert prep(close=2) == B.EINVAL
+    assert prep(w=None) == B.EINVAL and prep(inter=None) == B.EINVAL and prep(lg=None) == B.EINVAL
+    assert prep(close=1, f=None) == B.EINVAL
+    assert prep(inter=INTER + 8) == B.EUNSUPPORTED and prep(lg=LOG + 2) == B.EUNSUPPORTED
+    assert prep(stride=4 * 8 - 8) == B.EINVAL
+    assert prep(inter=SRC + 16) == B.EALIAS and prep(lg=INTER + 64) == B.EALIAS and prep(w0=LOG) == B.EALIAS
+    st.partial_valid = 1
+    assert prep() == B.ESTATE          # an open partial must be closed first
+    st.partial_valid, st.n_completed = 0, 7
+    assert prep(close=1) == B.EUNSUPPORTED or prep(close=1) == B.ESTATE   # 9 inter sources: too many
+    st.n_completed = 0
+    rcf, stf = _store(T=4, d=8, dtype=B.F32)
+    assert B.lib().attnres_block_prepare(ctypes.byref(stf), None, 0, W, 4, INTER, 0, LOG, None, 1e-5,
+                                         None) == B.EUNSUPPORTED
+
+    def merge(f=OUT, w=W, inter=INTER, lg=LOG, out=0x58000000, wts=W0):
+        return B.lib().attnres_block_merge(ctypes.byref(st), f, w, inter, lg, out, wts, 1e-5, None)
+
+    assert merge(f=None) == B.EINVAL and merge(out=None) == B.EINVAL
+    assert merge(out=SRC) == B.EALIAS and merge(out=INTER + 16) == B.EALIAS and merge(wts=LOG) == B.EALIAS
+    assert (st.n_completed, st.partial_valid) == (0, 0)
+
+    rc, st0 = _store(T=0)
+    call = lambda: B.lib().attnres_block_prepare(ctypes.byref(st0), None, 0, None, 12, None, 0, None, None,
+                                                 1e-5, None)
+    assert call() == B.OK and (st0.n_completed, st0.partial_valid) == (0, 0)
+    assert B.lib().attnres_block_merge(ctypes.byref(st0), None, None, None, None, None, None, 1e-5, None) == B.OK
+    assert st0.partial_valid == 1
+    assert B.lib().attnres_block_prepare(ctypes.byref(st0), None, 1, None, 12, None, 0, None, None, 1e-5,
+                                         None) == B.OK
+    assert (st0.n_completed, st0.partial_valid) == (1, 0)
