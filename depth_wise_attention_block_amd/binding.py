@@ -66,6 +66,8 @@ _SIGNATURES = {
     "attnres_block_merge": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_float, ctypes.c_void_p]),
+    "attnres_split_queries": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(attnres_launch_t)]),
 }
@@ -159,6 +161,21 @@ def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None =
                                  _dtype_code(sources), _stream(dev, stream))
     _check("attnres_aggregate", rc)
     return out, weights
+
+
+def split_queries(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``attnres_split_queries``: float32 queries ``[n, d]`` -> bf16 ``[n, 2, d]``
+    (hi, lo) as the two-phase pass reads them."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 [n, d] tensor")
+    n, d = w.shape
+    if out is None:
+        out = torch.empty((n, 2, d), dtype=torch.bfloat16, device=w.device)
+    if out.dtype != torch.bfloat16 or out.shape != (n, 2, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [n, 2, d] tensor")
+    _check("attnres_split_queries", lib().attnres_split_queries(w.data_ptr(), n, d, out.data_ptr(),
+                                                                _stream(w.device, stream)))
+    return out
 
 
 class SourceStore:
@@ -256,17 +273,19 @@ class SourceStore:
 
     # ---- two-phase schedule -------------------------------------------------
 
-    def block_prepare(self, layer_out, close_block: bool, w: torch.Tensor, inter: torch.Tensor,
+    def block_prepare(self, layer_out, close_block: bool, w_split: torch.Tensor, inter: torch.Tensor,
                       logits: torch.Tensor, weights0=None, *, eps=1e-5, stream=None):
         """``attnres_block_prepare``: optionally close the open block with
         ``layer_out``, then one pass over the K inter-block sources for the B
-        queries ``w`` ``[B, d]``.  ``inter`` is ``[B, T, d]`` (rows may be strided
-        along dim 0), ``logits`` ``[B, T, K]`` float32 with ``K = 1 +
-        n_completed`` after the close; ``weights0`` optional ``[T, K]``."""
+        queries ``w_split`` ``[B, 2, d]`` (from :func:`split_queries`).
+        ``inter`` is ``[B, T, d]`` (rows may be strided along dim 0), ``logits``
+        ``[B, T, K]`` float32 with ``K = 1 + n_completed`` after the close;
+        ``weights0`` optional ``[T, K]``."""
         dev = self.slots.device
-        B = w.shape[0]
-        if w.dtype != torch.float32 or w.dim() != 2 or w.shape[1] != self.d or not w.is_contiguous():
-            raise ValueError("w must be a contiguous float32 [B, d] tensor")
+        B = w_split.shape[0]
+        if w_split.dtype != torch.bfloat16 or w_split.dim() != 3 or w_split.shape[1:] != (2, self.d) \
+                or not w_split.is_contiguous():
+            raise ValueError("w_split must be a contiguous bfloat16 [B, 2, d] tensor")
         if inter.dim() != 3 or inter.shape[0] != B or inter.shape[1:] != (self.T, self.d) or \
                 inter.dtype != self.slots.dtype or (self.T > 0 and (inter.stride(2) != 1 or inter.stride(1) != self.d)):
             raise ValueError("inter must be [B, T, d] of the store dtype with contiguous rows")
@@ -281,7 +300,7 @@ class SourceStore:
             raise ValueError("closing needs a contiguous [T, d] layer_out like the store")
         stride = inter.stride(0) if B > 1 else self.T * self.d
         rc = lib().attnres_block_prepare(ctypes.byref(self._st), layer_out.data_ptr() if close_block else None,
-                                         int(bool(close_block)), w.data_ptr(), B, inter.data_ptr(), stride,
+                                         int(bool(close_block)), w_split.data_ptr(), B, inter.data_ptr(), stride,
                                          logits.data_ptr(), weights0.data_ptr() if weights0 is not None else None,
                                          float(eps), _stream(dev, stream))
         _check("attnres_block_prepare", rc)

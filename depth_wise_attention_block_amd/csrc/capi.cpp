@@ -238,8 +238,21 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
   return ATTNRES_OK;
 }
 
+ATTNRES_API int attnres_split_queries(const float* w, int32_t n, int32_t d, void* w_split, void* stream) {
+  if (n < 0 || d <= 0 || d > ATTNRES_MAX_D_BF16) return ATTNRES_EINVAL;
+  if (n == 0) return ATTNRES_OK;
+  if (w == nullptr || w_split == nullptr) return ATTNRES_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(w) & 3u) != 0 || (reinterpret_cast<uintptr_t>(w_split) & 1u) != 0)
+    return ATTNRES_EUNSUPPORTED;
+  if (overlap(range(w, (int64_t)n * d * 4), range(w_split, (int64_t)n * d * 4))) return ATTNRES_EALIAS;
+  (void)hipGetLastError();
+  return attnres::launch_split_queries(w, n, d, w_split, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ATTNRES_OK
+             : ATTNRES_ELAUNCH;
+}
+
 ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out, int32_t close_block,
-                                      const float* w, int32_t B, void* inter, int64_t inter_stride, float* logits,
+                                      const void* w, int32_t B, void* inter, int64_t inter_stride, float* logits,
                                       float* weights0, float eps, void* stream) {
   int rc = check_store(st);
   if (rc != ATTNRES_OK) return rc;
@@ -267,7 +280,7 @@ ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out
     if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
     if (weights0 != nullptr && (reinterpret_cast<uintptr_t>(weights0) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
     const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * 2);
-    const Range r_w = range(w, (int64_t)B * d * 4);
+    const Range r_w = range(w, (int64_t)B * 2 * d * 2);
     const Range r_in = range(inter, ((int64_t)(B - 1) * inter_stride + row) * 2);
     const Range r_lg = range(logits, (int64_t)B * T * K * 4);
     const Range r_f = close_block ? range(layer_out, row * 2) : Range{0, 0};
@@ -290,7 +303,7 @@ ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out
     a.B = B;
     a.T = T;
     a.d = d;
-    a.w = w;
+    a.w_split = w;
     a.inter = inter;
     a.inter_stride = inter_stride;
     a.logits = logits;

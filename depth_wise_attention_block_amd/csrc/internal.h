@@ -63,7 +63,7 @@ struct PrepareArgs {
   int B;                // queries
   int64_t T;
   int d;
-  const float* w;       // [B][d]
+  const void* w_split;  // [B][2][d] bf16: query b's hi row, then its lo row
   void* inter;          // [B] rows of [T][d] bf16 at inter_stride elements
   int64_t inter_stride;
   float* logits;        // [B][T][K]
@@ -77,6 +77,9 @@ struct PrepareArgs {
 };
 
 hipError_t launch_block_prepare(const PrepareArgs& a, hipStream_t stream);
+
+// Split float32 queries [n][d] into bf16 hi and lo rows [n][2][d], w ~ hi + lo.
+hipError_t launch_split_queries(const float* w, int64_t n, int d, void* out, hipStream_t stream);
 
 // Phase 2: one later layer of the block.
 struct MergeArgs {

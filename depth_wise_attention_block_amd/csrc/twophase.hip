@@ -12,9 +12,12 @@
 //     z_b,s                                     (float32 logits)
 // R_0 is exactly the block's first-layer residual (no partial source yet).
 // The B x K dot products and B weighted sums are the arithmetic of a small
-// per-token contraction; the weighted sums use v_dot2_f32_bf16 on source pairs
-// (the rows are transposed in registers into (source 2p, source 2p+1) element
-// pairs once per token) with each weight split into bf16 hi + lo.
+// per-token contraction.  The dot products run on v_dot2_f32_bf16 with the
+// queries pre-split into bf16 hi + lo (attnres_split_queries, once per set of
+// frozen queries); the weighted sums run on the matrix cores
+// (v_mfma_f32_4x4x4_16b_bf16): the rows are transposed in registers into
+// (source 2p, source 2p+1) element pairs once per token, which is exactly the
+// MFMA B operand, and each weight enters as bf16 hi + lo.
 //
 // Phase 2, merge_kernel (one launch per later layer of the block).  Per token:
 // update the partial slot with the previous layer's output (copy or add, as in
@@ -35,9 +38,19 @@ constexpr int kMaxInter = kMaxInterSources;   // inter-block sources per pass
 constexpr int kMaxQueries = kMaxBlockQueries; // layer queries per pass
 constexpr int kPairs = kMaxInter / 2;
 constexpr int kNoClose = 0, kCloseCopy = 1, kCloseAdd = 2;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <int kV>
 constexpr int waves_per_simd2() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
+// The inter-block pass holds kK rows of kV vectors per lane.  With 8 rows at
+// kV = 2 it needs about 150 VGPRs: 3 waves per SIMD and no spills run faster
+// than 4 waves with spills to scratch.  4 rows fit in 128 VGPRs (4 waves).
+// (8 rows at kV = 4, d above 14336, cannot fit in 256 and spill a little.)
+template <int kV, int kK>
+constexpr int waves_per_simd_prepare() {
+  return kV == 1 ? (kK <= 4 ? 5 : 4) : kV == 2 ? (kK <= 4 ? 4 : 3) : 2;
+}
 
 // Byte selectors of v_perm_b32 (result byte i <- selector byte i; 0-3 pick the
 // second operand's bytes, 4-7 the first's): (a.lo, b.lo) and (a.hi, b.hi).
@@ -45,14 +58,16 @@ constexpr unsigned kSelLo = 0x05040100u, kSelHi = 0x07060302u;
 
 __device__ __forceinline__ unsigned pack2(float a, float b) { return pack_bf16(a, b); }
 
-template <int kV, int kClose>
-__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd2<kV>())))
+template <int kV, int kClose, int kK>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_prepare<kV, kK>())))
 interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, int64_t src_stride_v,
-                  const float* __restrict__ w, u32x4* __restrict__ inter, int64_t inter_stride_v,
+                  const u32x4* __restrict__ w_split, u32x4* __restrict__ inter, int64_t inter_stride_v,
                   float* __restrict__ logits, float* __restrict__ weights0, float eps, float inv_d,
                   const u32x4* __restrict__ layer_out) {
   __shared__ float red_ss[2][kMaxWaves][kMaxInter];
   __shared__ float red_dt[2][kMaxWaves][kMaxQueries][kMaxInter];
+  // per wave: every query's weights as bf16 pairs (sources 2p, 2p+1), hi and lo
+  __shared__ unsigned a_pairs[kMaxWaves][2][kMaxQueries][kPairs];
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -66,10 +81,10 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
     u32x4* tok = src + t * (int64_t)nvec;
 
     // 1. the K inter-block rows (the last one formed here when closing)
-    u32x4 x[kMaxInter][kV];
+    u32x4 x[kK][kV];
     u32x4 f[kV];
 #pragma unroll
-    for (int s = 0; s < kMaxInter; ++s) {
+    for (int s = 0; s < kK; ++s) {
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
         const int idx = v * nthr + tid;
@@ -90,7 +105,7 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
     }
     if constexpr (kClose != kNoClose) {
 #pragma unroll
-      for (int s = 0; s < kMaxInter; ++s) {
+      for (int s = 0; s < kK; ++s) {
         if (s == K - 1) {
 #pragma unroll
           for (int v = 0; v < kV; ++v) {
@@ -107,7 +122,7 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
     // 2. sums of squares (shared by every query)
     float gss = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxInter; ++s) {
+    for (int s = 0; s < kK; ++s) {
       if (s < K) {
         float ss = 0.f;
 #pragma unroll
@@ -121,19 +136,28 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
 
     // 3. w_b . x_s for every query b and source s
     for (int b = 0; b < B; ++b) {
-      Query<true, kV> q;
-      load_query<true, kV>(q, w + (int64_t)b * nvec * 8, nvec, tid, nthr);
+      u32x4 qhi[kV], qlo[kV];
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int idx = v * nthr + tid;
+        qhi[v] = u32x4{0, 0, 0, 0};
+        qlo[v] = u32x4{0, 0, 0, 0};
+        if (idx < nvec) {
+          qhi[v] = w_split[(int64_t)(2 * b) * nvec + idx];
+          qlo[v] = w_split[(int64_t)(2 * b + 1) * nvec + idx];
+        }
+      }
       float gdt = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxInter; ++s) {
+      for (int s = 0; s < kK; ++s) {
         if (s < K) {
           float dt = 0.f;
 #pragma unroll
           for (int v = 0; v < kV; ++v)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              dt = dot2(x[s][v][k], q.hi[v][k], dt);
-              dt = dot2(x[s][v][k], q.lo[v][k], dt);
+              dt = dot2(x[s][v][k], qhi[v][k], dt);
+              dt = dot2(x[s][v][k], qlo[v][k], dt);
             }
           gdt = put_lane(wave_sum(dt), s, gdt, s16);
         }
@@ -143,7 +167,6 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
     __syncthreads();
 
     // 4. softmax per query: lane L handles query 8r + L/8, source L%8, r = 0, 1
-    float a_r[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int b = 8 * r + (lane >> 3);
@@ -166,13 +189,21 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
         logits[((int64_t)b * T + t) * K + s] = z;
         if (b == 0 && weights0 != nullptr) weights0[t * K + s] = a;
       }
-      a_r[r] = a;
+      // lanes with an even source pack (a_s, a_s+1) as bf16 hi and lo words
+      const float a_next = dpp<kDppXor1>(a, a);
+      if ((s & 1) == 0 && b < kMaxQueries) {
+        const __bf16 h0 = (__bf16)a, h1 = (__bf16)a_next;
+        a_pairs[wave][0][b][s >> 1] = __builtin_bit_cast(unsigned, bf16x2{h0, h1});
+        a_pairs[wave][1][b][s >> 1] = pack_bf16(a - (float)h0, a_next - (float)h1);
+      }
     }
+
+    __builtin_amdgcn_wave_barrier();  // this wave's weight pairs are in LDS
 
     // 5. rows -> source-pair form: x[2p] holds (H_2p[j], H_2p+1[j]) for the even
     //    element j of every word, x[2p+1] the same for the odd element
 #pragma unroll
-    for (int p = 0; p < kPairs; ++p)
+    for (int p = 0; p < kK / 2; ++p)
 #pragma unroll
       for (int v = 0; v < kV; ++v)
 #pragma unroll
@@ -182,42 +213,60 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
           x[2 * p + 1][v][k] = __builtin_amdgcn_perm(eb, ea, kSelHi);
         }
 
-    // 6. R_b = sum_s a_b,s H_s for every query
-    for (int b = 0; b < B; ++b) {
-      const float ab = b < 8 ? a_r[0] : a_r[1];
-      const int base = 8 * (b & 7);
-      unsigned ahi[kPairs], alo[kPairs];
+    // 6. R_b = sum_s a_b,s H_s for every query on the matrix cores:
+    //    v_mfma_f32_4x4x4_16b_bf16 works on 16 blocks of 4 lanes; in a block,
+    //    lane (base+m) gives row m of A (query q0+m's weights for 4 sources),
+    //    lane (base+n) gives column n of B (its own element of those 4
+    //    sources, i.e. two source-pair words) and gets D[m][n] = R_q0+m at its
+    //    element.  Weights enter as bf16 hi + lo (two products per source).
+    const int mq = lane & 3;
+    const int nsg = (K + 3) >> 2;  // source groups of 4
+    for (int q0 = 0; q0 < B; q0 += 4) {
+      short4v ahi[kK / 4], alo[kK / 4];
 #pragma unroll
-      for (int p = 0; p < kPairs; ++p) {
-        const float a0 = (2 * p < K) ? lane_bcast(ab, base + 2 * p) : 0.f;
-        const float a1 = (2 * p + 1 < K) ? lane_bcast(ab, base + 2 * p + 1) : 0.f;
-        const __bf16 h0 = (__bf16)a0, h1 = (__bf16)a1;
-        ahi[p] = __builtin_bit_cast(unsigned, bf16x2{h0, h1});
-        alo[p] = pack2(a0 - (float)h0, a1 - (float)h1);
+      for (int sg = 0; sg < kK / 4; ++sg) {
+        const int qq = min(q0 + mq, kMaxQueries - 1);
+        ahi[sg] = __builtin_bit_cast(short4v, *reinterpret_cast<const u32x2*>(&a_pairs[wave][0][qq][2 * sg]));
+        alo[sg] = __builtin_bit_cast(short4v, *reinterpret_cast<const u32x2*>(&a_pairs[wave][1][qq][2 * sg]));
       }
-      u32x4* row = inter + (int64_t)b * inter_stride_v + t * (int64_t)nvec;
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
         const int idx = v * nthr + tid;
-        float acc[8];
+        // the vector's 8 elements in two halves of 4; half 0's results wait as
+        // packed bf16 words so that every query row goes out as one 16-byte
+        // store (two 8-byte halves of a line written apart cost far more)
+        u32x2 first[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int h = 0; h < 2; ++h) {
+          f32x4 acc[4];
 #pragma unroll
-        for (int p = 0; p < kPairs; ++p) {
-          if (2 * p < K) {
+          for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              acc[2 * k] = dot2(x[2 * p][v][k], ahi[p], acc[2 * k]);
-              acc[2 * k] = dot2(x[2 * p][v][k], alo[p], acc[2 * k]);
-              acc[2 * k + 1] = dot2(x[2 * p + 1][v][k], ahi[p], acc[2 * k + 1]);
-              acc[2 * k + 1] = dot2(x[2 * p + 1][v][k], alo[p], acc[2 * k + 1]);
+          for (int sg = 0; sg < kK / 4; ++sg) {
+            if (sg < nsg) {
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                  const int k = 2 * h + kk;
+                  const u32x2 bw = {x[4 * sg + e][v][k], x[4 * sg + 2 + e][v][k]};
+                  const short4v bop = __builtin_bit_cast(short4v, bw);
+                  acc[2 * kk + e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi[sg], bop, acc[2 * kk + e], 0, 0, 0);
+                  acc[2 * kk + e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo[sg], bop, acc[2 * kk + e], 0, 0, 0);
+                }
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x2 o = {pack_bf16(acc[0][m], acc[1][m]), pack_bf16(acc[2][m], acc[3][m])};
+            if (h == 0) {
+              first[m] = o;
+            } else if (q0 + m < B && idx < nvec) {
+              const u32x4 row = {first[m][0], first[m][1], o[0], o[1]};
+              __builtin_nontemporal_store(row, inter + (int64_t)(q0 + m) * inter_stride_v + t * (int64_t)nvec + idx);
             }
           }
         }
-        u32x4 o;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-        if (idx < nvec) __builtin_nontemporal_store(o, row + idx);
       }
     }
   }
@@ -311,11 +360,25 @@ merge_kernel(u32x4* __restrict__ slot, const u32x4* __restrict__ layer_out, cons
   }
 }
 
-template <int kV, int kClose>
+__global__ void __launch_bounds__(256) split_queries_kernel(const float* __restrict__ w, int64_t n, int d,
+                                                           unsigned short* __restrict__ out) {
+  const int64_t total = n * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t q = i / d, j = i - q * d;
+    const float x = w[i];
+    const __bf16 hi = (__bf16)x;
+    const __bf16 lo = (__bf16)(x - (float)hi);
+    out[(2 * q) * d + j] = __builtin_bit_cast(unsigned short, hi);
+    out[(2 * q + 1) * d + j] = __builtin_bit_cast(unsigned short, lo);
+  }
+}
+
+template <int kV, int kClose, int kK>
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
   const int nvec = a.d / 8;
-  hipLaunchKernelGGL((interblock_kernel<kV, kClose>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
-                     static_cast<u32x4*>(a.store), a.K, a.B, a.T, nvec, a.slot_stride / 8, a.w,
+  hipLaunchKernelGGL((interblock_kernel<kV, kClose, kK>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                     static_cast<u32x4*>(a.store), a.K, a.B, a.T, nvec, a.slot_stride / 8,
+                     static_cast<const u32x4*>(a.w_split),
                      static_cast<u32x4*>(a.inter), a.inter_stride / 8, a.logits, a.weights0, a.eps,
                      1.0f / (float)a.d, static_cast<const u32x4*>(a.layer_out));
   return hipGetLastError();
@@ -331,15 +394,22 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int kClose>
-hipError_t prepare_v(const PrepareArgs& a, hipStream_t stream) {
+// Register footprint follows the number of inter-block rows held: blocks with
+// at most 4 of them use the smaller instance.
+template <int kClose, int kK>
+hipError_t prepare_vk(const PrepareArgs& a, hipStream_t stream) {
   switch (a.vecs_per_lane) {
-    case 1: return launch_prepare<1, kClose>(a, stream);
-    case 2: return launch_prepare<2, kClose>(a, stream);
-    case 3: return launch_prepare<3, kClose>(a, stream);
-    case 4: return launch_prepare<4, kClose>(a, stream);
+    case 1: return launch_prepare<1, kClose, kK>(a, stream);
+    case 2: return launch_prepare<2, kClose, kK>(a, stream);
+    case 3: return launch_prepare<3, kClose, kK>(a, stream);
+    case 4: return launch_prepare<4, kClose, kK>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int kClose>
+hipError_t prepare_v(const PrepareArgs& a, hipStream_t stream) {
+  return a.K <= 4 ? prepare_vk<kClose, 4>(a, stream) : prepare_vk<kClose, kMaxInter>(a, stream);
 }
 
 template <bool kAdd>
@@ -362,6 +432,15 @@ hipError_t launch_block_prepare(const PrepareArgs& a, hipStream_t stream) {
     case PrepareArgs::kAdd: return prepare_v<kCloseAdd>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_split_queries(const float* w, int64_t n, int d, void* out, hipStream_t stream) {
+  int64_t grid = (n * d + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(split_queries_kernel, dim3((unsigned)grid), dim3(256), 0, stream, w, n, d,
+                     static_cast<unsigned short*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_block_merge(const MergeArgs& a, hipStream_t stream) {

@@ -17,7 +17,7 @@ from typing import Callable, Optional, Sequence
 
 import torch
 
-from .binding import MAX_BLOCK_QUERIES, MAX_INTER_SOURCES, SourceStore, aggregate
+from .binding import MAX_BLOCK_QUERIES, MAX_INTER_SOURCES, SourceStore, aggregate, split_queries
 
 
 def closes_block(layer: int, num_layers: int, block_size: int) -> bool:
@@ -32,7 +32,7 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                  on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
                  fused: bool = True, two_phase_from: Optional[int] = None,
                  inter: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                 eps: float = 1e-5):
+                 queries_split: Optional[torch.Tensor] = None, eps: float = 1e-5):
     """Run every layer's aggregation and partial-sum update in stream order.
 
     Per layer one of:
@@ -55,7 +55,9 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     likewise ``[T, 9]`` (each layer writes a ``[T, S_l]`` block at its start) or
     ``[L, T, 9]``.  Two-phase blocks need ``inter`` ``[block_size, T, d]`` (store
     dtype) and ``logits`` (float32, ``block_size * T * 8`` elements) unless
-    ``out`` is ``[L, T, d]``, whose rows then hold the pass's results directly.
+    ``out`` is ``[L, T, d]``, whose rows then hold the pass's results directly;
+    ``queries_split`` ``[L, 2, d]`` (:func:`split_queries` of all queries, done
+    once since the queries are frozen parameters) saves the split per pass.
     ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation is enqueued
     (1-based l).  Returns the output layer's ``(out, weights)`` when
     ``final_query`` is given, else None.
@@ -108,7 +110,10 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
         if n in two_phase and i == 1:
             B = last - l + 1
             K = n  # h_0 and b_1..b_{n-1} once the previous block is closed
-            W = torch.stack([queries[j] for j in range(l - 1, last)])
+            if queries_split is not None:
+                W = queries_split[l - 1:last]
+            else:
+                W = split_queries(torch.stack([queries[j] for j in range(l - 1, last)]))
             block_rows = out[l - 1:last] if out.dim() == 3 else inter[:B]
             lg_buf = logits if out.dim() != 3 else None
             if lg_buf is None:

@@ -22,7 +22,7 @@ from __future__ import annotations
 import torch
 
 from . import synth
-from .binding import MAX_SOURCES, SourceStore
+from .binding import MAX_SOURCES, SourceStore, split_queries
 from .schedule import closes_block, run_schedule
 
 
@@ -85,6 +85,8 @@ class Schedule:
         self.F = [synth.layer_output(T, d, std=layer_out_std, seed=seed, tag=l, device=device)
                   for l in range(layers)]
         self.W = [synth.query(d, seed=seed, device=device, tag=l) for l in range(layers)]
+        # the queries are frozen parameters: split once for the two-phase pass
+        self.W_split = split_queries(torch.stack(self.W))
         self.w_out = synth.query(d, seed=seed, device=device, tag=10_000)
         self.out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
         self.weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)
@@ -105,7 +107,8 @@ class Schedule:
                 dev = self.out.device
                 self._inter = torch.empty((self.block_size, self.T, self.d), dtype=torch.bfloat16, device=dev)
                 self._logits = torch.empty(self.block_size * self.T * 8, dtype=torch.float32, device=dev)
-            kw = dict(two_phase_from=self.TWO_PHASE_FROM, inter=self._inter, logits=self._logits)
+            kw = dict(two_phase_from=self.TWO_PHASE_FROM, inter=self._inter, logits=self._logits,
+                      queries_split=self.W_split)
         elif mode not in ("fused", "unfused"):
             raise ValueError(f"unknown mode {mode!r}")
         run_schedule(self.store, self.F, self.W, self.block_size, out=self.out, weights=self.weights,

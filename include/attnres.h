@@ -197,19 +197,32 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
 #define ATTNRES_MAX_BLOCK_QUERIES 16
 
 /*
+ * attnres_split_queries -- pseudo-queries in the form the two-phase pass reads:
+ * each float32 row w[q] becomes two bf16 rows, hi = bf16(w) and lo =
+ * bf16(w - hi) (both rounded to nearest even), so hi + lo keeps about 16
+ * significant bits.  The queries are layer parameters, frozen after training
+ * (kimi.papertok.ai §4.2), so this runs once, not per token.
+ *   w         device, [n][d] float32.
+ *   w_split   device, [n][2][d] bf16 (row 2q = hi, row 2q+1 = lo).
+ */
+ATTNRES_API int attnres_split_queries(const float* w, int32_t n, int32_t d, void* w_split, void* stream);
+
+/*
  * attnres_block_prepare -- phase 1 for one block.
  *
  * If close_block, layer_out (the previous block's last layer output) is first
  * added into the partial slot and the block is closed, exactly as
  * attnres_accumulate(st, layer_out, 1) (copy when no partial is open);
  * otherwise no partial may be open (ATTNRES_ESTATE).  Then with K = 1 +
- * n_completed inter-block sources (slots [0, K)) and the B queries w[b]:
+ * n_completed inter-block sources (slots [0, K)) and the B queries w_b (given
+ * split, as attnres_split_queries writes them):
  *   z[b][t][s] = w_b . RMSNorm(H_s[t])          -> logits, float32 [B][T][K]
  *   R_b[t]     = sum_s softmax_s(z[b][t]) H_s[t] -> inter row b, bf16 [T][d]
  *   weights0[t][s] = softmax_s(z[0][t])         (optional, float32 [T][K])
  * R_0 is the residual of the block's first layer.
  *
- *   w             device, [B][d] float32, 16-byte aligned.
+ *   w_split       device, [B][2][d] bf16 from attnres_split_queries, 16-byte
+ *                 aligned.
  *   B             1..ATTNRES_MAX_BLOCK_QUERIES.
  *   inter         device, B rows of [T][d] bf16, row b at element b*inter_stride
  *                 (0 means T*d); 16-byte aligned.
@@ -218,7 +231,7 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
  * (ATTNRES_EALIAS).  *st is updated on success only.
  */
 ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out, int32_t close_block,
-                                      const float* w, int32_t B, void* inter, int64_t inter_stride,
+                                      const void* w_split, int32_t B, void* inter, int64_t inter_stride,
                                       float* logits, float* weights0, float eps, void* stream);
 
 /*

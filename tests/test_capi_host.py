@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -236,6 +236,11 @@ def test_two_phase_checks_and_bookkeeping(lib):
     assert merge(f=None) == B.EINVAL and merge(out=None) == B.EINVAL
     assert merge(out=SRC) == B.EALIAS and merge(out=INTER + 16) == B.EALIAS and merge(wts=LOG) == B.EALIAS
     assert (st.n_completed, st.partial_valid) == (0, 0)
+
+    split = B.lib().attnres_split_queries
+    assert split(None, 2, 8, OUT, None) == B.EINVAL and split(W, -1, 8, OUT, None) == B.EINVAL
+    assert split(W + 2, 2, 8, OUT, None) == B.EUNSUPPORTED and split(W, 2, 8, W + 16, None) == B.EALIAS
+    assert split(None, 0, 8, None, None) == B.OK
 
     rc, st0 = _store(T=0)
     call = lambda: B.lib().attnres_block_prepare(ctypes.byref(st0), None, 0, None, 12, None, 0, None, None,

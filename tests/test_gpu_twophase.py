@@ -15,6 +15,19 @@ from tests.gpu_util import compare, device, host, note, oracle_aggregate, same_b
 pytestmark = pytest.mark.gpu
 
 
+def test_split_queries_is_round_to_nearest_hi_then_lo():
+    dev = device()
+    w = synth.query(7176, seed=4, device=dev).view(1, -1).repeat(3, 1) * torch.tensor([[1.0], [1e-3], [37.0]],
+                                                                                     device=dev)
+    w = w.contiguous()
+    ws = B.split_queries(w)
+    torch.cuda.synchronize()
+    hw = host(w)
+    hi = orc.bf16_round(hw)
+    lo = orc.bf16_round((hw - hi).astype(np.float32))
+    assert same_bits(ws[:, 0], hi) and same_bits(ws[:, 1], lo)
+
+
 def _store(T, d, seed, n_completed, partial_valid, dev):
     st = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev)
     synth.sources(9, T, d, scale=(0.5, 50.0), seed=seed, out=st.slots)
@@ -24,7 +37,8 @@ def _store(T, d, seed, n_completed, partial_valid, dev):
 
 @pytest.mark.parametrize("T,d", [(37, 7168), (5, 264), (300, 7176)])
 @pytest.mark.parametrize("n_completed,partial_valid,close", [(0, False, False), (3, False, False), (6, True, True),
-                                                            (4, False, True), (7, False, False)])
+                                                            (4, False, True), (7, False, False),
+                                                            (2, True, True), (1, False, True)])
 @pytest.mark.parametrize("Bq", [1, 12, 16])
 def test_prepare_matches_oracle(T, d, n_completed, partial_valid, close, Bq):
     dev = device()
@@ -37,7 +51,7 @@ def test_prepare_matches_oracle(T, d, n_completed, partial_valid, close, Bq):
     inter = torch.empty((Bq, T, d), dtype=torch.bfloat16, device=dev)
     logits = torch.empty((Bq, T, K), dtype=torch.float32, device=dev)
     w0 = torch.empty((T, K), dtype=torch.float32, device=dev)
-    st.block_prepare(F if close else None, close, W, inter, logits, w0)
+    st.block_prepare(F if close else None, close, B.split_queries(W), inter, logits, w0)
     torch.cuda.synchronize()
     assert st.n_completed == K - 1 and not st.partial_valid
     H = slots_before[:K].copy()
@@ -65,7 +79,7 @@ def test_merge_matches_oracle_through_a_block(T, d):
     Fs = [synth.layer_output(T, d, std=0.3, seed=b, tag=50 + b, device=dev) for b in range(Bq)]
     inter = torch.empty((Bq, T, d), dtype=torch.bfloat16, device=dev)
     logits = torch.empty((Bq, T, K), dtype=torch.float32, device=dev)
-    st.block_prepare(None, False, W, inter, logits)
+    st.block_prepare(None, False, B.split_queries(W), inter, logits)
     partial = None
     for i in range(2, Bq + 1):
         note(f"merge layer {i} T={T} d={d}")
@@ -86,7 +100,7 @@ def test_merge_in_place_over_the_inter_row():
     W = torch.stack([synth.query(d, seed=b, device=dev, tag=60 + b) for b in range(2)])
     inter = torch.empty((2, T, d), dtype=torch.bfloat16, device=dev)
     logits = torch.empty((2, T, K), dtype=torch.float32, device=dev)
-    st.block_prepare(None, False, W, inter, logits)
+    st.block_prepare(None, False, B.split_queries(W), inter, logits)
     ref_store = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev, slots=st.slots.clone())
     ref_store.set_state(st.n_completed, st.partial_valid)
     F = synth.layer_output(T, d, std=1.0, seed=3, tag=61, device=dev)
