@@ -163,19 +163,36 @@ def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None =
     return out, weights
 
 
+def prepared_query_shape(n: int, d: int):
+    """Shape of :func:`split_queries`' output for n queries of width d:
+    ``[ceil(n/4), 2, d/8, 4, 8]`` bf16 -- group, plane (hi, lo), 8-element chunk,
+    query within the group, element."""
+    return ((n + 3) // 4, 2, d // 8, 4, 8)
+
+
 def split_queries(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """``attnres_split_queries``: float32 queries ``[n, d]`` -> bf16 ``[n, 2, d]``
-    (hi, lo) as the two-phase pass reads them."""
+    """``attnres_split_queries``: float32 queries ``[n, d]`` -> the prepared
+    bf16 form ``prepared_query_shape(n, d)`` (hi and lo halves, queries grouped
+    by four) that the two-phase pass reads."""
     if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w must be a contiguous float32 [n, d] tensor")
     n, d = w.shape
+    shape = prepared_query_shape(n, d)
     if out is None:
-        out = torch.empty((n, 2, d), dtype=torch.bfloat16, device=w.device)
-    if out.dtype != torch.bfloat16 or out.shape != (n, 2, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 [n, 2, d] tensor")
+        out = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 {list(shape)} tensor")
     _check("attnres_split_queries", lib().attnres_split_queries(w.data_ptr(), n, d, out.data_ptr(),
                                                                 _stream(w.device, stream)))
     return out
+
+
+def unpack_prepared_queries(ws: torch.Tensor, n: int) -> torch.Tensor:
+    """Inverse layout of :func:`split_queries` (no arithmetic): ``[n, 2, d]``
+    with plane 0 = hi, plane 1 = lo."""
+    G, P, C, four, eight = ws.shape
+    rows = ws.permute(0, 3, 1, 2, 4).reshape(G * four, P, C * eight)
+    return rows[:n]
 
 
 class SourceStore:
@@ -277,15 +294,15 @@ class SourceStore:
                       logits: torch.Tensor, weights0=None, *, eps=1e-5, stream=None):
         """``attnres_block_prepare``: optionally close the open block with
         ``layer_out``, then one pass over the K inter-block sources for the B
-        queries ``w_split`` ``[B, 2, d]`` (from :func:`split_queries`).
-        ``inter`` is ``[B, T, d]`` (rows may be strided along dim 0), ``logits``
+        queries ``w_split`` (:func:`split_queries` of the B queries).  ``inter``
+        is ``[B, T, d]`` (rows may be strided along dim 0), ``logits``
         ``[B, T, K]`` float32 with ``K = 1 + n_completed`` after the close;
         ``weights0`` optional ``[T, K]``."""
         dev = self.slots.device
-        B = w_split.shape[0]
-        if w_split.dtype != torch.bfloat16 or w_split.dim() != 3 or w_split.shape[1:] != (2, self.d) \
+        B = inter.shape[0] if inter.dim() == 3 else -1
+        if w_split.dtype != torch.bfloat16 or tuple(w_split.shape) != prepared_query_shape(B, self.d) \
                 or not w_split.is_contiguous():
-            raise ValueError("w_split must be a contiguous bfloat16 [B, 2, d] tensor")
+            raise ValueError("w_split must be split_queries() of the B queries (contiguous bfloat16)")
         if inter.dim() != 3 or inter.shape[0] != B or inter.shape[1:] != (self.T, self.d) or \
                 inter.dtype != self.slots.dtype or (self.T > 0 and (inter.stride(2) != 1 or inter.stride(1) != self.d)):
             raise ValueError("inter must be [B, T, d] of the store dtype with contiguous rows")

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/attnres.h"
+#include "attnres.h"
 #include "internal.h"
 
 static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
@@ -21,9 +21,13 @@ int elems_per_vec(int32_t dtype) { return attnres::kVecBytes / elem_bytes(dtype)
 bool known_dtype(int32_t dtype) { return dtype == ATTNRES_BF16 || dtype == ATTNRES_F32; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Bytes of n prepared queries: ceil(n / 4) groups of [2][d / 8][4][8] bf16.
+int64_t prepared_query_bytes(int64_t n, int d) { return ATTNRES_PREPARED_QUERY_BYTES(n, d); }
+
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
+
 Range range(const void* p, int64_t bytes) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
   return Range{lo, lo + static_cast<uintptr_t>(bytes)};
@@ -239,12 +243,11 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
 }
 
 ATTNRES_API int attnres_split_queries(const float* w, int32_t n, int32_t d, void* w_split, void* stream) {
-  if (n < 0 || d <= 0 || d > ATTNRES_MAX_D_BF16) return ATTNRES_EINVAL;
+  if (n < 0 || n > (1 << 20) || d <= 0 || d > ATTNRES_MAX_D_BF16) return ATTNRES_EINVAL;
   if (n == 0) return ATTNRES_OK;
   if (w == nullptr || w_split == nullptr) return ATTNRES_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(w) & 3u) != 0 || (reinterpret_cast<uintptr_t>(w_split) & 1u) != 0)
-    return ATTNRES_EUNSUPPORTED;
-  if (overlap(range(w, (int64_t)n * d * 4), range(w_split, (int64_t)n * d * 4))) return ATTNRES_EALIAS;
+  if (d % 8 != 0 || !aligned16(w) || !aligned16(w_split)) return ATTNRES_EUNSUPPORTED;
+  if (overlap(range(w, (int64_t)n * d * 4), range(w_split, prepared_query_bytes(n, d)))) return ATTNRES_EALIAS;
   (void)hipGetLastError();
   return attnres::launch_split_queries(w, n, d, w_split, static_cast<hipStream_t>(stream)) == hipSuccess
              ? ATTNRES_OK
@@ -280,7 +283,7 @@ ATTNRES_API int attnres_block_prepare(attnres_store_t* st, const void* layer_out
     if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
     if (weights0 != nullptr && (reinterpret_cast<uintptr_t>(weights0) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
     const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * 2);
-    const Range r_w = range(w, (int64_t)B * 2 * d * 2);
+    const Range r_w = range(w, prepared_query_bytes(B, d));
     const Range r_in = range(inter, ((int64_t)(B - 1) * inter_stride + row) * 2);
     const Range r_lg = range(logits, (int64_t)B * T * K * 4);
     const Range r_f = close_block ? range(layer_out, row * 2) : Range{0, 0};

@@ -41,6 +41,8 @@ constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- 7-i in 8
 constexpr int kDppMirror = 0x140;     // row_mirror: lane i <- 15-i in 16
 constexpr int kDppBcast15 = 0x142;    // row_bcast:15 -> next row
 constexpr int kDppBcast31 = 0x143;    // row_bcast:31 -> rows 2,3
+constexpr int kDppRor4 = 0x124;       // row_ror:4: rotate each 16-lane row by 4
+constexpr int kDppRor8 = 0x128;       // row_ror:8: rotate each 16-lane row by 8
 
 template <int kCtrl, int kRowMask = 0xF>
 __device__ __forceinline__ float dpp(float old, float src) {

@@ -25,6 +25,13 @@ def closes_block(layer: int, num_layers: int, block_size: int) -> bool:
     return layer % block_size == 0 or layer == num_layers
 
 
+def block_queries_split(queries: Sequence[torch.Tensor], block_size: int):
+    """:func:`split_queries` of every block's queries (list indexed by block - 1)."""
+    L = len(queries)
+    return [split_queries(torch.stack(list(queries[l0:min(l0 + block_size, L)])))
+            for l0 in range(0, L, block_size)]
+
+
 def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], queries: Sequence[torch.Tensor],
                  block_size: int, *, out: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
                  final_query: Optional[torch.Tensor] = None, final_out: Optional[torch.Tensor] = None,
@@ -32,7 +39,7 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                  on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
                  fused: bool = True, two_phase_from: Optional[int] = None,
                  inter: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                 queries_split: Optional[torch.Tensor] = None, eps: float = 1e-5):
+                 queries_split: Optional[Sequence[Optional[torch.Tensor]]] = None, eps: float = 1e-5):
     """Run every layer's aggregation and partial-sum update in stream order.
 
     Per layer one of:
@@ -56,8 +63,9 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     ``[L, T, 9]``.  Two-phase blocks need ``inter`` ``[block_size, T, d]`` (store
     dtype) and ``logits`` (float32, ``block_size * T * 8`` elements) unless
     ``out`` is ``[L, T, d]``, whose rows then hold the pass's results directly;
-    ``queries_split`` ``[L, 2, d]`` (:func:`split_queries` of all queries, done
-    once since the queries are frozen parameters) saves the split per pass.
+    ``queries_split[n-1]`` (:func:`split_queries` of block n's queries, done
+    once since the queries are frozen parameters) saves the split per pass;
+    ``block_queries_split`` builds that list.
     ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation is enqueued
     (1-based l).  Returns the output layer's ``(out, weights)`` when
     ``final_query`` is given, else None.
@@ -110,8 +118,8 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
         if n in two_phase and i == 1:
             B = last - l + 1
             K = n  # h_0 and b_1..b_{n-1} once the previous block is closed
-            if queries_split is not None:
-                W = queries_split[l - 1:last]
+            if queries_split is not None and queries_split[n - 1] is not None:
+                W = queries_split[n - 1]
             else:
                 W = split_queries(torch.stack([queries[j] for j in range(l - 1, last)]))
             block_rows = out[l - 1:last] if out.dim() == 3 else inter[:B]

@@ -22,8 +22,8 @@ from __future__ import annotations
 import torch
 
 from . import synth
-from .binding import MAX_SOURCES, SourceStore, split_queries
-from .schedule import closes_block, run_schedule
+from .binding import MAX_SOURCES, SourceStore
+from .schedule import block_queries_split, closes_block, run_schedule
 
 
 class LayerStep:
@@ -85,8 +85,8 @@ class Schedule:
         self.F = [synth.layer_output(T, d, std=layer_out_std, seed=seed, tag=l, device=device)
                   for l in range(layers)]
         self.W = [synth.query(d, seed=seed, device=device, tag=l) for l in range(layers)]
-        # the queries are frozen parameters: split once for the two-phase pass
-        self.W_split = split_queries(torch.stack(self.W))
+        # the queries are frozen parameters: prepared once for the two-phase pass
+        self.W_split = block_queries_split(self.W, block_size)
         self.w_out = synth.query(d, seed=seed, device=device, tag=10_000)
         self.out = torch.empty((T, d), dtype=torch.bfloat16, device=device)
         self.weights = torch.empty((T, MAX_SOURCES), dtype=torch.float32, device=device)

@@ -198,13 +198,18 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
 
 /*
  * attnres_split_queries -- pseudo-queries in the form the two-phase pass reads:
- * each float32 row w[q] becomes two bf16 rows, hi = bf16(w) and lo =
+ * each float32 element becomes two bf16 values, hi = bf16(w) and lo =
  * bf16(w - hi) (both rounded to nearest even), so hi + lo keeps about 16
  * significant bits.  The queries are layer parameters, frozen after training
  * (kimi.papertok.ai §4.2), so this runs once, not per token.
- *   w         device, [n][d] float32.
- *   w_split   device, [n][2][d] bf16 (row 2q = hi, row 2q+1 = lo).
+ *   w         device, [n][d] float32, 16-byte aligned; d a multiple of 8.
+ *   w_split   device, ATTNRES_PREPARED_QUERY_BYTES(n, d) bytes, 16-byte
+ *             aligned: queries in groups of four, bf16
+ *             [ceil(n/4)][2][d/8][4][8] -- group g, plane (0 hi, 1 lo), 8-element
+ *             chunk c, query 4g+m, element 8c+e; queries past n are zero.
+ * ATTNRES_EUNSUPPORTED for d % 8 != 0 or misaligned pointers.
  */
+#define ATTNRES_PREPARED_QUERY_BYTES(n, d) ((((int64_t)(n) + 3) / 4) * 16 * (int64_t)(d))
 ATTNRES_API int attnres_split_queries(const float* w, int32_t n, int32_t d, void* w_split, void* stream);
 
 /*
@@ -221,8 +226,8 @@ ATTNRES_API int attnres_split_queries(const float* w, int32_t n, int32_t d, void
  *   weights0[t][s] = softmax_s(z[0][t])         (optional, float32 [T][K])
  * R_0 is the residual of the block's first layer.
  *
- *   w_split       device, [B][2][d] bf16 from attnres_split_queries, 16-byte
- *                 aligned.
+ *   w_split       device, the B queries as attnres_split_queries prepares them
+ *                 (ATTNRES_PREPARED_QUERY_BYTES(B, d) bytes), 16-byte aligned.
  *   B             1..ATTNRES_MAX_BLOCK_QUERIES.
  *   inter         device, B rows of [T][d] bf16, row b at element b*inter_stride
  *                 (0 means T*d); 16-byte aligned.

@@ -241,6 +241,7 @@ def test_two_phase_checks_and_bookkeeping(lib):
     assert split(None, 2, 8, OUT, None) == B.EINVAL and split(W, -1, 8, OUT, None) == B.EINVAL
     assert split(W + 2, 2, 8, OUT, None) == B.EUNSUPPORTED and split(W, 2, 8, W + 16, None) == B.EALIAS
     assert split(None, 0, 8, None, None) == B.OK
+    assert split(W, 2, 12, OUT, None) == B.EUNSUPPORTED and split(W, 2, 8, OUT + 8, None) == B.EUNSUPPORTED
 
     rc, st0 = _store(T=0)
     call = lambda: B.lib().attnres_block_prepare(ctypes.byref(st0), None, 0, None, 12, None, 0, None, None,

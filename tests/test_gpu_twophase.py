@@ -22,10 +22,13 @@ def test_split_queries_is_round_to_nearest_hi_then_lo():
     w = w.contiguous()
     ws = B.split_queries(w)
     torch.cuda.synchronize()
+    assert tuple(ws.shape) == (1, 2, 7176 // 8, 4, 8)
+    rows = B.unpack_prepared_queries(ws, 4)
     hw = host(w)
     hi = orc.bf16_round(hw)
     lo = orc.bf16_round((hw - hi).astype(np.float32))
-    assert same_bits(ws[:, 0], hi) and same_bits(ws[:, 1], lo)
+    assert same_bits(rows[:3, 0], hi) and same_bits(rows[:3, 1], lo)
+    assert not rows[3].any(), "the group's padding query is zero"
 
 
 def _store(T, d, seed, n_completed, partial_valid, dev):
