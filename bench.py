@@ -19,7 +19,6 @@ Other workloads (``--workload``) are for measurement notes, not bench lines.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,7 +30,6 @@ sys.path.insert(0, REPO)
 METRIC = "Block AttnRes tokens/s and achieved HBM GB/s (% peak), d=7168, S=9, bf16"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 COUNTERS_FILE = os.path.join(REPO, "profiles", "aggregate_prefill_t262144_counters.json")
-AGG_SOURCE = os.path.join(REPO, "depth_wise_attention_block_amd", "csrc", "aggregate.hip")
 
 
 def parse():
@@ -57,11 +55,6 @@ def parse():
     return p.parse_args()
 
 
-def source_digest() -> str:
-    with open(AGG_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def counter_traffic(kernel: str, T: int):
     """HBM bytes per launch of ``kernel`` from the committed counter summary, if
     it was taken on the current kernel source at this T; else None."""
@@ -70,7 +63,8 @@ def counter_traffic(kernel: str, T: int):
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("aggregate_source_sha256") != source_digest() or c.get("workload", {}).get("T") != T:
+    from depth_wise_attention_block_amd.profiling import aggregate_source_digest
+    if c.get("aggregate_source_sha256") != aggregate_source_digest() or c.get("workload", {}).get("T") != T:
         return None
     k = c.get("kernels", {}).get(kernel)
     return None if k is None else k.get("traffic_bytes_per_launch")

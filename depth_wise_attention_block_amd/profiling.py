@@ -2,14 +2,14 @@
 
     python -m depth_wise_attention_block_amd.profiling trace  --csv KERNEL_STATS.csv --cmd "..." --out X.txt
     python -m depth_wise_attention_block_amd.profiling trace  --db RESULTS.db       --cmd "..." --out X.txt
-    python -m depth_wise_attention_block_amd.profiling counters --fetch FETCH.csv --write WRITE.csv \
-        --cmd-fetch "..." --cmd-write "..." --out X.json
+    python -m depth_wise_attention_block_amd.profiling counters \
+        --run LABEL FETCH.csv WRITE.csv "fetch command" "write command" [--run ...] --out X.json
 
 ``counters`` calibrates each counter with the plain-copy kernel that
-``bench.py --with-copy`` launches (it moves a known T*d bf16 in and out), and
-records the HBM bytes per aggregation launch together with the SHA-256 of the
-kernel source it was taken on; ``bench.py`` reports that traffic only while the
-source is unchanged.
+``bench.py --with-copy`` launches in every run (it moves a known T*d bf16 in and
+out), and records the HBM bytes per launch of each kernel together with the
+SHA-256 of the sources the aggregation kernel is compiled from;
+``bench.py`` reports that traffic only while those sources are unchanged.
 """
 
 from __future__ import annotations
@@ -23,7 +23,16 @@ import os
 import sqlite3
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-AGG_SOURCE = os.path.join(HERE, "csrc", "aggregate.hip")
+# every file the aggregation kernels are compiled from
+AGG_SOURCES = tuple(os.path.join(HERE, "csrc", f) for f in ("aggregate.hip", "device_common.h", "internal.h"))
+
+
+def aggregate_source_digest() -> str:
+    h = hashlib.sha256()
+    for path in AGG_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 COPY_KERNEL = "accumulate_kernel<true, true>"
 
@@ -61,11 +70,27 @@ def kernel_stats_from_csv(csv_path: str):
     return out
 
 
-def write_trace_summary(stats, cmd: str, out_path: str, top: int = 8) -> None:
+def dispatch_durations(trace_csv: str, match: str, last: int):
+    """Durations (us) of the last ``last`` dispatches whose kernel name contains
+    ``match``, in launch order, from a ``*_kernel_trace.csv``."""
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if match in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), _short(r["Kernel_Name"]),
+                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    return [(n, d) for _, n, d in rows[-last:]]
+
+
+def write_trace_summary(stats, cmd: str, out_path: str, top: int = 8, dispatches=None) -> None:
     lines = [f"# rocprofv3 kernel-trace summary", f"# command: {cmd}", "#",
              f"# {'kernel':<60} {'calls':>6} {'total_us':>12} {'avg_us':>10}"]
     for name, calls, tot, avg in sorted(stats, key=lambda r: -r[2])[:top]:
         lines.append(f"  {_short(name)[:60]:<60} {calls:>6} {tot:>12.1f} {avg:>10.1f}")
+    if dispatches:
+        lines += ["#", "# last dispatches in launch order (us):"]
+        lines += [f"  {n[:60]:<60} {d:>10.1f}" for n, d in dispatches]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -79,35 +104,42 @@ def _per_kernel(csv_path: str, counter: str):
     return vals
 
 
-def counters_summary(fetch_csv: str, write_csv: str, T: int, d: int, S: int, cmd_fetch: str, cmd_write: str):
-    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
-    write = _per_kernel(write_csv, "WRITE_SIZE")
+def counters_summary(runs, T: int, d: int, S: int):
+    """``runs``: list of (label, fetch_csv, write_csv, fetch_cmd, write_cmd).
+    Each run is calibrated by its own copy kernel; kernels seen in several runs
+    keep the first run's figures."""
     kib = 1024.0
     mean = lambda v: sum(v) / len(v)
     copy_bytes = 2 * T * d                       # the copy reads and writes T*d bf16
-    f_scale = copy_bytes / (mean(fetch[COPY_KERNEL]) * kib)
-    w_scale = copy_bytes / (mean(write[COPY_KERNEL]) * kib)
-    kernels = {}
-    for name in sorted(set(fetch) & set(write)):
-        if not name.startswith(("aggregate_kernel", "accumulate_kernel")):
-            continue
-        fb = mean(fetch[name]) * kib * f_scale
-        wb = mean(write[name]) * kib * w_scale
-        entry = {"fetch_kib_raw": mean(fetch[name]), "write_kib_raw": mean(write[name]),
-                 "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb,
-                 "launches": len(fetch[name])}
-        alg = algorithmic_bytes(name, T, d, S)
-        if alg is not None:
-            entry.update({"algorithmic_read_bytes": alg[0], "algorithmic_write_bytes": alg[1],
-                          "traffic_over_algorithmic": (fb + wb) / (alg[0] + alg[1])})
-        kernels[name] = entry
+    commands, calibration, kernels = {}, {}, {}
+    for label, fetch_csv, write_csv, cmd_fetch, cmd_write in runs:
+        fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+        write = _per_kernel(write_csv, "WRITE_SIZE")
+        f_scale = copy_bytes / (mean(fetch[COPY_KERNEL]) * kib)
+        w_scale = copy_bytes / (mean(write[COPY_KERNEL]) * kib)
+        commands[label] = {"FETCH_SIZE": cmd_fetch, "WRITE_SIZE": cmd_write}
+        calibration[label] = {"kernel": COPY_KERNEL, "bytes_moved_each_way": copy_bytes,
+                              "fetch_scale": f_scale, "write_scale": w_scale}
+        for name in sorted(set(fetch) & set(write)):
+            if name in kernels or not name.startswith(("aggregate_kernel", "accumulate_kernel")):
+                continue
+            fb = mean(fetch[name]) * kib * f_scale
+            wb = mean(write[name]) * kib * w_scale
+            entry = {"run": label, "fetch_kib_raw": mean(fetch[name]), "write_kib_raw": mean(write[name]),
+                     "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                     "traffic_bytes_per_launch": fb + wb, "launches": len(fetch[name])}
+            alg = algorithmic_bytes(name, T, d, S)
+            if alg is not None:
+                entry.update({"algorithmic_read_bytes": alg[0], "algorithmic_write_bytes": alg[1],
+                              "traffic_over_algorithmic": (fb + wb) / (alg[0] + alg[1])})
+            kernels[name] = entry
     return {
         "workload": {"T": T, "d": d, "S": S},
-        "commands": {"FETCH_SIZE": cmd_fetch, "WRITE_SIZE": cmd_write},
-        "copy_calibration": {"kernel": COPY_KERNEL, "bytes_moved_each_way": copy_bytes,
-                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "commands": commands,
+        "copy_calibration": calibration,
         "kernels": kernels,
-        "aggregate_source_sha256": hashlib.sha256(open(AGG_SOURCE, "rb").read()).hexdigest(),
+        "aggregate_sources": [os.path.relpath(p, os.path.dirname(HERE)) for p in AGG_SOURCES],
+        "aggregate_source_sha256": aggregate_source_digest(),
     }
 
 
@@ -119,11 +151,11 @@ def main():
     t.add_argument("--csv")
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--dispatches", nargs=3, metavar=("TRACE_CSV", "NAME_SUBSTRING", "LAST"),
+                   help="also list the last LAST dispatches of matching kernels")
     c = sub.add_parser("counters")
-    c.add_argument("--fetch", required=True)
-    c.add_argument("--write", required=True)
-    c.add_argument("--cmd-fetch", required=True)
-    c.add_argument("--cmd-write", required=True)
+    c.add_argument("--run", nargs=5, action="append", required=True,
+                   metavar=("LABEL", "FETCH_CSV", "WRITE_CSV", "FETCH_CMD", "WRITE_CMD"))
     c.add_argument("--T", type=int, default=262144)
     c.add_argument("--d", type=int, default=7168)
     c.add_argument("--S", type=int, default=9)
@@ -131,9 +163,10 @@ def main():
     a = p.parse_args()
     if a.what == "trace":
         stats = kernel_stats_from_db(a.db) if a.db else kernel_stats_from_csv(a.csv)
-        write_trace_summary(stats, a.cmd, a.out)
+        disp = dispatch_durations(a.dispatches[0], a.dispatches[1], int(a.dispatches[2])) if a.dispatches else None
+        write_trace_summary(stats, a.cmd, a.out, dispatches=disp)
     else:
-        s = counters_summary(a.fetch, a.write, a.T, a.d, a.S, a.cmd_fetch, a.cmd_write)
+        s = counters_summary(a.run, a.T, a.d, a.S)
         with open(a.out, "w") as f:
             json.dump(s, f, indent=1)
             f.write("\n")

@@ -50,8 +50,9 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
         when it was the block's last layer) and aggregates with w_l;
       * ``two_phase_from=n0``: blocks n >= n0 run the two-phase schedule --
         one ``attnres_block_prepare`` (closing the previous block, then one pass
-        over h_0, b_1..b_{n-1} for all the block's queries; its first query's
-        result is the block's first residual) and one ``attnres_block_merge``
+        over h_0, b_1..b_{n-1} for all the block's queries -- one pass per 16
+        queries for longer blocks; its first query's result is the block's first
+        residual) and one ``attnres_block_merge``
         per later layer; other blocks run as in the default.
     The output layer's aggregation is fused with the last update.  All modes
     agree with the oracle; the fused and unfused ones bit for bit with each
@@ -104,8 +105,6 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     two_phase = set()
     if two_phase_from is not None:
         two_phase = {n for n in range(max(1, two_phase_from), num_blocks + 1) if n <= MAX_INTER_SOURCES}
-        if block_size > MAX_BLOCK_QUERIES:
-            raise ValueError(f"two-phase blocks hold at most {MAX_BLOCK_QUERIES} layers")
         if two_phase and out.dim() != 3 and (inter is None or logits is None):
             inter = torch.empty((block_size, T, d), dtype=store.slots.dtype, device=dev)
             logits = torch.empty(block_size * T * MAX_INTER_SOURCES, dtype=torch.float32, device=dev)
@@ -128,8 +127,14 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                 lg_buf = torch.empty(B * T * K, dtype=torch.float32, device=dev)
             block_logits = lg_buf[: B * T * K].view(B, T, K)
             a = wview(l, K)
-            store.block_prepare(layer_outputs[l - 2] if l > 1 else None, l > 1, W, block_rows, block_logits, a,
-                                eps=eps)
+            # one pass per MAX_BLOCK_QUERIES queries (groups of four in W); only
+            # the first closes the previous block
+            for q0 in range(0, B, MAX_BLOCK_QUERIES):
+                q1 = min(q0 + MAX_BLOCK_QUERIES, B)
+                first = q0 == 0
+                store.block_prepare(layer_outputs[l - 2] if first and l > 1 else None, first and l > 1,
+                                    W[q0 // 4:(q1 + 3) // 4], block_rows[q0:q1], block_logits[q0:q1],
+                                    a if first else None, eps=eps)
             r = block_rows[0]
         elif n in two_phase:
             a = wview(l, n + 1)

@@ -116,13 +116,10 @@ def test_merge_in_place_over_the_inter_row():
     assert torch.equal(same.view(torch.int16), separate.view(torch.int16)) and torch.equal(wa, wb)
 
 
-@pytest.mark.parametrize("two_phase_from", [1, 2, 4])
-@pytest.mark.parametrize("out3d", [True, False])
-def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
-    """30 layers in blocks of 4 (8 blocks, up to 9 sources), every layer compared."""
+def _check_schedule(L, Bsz, T, d, two_phase_from, out3d, tag):
+    """Every layer of an L-layer schedule in blocks of Bsz against the oracle."""
     dev = device()
-    L, Bsz, T, d = 30, 4, 300, 520
-    note(f"two-phase schedule from block {two_phase_from} out3d={out3d}")
+    note(f"{tag}: L={L} block={Bsz} T={T} d={d} two-phase from {two_phase_from} out3d={out3d}")
     store = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev)
     synth.fill_normal_(store.h0, 1.0, seed=1, tag=1)
     Fs = [synth.layer_output(T, d, std=0.1, seed=1, tag=l, device=dev) for l in range(L)]
@@ -145,6 +142,7 @@ def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
         assert same_bits(store.slots[k + 1], b), f"block {k + 1}"
     # rebuild each layer's sources to size the extra rounding of the inter part
     blocks = ref["blocks"]
+    first_two_phase = two_phase_from if two_phase_from is not None else L + 1
     for l in range(1, L + 1):
         n, i = (l - 1) // Bsz + 1, (l - 1) % Bsz + 1
         srcs = [host(store.h0)] + blocks[:n - 1]
@@ -154,10 +152,28 @@ def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
                 part = orc.accumulate(part, host(Fs[j - 1]), "bf16")
             srcs.append(part)
         Hs = np.stack(srcs)
-        extra = weighted_abs(Hs, ref["a"][l - 1], n) if (n >= two_phase_from and i >= 2) else None
+        extra = weighted_abs(Hs, ref["a"][l - 1], n) if (n >= first_two_phase and i >= 2) else None
         compare(got_r[l - 1], got_a[l - 1], ref["r"][l - 1], ref["a"][l - 1], True, f"layer {l} S={len(srcs)}",
                 extra_rounding=extra)
     compare(host(final_r), host(final_a), ref["final_r"], ref["final_a"], True, "output layer")
+
+
+@pytest.mark.parametrize("two_phase_from", [1, 2, 4])
+@pytest.mark.parametrize("out3d", [True, False])
+def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
+    """30 layers in blocks of 4 (8 blocks, up to 9 sources), every layer compared."""
+    _check_schedule(30, 4, 300, 520, two_phase_from, out3d, "two-phase schedule")
+
+
+@pytest.mark.parametrize("two_phase_from", [1, None])
+def test_sublayer_granularity_schedule(two_phase_from):
+    """One aggregation per residual sublayer (attention and MLP each with its own
+    query), as in the reduced attention-residuals study of llm-atlas.k1412.top/k3
+    (16 transformer blocks, 32 residual sublayers): 20 layers = 40 sublayer
+    steps in blocks of 10 layers = 20 steps.  Two-phase blocks then hold 20
+    queries, more than one inter-block pass takes: the schedule runs two passes
+    per block, the first closing the previous block."""
+    _check_schedule(40, 20, 96, 264, two_phase_from, False, "sublayer schedule")
 
 
 def test_schedule_93_two_phase_sampled():
