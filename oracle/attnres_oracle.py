@@ -27,7 +27,12 @@ notes): eps sits inside the square root; the RMSNorm has no gain; there is no
 temperature; values are the raw sources; the first layer of a block has no
 partial source at all; a block representation is the plain sum of its layers'
 outputs; a bf16 store forms each partial sum in float32 and rounds it to bf16
-with round-to-nearest-even.
+with round-to-nearest-even.  Backward: the pages give no formula, only that
+training recomputes the aggregation ([TUT] §4.6) and that the gradient
+reaches a source along a value path and a softmax/query/key path ([ATLAS]
+round-06 study, spike trajectory x backward path); the gradient here is the exact
+derivative of the forward definition, and the rounding of a stored sum passes
+gradients through unchanged.
 
 Parity pins (tests that fix this oracle to something other than itself):
 every function below is pinned -- the worked example of [BLOG2] §2.1, a
@@ -35,8 +40,11 @@ library reduction (torch ``rms_norm`` + ``scaled_dot_product_attention``, up to
 94 sources), closed forms (S=1, zero query, equal sources, S=2 logistic),
 invariants, 50-digit brute force, bf16 rounding against torch and hand-made
 ties, the schedule's source counts from [TUT] §4.5 / [ATLAS]'s widget, and
-([TUT] §4.3) Block AttnRes with one layer per block being Full AttnRes.  None
-is marked "parity unpinned".
+([TUT] §4.3) Block AttnRes with one layer per block being Full AttnRes.
+Backward: torch autograd through the library reduction, central finite
+differences, closed forms (one source, zero query, identical sources), the
+rescaling invariant, and autograd through a whole Block AttnRes schedule with
+exact partial sums.  None is marked "parity unpinned".
 """
 
 from __future__ import annotations
@@ -248,3 +256,124 @@ def run_full_schedule(h0, layer_outputs, queries, final_query=None, eps: float =
         sources.append(np.asarray(F, dtype=np.float32))
     final = depth_attention(np.stack(sources), final_query, eps) if final_query is not None else None
     return per_layer, final
+
+
+# ----------------------------------------------------------------------------
+# Backward: the derivative of depth_attention, then of the Block AttnRes
+# schedule.  The pages fix no formula; training recomputes the aggregation
+# ([TUT] §4.6), and the gradient reaches each source along a value path (the
+# weight times the upstream gradient) and along the softmax / query / key path
+# ([ATLAS] round-06 study, spike trajectory x backward path).  Written as the chain
+# rule through the forward's steps, in the forward's order.
+# ----------------------------------------------------------------------------
+
+def depth_attention_backward(H, w, g, eps: float = EPS):
+    """Gradients of ``L = sum_t g[t] . r[t]`` for ``r, a = depth_attention(H, w)``.
+
+    Args:
+      H: ``[S, T, d]`` sources; w: ``[d]`` query; g: ``[T, d]`` upstream
+         gradient dL/dr.  Any real dtype, upcast to float64.
+    Returns:
+      ``(dH, dw)``: ``[S, T, d]`` and ``[d]`` (summed over tokens), float64.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    S, T, d = H.shape
+    # forward, recomputed step by step
+    mean_square = np.mean(H * H, axis=-1, keepdims=True)           # [S, T, 1]
+    rms = np.sqrt(mean_square + eps)
+    keys = H / rms                                                  # [S, T, d]
+    logits = (keys @ w).T                                           # [T, S]
+    a = softmax(logits, axis=1)                                     # [T, S]
+    # r = sum_s a_s H_s: value path, and the gradient of each weight
+    dH = np.zeros_like(H)
+    da = np.zeros((T, S))
+    for s in range(S):
+        dH[s] += a[:, s:s + 1] * g                                  # value path
+        da[:, s] = np.sum(g * H[s], axis=1)                         # dL/da_s = g . H_s
+    # softmax over sources: dz_s = a_s (da_s - sum_s' a_s' da_s')
+    dz = a * (da - np.sum(a * da, axis=1, keepdims=True))          # [T, S]
+    # logits = keys . w
+    dw = np.zeros(d)
+    dkeys = np.zeros_like(H)
+    for s in range(S):
+        dw += np.sum(dz[:, s:s + 1] * keys[s], axis=0)
+        dkeys[s] = dz[:, s:s + 1] * w
+    # keys = H / sqrt(mean(H^2) + eps): dH = (dkeys - keys * mean(dkeys * keys)) / rms
+    dH += (dkeys - keys * np.mean(dkeys * keys, axis=-1, keepdims=True)) / rms
+    return dH, dw
+
+
+def layer_sources(h0, layer_outputs, block_size: int, dtype: str):
+    """Per layer: the names and stacked sources it aggregates (as the store holds
+    them, partial sums rounded to ``dtype``), plus the block representations."""
+    h0 = np.asarray(h0, dtype=np.float32)
+    num_layers = len(layer_outputs)
+    blocks, partial, per_layer = [], None, []
+    for l, ((n, i), F) in enumerate(zip(block_layout(num_layers, block_size), layer_outputs), start=1):
+        if i == 1:
+            partial = None
+        named = {"h0": h0, "partial": partial}
+        named.update({f"b{k + 1}": b for k, b in enumerate(blocks)})
+        names = layer_source_names(n, i)
+        per_layer.append((names, np.stack([named[x] for x in names])))
+        partial = accumulate(partial, F, dtype)
+        if i == block_size or l == num_layers:
+            blocks.append(partial)
+            partial = None
+    return per_layer, blocks
+
+
+def run_schedule_backward(h0, layer_outputs, queries, block_size: int, dtype: str, grad_r,
+                          final_query=None, grad_final=None, eps: float = EPS):
+    """Backward of ``run_schedule``: every layer's aggregation (and the output
+    layer's, if ``final_query`` is given) differentiated, and each source's
+    gradient handed to what the source is made of.
+
+    ``grad_r[l-1]`` is dL/dr_l (layer outputs are inputs here, so these are
+    independent), ``grad_final`` dL/d(final r).  h_0 is a source of every
+    layer; b_k is the sum of block k's layer outputs, so its gradient reaches
+    each of them; the partial sum at layer l is the sum of the block's layer
+    outputs before l.  Stored sums are rounded to ``dtype`` in the forward; the
+    rounding passes gradients through unchanged.
+
+    Returns dict with ``dF`` (list of ``[T, d]``), ``dh0``, ``dw`` (list of
+    ``[d]``) and, with ``final_query``, ``dw_final``; all float64.
+    """
+    num_layers = len(layer_outputs)
+    per_layer, blocks = layer_sources(h0, layer_outputs, block_size, dtype)
+    layout = block_layout(num_layers, block_size)
+    T, d = np.asarray(h0).shape
+    dF = [np.zeros((T, d)) for _ in range(num_layers)]
+    dh0 = np.zeros((T, d))
+    out = {"dw": []}
+
+    def block_members(k):
+        return [j for j in range(1, num_layers + 1) if layout[j - 1][0] == k]
+
+    def hand_out(names, dH, layer):
+        nonlocal dh0
+        for name, g in zip(names, dH):
+            if name == "h0":
+                dh0 = dh0 + g
+            elif name == "partial":          # the block's layers before `layer`
+                for j in block_members(layout[layer - 1][0]):
+                    if j < layer:
+                        dF[j - 1] += g
+            else:                            # b_k: every layer of block k
+                for j in block_members(int(name[1:])):
+                    dF[j - 1] += g
+
+    for l, ((names, H), w, g) in enumerate(zip(per_layer, queries, grad_r), start=1):
+        dH, dw = depth_attention_backward(H, w, g, eps)
+        out["dw"].append(dw)
+        hand_out(names, dH, l)
+    if final_query is not None:
+        names = ["h0"] + [f"b{k}" for k in range(1, len(blocks) + 1)]
+        H = np.stack([np.asarray(h0, np.float32)] + blocks)
+        dH, out["dw_final"] = depth_attention_backward(H, final_query, grad_final, eps)
+        hand_out(names, dH, None)
+    out["dF"] = dF
+    out["dh0"] = dh0
+    return out

@@ -196,3 +196,105 @@ def pin_bruteforce(agg, seed=4):
 
 
 ALL_PINS = (pin_worked_example, pin_library, pin_closed_forms, pin_invariants, pin_bruteforce)
+
+
+# ----------------------------------------------------------------------------
+# Backward pins: ``bwd(H, w, g, eps) -> (dH, dw)``, the gradients of
+# ``sum(g * r)``.  Facts used: torch autograd through the library reduction
+# above; central finite differences (Richardson-extrapolated) of the forward;
+# closed forms (one source: the gradient passes through unchanged; a zero
+# query or identical sources: every source gets g / S); the rescaling
+# invariant (keys blind to a positive rescaling, so d/dc L(c H_s) = a_s g.H_s
+# up to eps); permutation equivariance.
+# ----------------------------------------------------------------------------
+
+def library_backward(H, w, g, eps=EPS):
+    """dL/dH and dL/dw of L = sum(g * r) by autograd through rms_norm + sdpa."""
+    Ht = torch.tensor(np.asarray(H, np.float64), requires_grad=True)
+    wt = torch.tensor(np.asarray(w, np.float64), requires_grad=True)
+    S, T, d = Ht.shape
+    keys = F.rms_norm(Ht, (d,), eps=eps).permute(1, 0, 2)
+    q = wt.view(1, 1, d).expand(T, 1, d)
+    r = F.scaled_dot_product_attention(q, keys, Ht.permute(1, 0, 2), scale=1.0)[:, 0, :]
+    (r * torch.as_tensor(np.asarray(g, np.float64))).sum().backward()
+    return Ht.grad.numpy(), wt.grad.numpy()
+
+
+def pin_backward_library(bwd, seed=11):
+    H = synth.sources(6, 16, 64, scale=(1e-3, 10.0), seed=seed, dtype="f32").double().numpy()
+    H[2] *= 3e-3 / np.sqrt(np.mean(H[2] ** 2))            # mean square near eps
+    w = synth.query(64, seed=seed).double().numpy()
+    g = np.random.default_rng(seed).normal(size=(16, 64))
+    dH, dw = bwd(H, w, g, EPS)
+    dH_lib, dw_lib = library_backward(H, w, g, EPS)
+    _close(dH, dH_lib, rtol=1e-11, what="dH vs autograd")
+    _close(dw, dw_lib, rtol=1e-11, what="dw vs autograd")
+
+
+def _loss(H, w, g, eps):
+    from oracle import attnres_oracle as orc   # the forward, pinned by the pins above
+    r, _ = orc.depth_attention(H, w, eps)
+    return float(np.sum(g * r))
+
+
+def pin_backward_finite_difference(bwd, seed=12):
+    rng = np.random.default_rng(seed)
+    for S, T, d in ((1, 2, 4), (3, 2, 8), (9, 2, 8)):
+        H = rng.normal(size=(S, T, d)) * rng.uniform(0.3, 3.0, size=(S, 1, 1))
+        w = rng.normal(scale=1.0, size=d)
+        g = rng.normal(size=(T, d))
+        dH, dw = bwd(H, w, g, EPS)
+        for trial in range(4):
+            V = rng.normal(size=H.shape)
+            v = rng.normal(size=d)
+
+            def D(h):
+                return (_loss(H + h * V, w + h * v, g, EPS) - _loss(H - h * V, w - h * v, g, EPS)) / (2 * h)
+            fd = (4 * D(5e-4) - D(1e-3)) / 3                  # Richardson: error O(h^4)
+            an = float(np.sum(dH * V) + np.sum(dw * v))
+            assert abs(fd - an) <= 1e-8 * max(1.0, abs(fd)), f"S={S} direction {trial}: {an} vs {fd}"
+
+
+def pin_backward_closed_forms(bwd, seed=13):
+    rng = np.random.default_rng(seed)
+    S, T, d = 5, 7, 32
+    H = rng.normal(size=(S, T, d)) * rng.uniform(0.5, 4.0, size=(S, 1, 1))
+    w = rng.normal(scale=2 / math.sqrt(d), size=d)
+    g = rng.normal(size=(T, d))
+    # one source: r = h0, so dH = g exactly and the query gets nothing
+    dH, dw = bwd(H[:1], w, g, EPS)
+    assert np.array_equal(dH[0], g), "S=1: the gradient must pass through unchanged"
+    assert np.array_equal(dw, np.zeros(d)), "S=1: the query gradient must be zero"
+    # zero query: uniform weights, each source gets g / S (the key path carries w = 0)
+    dH, dw = bwd(H, np.zeros(d), g, EPS)
+    _close(dH, np.broadcast_to(g / S, dH.shape), rtol=1e-14, what="zero-query dH")
+    # identical sources: uniform weights, equal scores, no softmax gradient
+    same = np.repeat(H[:1], 4, axis=0)
+    dH, dw = bwd(same, w, g, EPS)
+    _close(dH, np.broadcast_to(g / 4, dH.shape), rtol=1e-13, what="identical-source dH")
+    _close(dw, np.zeros(d), rtol=0, atol=1e-12 * np.max(np.abs(g)) * np.max(np.abs(H)), what="identical-source dw")
+
+
+def pin_backward_invariants(bwd, seed=14):
+    rng = np.random.default_rng(seed)
+    S, T, d = 6, 9, 48
+    H = rng.normal(size=(S, T, d)) * rng.uniform(0.5, 4.0, size=(S, 1, 1))
+    w = rng.normal(scale=2 / math.sqrt(d), size=d)
+    g = rng.normal(size=(T, d))
+    from oracle import attnres_oracle as orc
+    _, a = orc.depth_attention(H, w, EPS)
+    dH, dw = bwd(H, w, g, EPS)
+    # keys are blind to a positive rescaling of a source (up to eps), so along
+    # H_s the loss changes only through the value: H_s . dH_s = a_s g . H_s
+    lhs = np.sum(H * dH, axis=-1)                               # [S, T]
+    rhs = (a.T * np.sum(g[None] * H, axis=-1))                  # [S, T]
+    _close(lhs, rhs, rtol=1e-4, what="rescaling invariant")
+    # permuting the sources permutes dH and leaves dw
+    perm = rng.permutation(S)
+    dH2, dw2 = bwd(H[perm], w, g, EPS)
+    _close(dH2, dH[perm], rtol=1e-13, what="permuted dH")
+    _close(dw2, dw, rtol=1e-13, what="permuted dw")
+
+
+BACKWARD_PINS = (pin_backward_library, pin_backward_finite_difference, pin_backward_closed_forms,
+                 pin_backward_invariants)
