@@ -68,6 +68,16 @@ _SIGNATURES = {
                                            ctypes.c_float, ctypes.c_void_p]),
     "attnres_split_queries": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                              ctypes.c_void_p]),
+    "attnres_add_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "attnres_aggregate_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p,
+                                                  ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                                                  ctypes.c_void_p]),
+    "attnres_aggregate_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.POINTER(ctypes.c_int64)]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(attnres_launch_t)]),
 }
@@ -161,6 +171,79 @@ def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None =
                                  _dtype_code(sources), _stream(dev, stream))
     _check("attnres_aggregate", rc)
     return out, weights
+
+
+def backward_workspace_bytes(T: int, d: int, dtype=torch.bfloat16) -> int:
+    """``attnres_aggregate_backward_workspace`` on the current device."""
+    out = ctypes.c_int64()
+    _check("attnres_aggregate_backward_workspace",
+           lib().attnres_aggregate_backward_workspace(T, d, _DTYPE_CODE[dtype], ctypes.byref(out)))
+    return out.value
+
+
+def add_rows(a: torch.Tensor | None, b: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """``attnres_add_rows``: ``out = a + b`` as the partial-sum update forms it
+    (``out = b`` when ``a`` is None); rows ``[T, d]``, contiguous."""
+    T, d = b.shape
+    for name, t in (("b", b), ("out", out)) + ((("a", a),) if a is not None else ()):
+        if not t.is_contiguous() or t.dtype != b.dtype or tuple(t.shape) != (T, d) or t.device != b.device:
+            raise ValueError(f"{name} must be a contiguous [T, d] tensor like b")
+    _check("attnres_add_rows", lib().attnres_add_rows(a.data_ptr() if a is not None else None, b.data_ptr(),
+                                                      out.data_ptr(), T, d, _dtype_code(b), _stream(b.device, stream)))
+    return out
+
+
+def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.Tensor, grad_sources: torch.Tensor,
+                       *, last_source: torch.Tensor | None = None, accumulate=0, grad_w: torch.Tensor | None = None,
+                       grad_last: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       eps: float = 1e-5, stream=None) -> torch.Tensor:
+    """``attnres_aggregate_backward``: writes (or, for the sources whose bit is
+    set in the ``accumulate`` mask, adds) dL/dH into ``grad_sources``
+    ``[S, T, d]`` float32 (rows contiguous, any row stride) and returns dL/dw
+    (``grad_w``, float32 ``[d]``).  ``sources`` holds the S rows, or the first
+    S-1 when ``last_source`` ``[T, d]`` gives the last one apart.  ``grad_out``
+    is dL/dr ``[T, d]`` in the sources' dtype; ``grad_last`` (optional,
+    ``[T, d]`` sources' dtype) receives the new gradient of the last source."""
+    if grad_sources.dim() != 3 or sources.dim() != 3:
+        raise ValueError("sources and grad_sources must be 3-D")
+    S, T, d = grad_sources.shape
+    if sources.shape[0] != (S - 1 if last_source is not None else S) or tuple(sources.shape[1:]) != (T, d):
+        raise ValueError("sources must hold S rows (S-1 with last_source) of [T, d]")
+    for name, t in (("sources", sources), ("grad_sources", grad_sources)):
+        if T > 0 and t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != d):
+            raise ValueError(f"each row of {name} must be a contiguous [T, d] block")
+    if last_source is not None and (not last_source.is_contiguous() or last_source.dtype != sources.dtype
+                                    or last_source.numel() != T * d):
+        raise ValueError("last_source must be a contiguous [T, d] tensor like the sources")
+    dev = grad_sources.device
+    if grad_sources.dtype != torch.float32:
+        raise ValueError("grad_sources must be float32")
+    if grad_w is None:
+        grad_w = torch.empty(d, dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = backward_workspace_bytes(T, d, sources.dtype)
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=dev)
+    checks = (("w", w, torch.float32, d), ("grad_out", grad_out, sources.dtype, T * d),
+              ("grad_w", grad_w, torch.float32, d))
+    if grad_last is not None:
+        checks += (("grad_last", grad_last, sources.dtype, T * d),)
+    for name, t, dt, n in checks:
+        if t.device != dev or not t.is_contiguous() or t.dtype != dt or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor with {n} elements on {dev}")
+    if not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous device tensor")
+    mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
+    src_stride = sources.stride(0) if sources.shape[0] > 1 else T * d
+    grad_stride = grad_sources.stride(0) if S > 1 else T * d
+    src_ptr = sources.data_ptr() if sources.shape[0] > 0 else None
+    rc = lib().attnres_aggregate_backward(
+        src_ptr, S, T, d, src_stride, last_source.data_ptr() if last_source is not None else None, w.data_ptr(),
+        grad_out.data_ptr(), grad_sources.data_ptr(),
+        grad_stride, mask & 0xFFFFFFFF, grad_last.data_ptr() if grad_last is not None else None, grad_w.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), float(eps), _dtype_code(sources),
+        _stream(dev, stream))
+    _check("attnres_aggregate_backward", rc)
+    return grad_w
 
 
 def prepared_query_shape(n: int, d: int):

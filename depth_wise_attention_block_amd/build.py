@@ -17,7 +17,7 @@ REPO = os.path.dirname(HERE)
 LIB_NAME = "libattnres.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 PATTERN_BENCH = os.path.join(HERE, "pattern_bench")
-SOURCES = ("aggregate.hip", "accumulate.hip", "twophase.hip", "capi.cpp")
+SOURCES = ("aggregate.hip", "accumulate.hip", "twophase.hip", "backward.hip", "capi.cpp")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 arithmetic; the host pass warns that

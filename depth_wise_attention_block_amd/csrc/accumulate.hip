@@ -20,7 +20,7 @@ constexpr int kUnroll = 4;  // independent 16-byte vectors per lane per trip
 
 template <bool kBf16, bool kCopy>
 __global__ void __launch_bounds__(kThreads)
-accumulate_kernel(u32x4* __restrict__ partial, const u32x4* __restrict__ layer_out, int64_t nvec) {
+accumulate_kernel(const u32x4* partial, const u32x4* __restrict__ layer_out, u32x4* out, int64_t nvec) {
   const int64_t chunk = (int64_t)kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * chunk; base < nvec; base += (int64_t)gridDim.x * chunk) {
     u32x4 f[kUnroll], p[kUnroll];
@@ -37,9 +37,9 @@ accumulate_kernel(u32x4* __restrict__ partial, const u32x4* __restrict__ layer_o
       const int64_t i = base + u * kThreads + threadIdx.x;
       if (i < nvec) {
         if constexpr (kCopy) {
-          __builtin_nontemporal_store(f[u], partial + i);
+          __builtin_nontemporal_store(f[u], out + i);
         } else {
-          __builtin_nontemporal_store(add_rows(p[u], f[u], kBf16), partial + i);
+          __builtin_nontemporal_store(add_rows(p[u], f[u], kBf16), out + i);
         }
       }
     }
@@ -55,17 +55,18 @@ hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream) {
   const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  u32x4* p = static_cast<u32x4*>(a.partial);
+  const u32x4* p = static_cast<const u32x4*>(a.partial);
   const u32x4* f = static_cast<const u32x4*>(a.layer_out);
+  u32x4* o = static_cast<u32x4*>(a.out != nullptr ? a.out : a.partial);
   if (a.copy) {
     hipLaunchKernelGGL((accumulate_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       p, f, nvec);
+                       p, f, o, nvec);
   } else if (a.bf16) {
     hipLaunchKernelGGL((accumulate_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       p, f, nvec);
+                       p, f, o, nvec);
   } else {
     hipLaunchKernelGGL((accumulate_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       p, f, nvec);
+                       p, f, o, nvec);
   }
   return hipGetLastError();
 }

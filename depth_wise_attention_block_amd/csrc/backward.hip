@@ -1,0 +1,323 @@
+// Backward of the Block AttnRes depth aggregation for gfx950 (MI355X).
+//
+// The forward ("Kimi K3技术详解系列（二）：AttnRes 与 Stable LatentMoE", §2;
+// kimi.papertok.ai ch. 4 §4.2 eq 8-9) is, per token over S sources H_s:
+//     rho_s = sqrt(mean(H_s^2) + eps),  z_s = w . H_s / rho_s,
+//     a = softmax(z),                    r = sum_s a_s H_s.
+// Training recomputes it in the backward pass (kimi.papertok.ai §4.6: the
+// aggregation sits inside activation checkpointing).  With g = dL/dr the
+// derivative is, per token,
+//     u_s = g . H_s,   delta_s = a_s (u_s - sum_s' a_s' u_s'),
+//     dL/dH_s = a_s g + (delta_s / rho_s) w - (delta_s z_s / (d rho_s^2)) H_s,
+//     dL/dw  += sum_s (delta_s / rho_s) H_s,
+// the first term being the value path and the other two the softmax / query /
+// key path of the gradient (llm-atlas.k1412.top/k3, round-06 study).
+//
+// One pass per token, like the forward: each lane loads its V 16-byte pieces
+// of every source and of g at once; three reductions per source (sum of
+// squares, w . H_s with w as bf16 hi + lo, g . H_s) share one LDS exchange and
+// one barrier; lanes 0..S-1 of every 16-lane row form the softmax and the
+// per-source coefficients, broadcast with readlane.  The float32 source
+// gradients are then written (or added into, per source) one source at a
+// time, the next source's old rows loading while the current one is formed.
+// dL/dw is accumulated per lane (in LDS) over the workgroup's tokens and
+// written as one float32 row per workgroup; reduce_rows_kernel sums those rows
+// in a fixed order, so the result is deterministic for a given grid.
+//
+// HBM bytes per token at S sources, bf16, all gradients accumulated:
+//   2 S d (sources) + 2 d (g) + 8 S d (old and new float32 gradients)
+//   (+ 2 d for the optional copy of the last source's gradient).
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace attnres {
+namespace {
+
+constexpr int kMaxSrc = 9;  // ATTNRES_MAX_SOURCES
+
+// Registers: all S sources, g and the query stay in registers for the whole
+// token (~190 VGPRs at kV = 2), so one 7-wave workgroup fits per CU; 2 waves
+// per SIMD is then the same occupancy as 3 and leaves room to avoid spills.
+template <int kV>
+constexpr int waves_per_simd_bwd() { return kV == 1 ? 4 : 2; }
+
+// Elements of a 16-byte vector and the float32 gradient vectors it maps to.
+template <bool kBf16>
+struct Elems {
+  static constexpr int kE = kBf16 ? 8 : 4;
+  static constexpr int kG = kE / 4;  // f32x4 gradient vectors per source vector
+};
+
+template <bool kBf16>
+__device__ __forceinline__ void unpack(u32x4 v, float (&e)[Elems<kBf16>::kE]) {
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      e[2 * k] = bf16_lo(v[k]);
+      e[2 * k + 1] = bf16_hi(v[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = __uint_as_float(v[k]);
+  }
+}
+
+template <bool kBf16, int kV>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_bwd<kV>())))
+aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
+                          const u32x4* __restrict__ last_src, const float* __restrict__ w,
+                          const u32x4* __restrict__ gout,
+                          f32x4* __restrict__ grad, int64_t grad_stride_v, unsigned acc_mask,
+                          u32x4* __restrict__ grad_last, float* __restrict__ dw_rows, float eps, float inv_d) {
+  using El = Elems<kBf16>;
+  constexpr int kE = El::kE, kGv = El::kG;
+  // [buffer][wave][sum of squares | w.x | g.x][source]
+  __shared__ float red[2][kMaxWaves][3][16];
+  // this lane's running dL/dw, [vector][lane] (each lane touches only its own)
+  __shared__ f32x4 dw4[kV * kGv][64 * kMaxWaves];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int s16 = lane & 15;
+
+  Query<kBf16, kV> q;
+  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
+#pragma unroll
+  for (int k = 0; k < kV * kGv; ++k) dw4[k][tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+    const u32x4* tok = src + t * (int64_t)nvec;
+
+    // 1. every source and g for this token, all loads at once
+    u32x4 x[kMaxSrc][kV], g[kV];
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      g[v] = idx < nvec ? __builtin_nontemporal_load(gout + t * (int64_t)nvec + idx) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+        // the last source may live elsewhere (a recomputed partial sum)
+        const u32x4* row = (last_src != nullptr && s == S - 1) ? last_src + t * (int64_t)nvec
+                                                               : tok + s * src_stride_v;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          const int idx = v * nthr + tid;
+          x[s][v] = idx < nvec ? __builtin_nontemporal_load(row + idx) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+
+    // 2. per source: sum of squares, w . H_s, g . H_s; wave sums
+    float gss = 0.f, gdt = 0.f, gug = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+        float ss = 0.f, dt = 0.f, ug = 0.f;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          if constexpr (kBf16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = dot2(x[s][v][k], x[s][v][k], ss);
+              dt = dot2(x[s][v][k], q.hi[v][k], dt);
+              dt = dot2(x[s][v][k], q.lo[v][k], dt);
+              ug = dot2(x[s][v][k], g[v][k], ug);
+            }
+          } else {
+            const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
+            const f32x4 gf = __builtin_bit_cast(f32x4, g[v]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = fmaf(xf[k], xf[k], ss);
+              dt = fmaf(xf[k], q.f[v][k], dt);
+              ug = fmaf(xf[k], gf[k], ug);
+            }
+          }
+        }
+        gss = put_lane(wave_sum(ss), s, gss, s16);
+        gdt = put_lane(wave_sum(dt), s, gdt, s16);
+        gug = put_lane(wave_sum(ug), s, gug, s16);
+        __builtin_amdgcn_sched_barrier(0);  // three reductions in flight at a time
+      }
+    }
+    if (lane < 16) {
+      red[buf][wave][0][lane] = gss;
+      red[buf][wave][1][lane] = gdt;
+      red[buf][wave][2][lane] = gug;
+    }
+    __syncthreads();
+
+    // 3. softmax and the per-source coefficients, lanes s16 < S of every row
+    float z = -INFINITY, rho = 1.f, ug = 0.f;
+    if (s16 < S) {
+      float ss = 0.f, dt = 0.f;
+      for (int k = 0; k < nwaves; ++k) {
+        ss += red[buf][k][0][s16];
+        dt += red[buf][k][1][s16];
+        ug += red[buf][k][2][s16];
+      }
+      rho = sqrtf(ss * inv_d + eps);
+      z = dt / rho;
+    }
+    const float m = row_max16(z);
+    const float p = (s16 < S) ? expf(z - m) : 0.f;
+    const float a = p / row_sum16(p);
+    const float ubar = row_sum16(a * ug);            // g . r
+    const float delta = a * (ug - ubar);             // dL/dz_s
+    const float c1 = delta / rho;                    // coefficient of w (and of H_s in dL/dw)
+    const float c3 = c1 * z * inv_d / rho;           // coefficient of H_s in dL/dH_s
+    float as[kMaxSrc], c1s[kMaxSrc], c3s[kMaxSrc];
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      as[s] = s < S ? lane_bcast(a, s) : 0.f;
+      c1s[s] = s < S ? lane_bcast(c1, s) : 0.f;
+      c3s[s] = s < S ? lane_bcast(c3, s) : 0.f;
+    }
+
+    // 5. dL/dH_s = a_s g + c1_s w - c3_s H_s, written or added, source by
+    //    source; the old rows of source s+1 load while source s is formed
+    f32x4 old[2][kV][kGv];
+    auto load_old = [&](int s, f32x4 (&o)[kV][kGv]) {
+      const bool add = (acc_mask >> s) & 1u;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int idx = v * nthr + tid;
+#pragma unroll
+        for (int h = 0; h < kGv; ++h) {
+          o[v][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (add && idx < nvec)
+            o[v][h] = __builtin_nontemporal_load(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+        }
+      }
+    };
+    load_old(0, old[0]);
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+        if (s + 1 < S) load_old(s + 1, old[(s + 1) & 1]);
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          const int idx = v * nthr + tid;
+          // the query in float32 is hi + lo (exact) or w itself
+          float xe[kE], ge[kE], wf[kE], r[kE];
+          unpack<kBf16>(x[s][v], xe);
+          unpack<kBf16>(g[v], ge);
+          if constexpr (kBf16) {
+            float lo[kE];
+            unpack<true>(q.hi[v], wf);
+            unpack<true>(q.lo[v], lo);
+#pragma unroll
+            for (int e = 0; e < kE; ++e) wf[e] += lo[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) wf[e] = q.f[v][e];
+          }
+#pragma unroll
+          for (int e = 0; e < kE; ++e) r[e] = fmaf(as[s], ge[e], fmaf(c1s[s], wf[e], -c3s[s] * xe[e]));
+          // dL/dw += c1_s H_s for this lane's elements
+#pragma unroll
+          for (int h = 0; h < kGv; ++h) {
+            f32x4 acc = dw4[v * kGv + h][tid];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(c1s[s], xe[4 * h + c], acc[c]);
+            dw4[v * kGv + h][tid] = acc;
+          }
+#pragma unroll
+          for (int h = 0; h < kGv; ++h) {
+            f32x4 o = old[s & 1][v][h];
+            o = f32x4{o[0] + r[4 * h], o[1] + r[4 * h + 1], o[2] + r[4 * h + 2], o[3] + r[4 * h + 3]};
+            if (idx < nvec) {
+              __builtin_nontemporal_store(o, grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+              old[s & 1][v][h] = o;  // kept for the copy of the last source's gradient
+            }
+          }
+        }
+        if (grad_last != nullptr && s == S - 1) {
+#pragma unroll
+          for (int v = 0; v < kV; ++v) {
+            const int idx = v * nthr + tid;
+            u32x4 o;
+            if constexpr (kBf16) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const f32x4 lo4 = old[s & 1][v][k >> 1];
+                o[k] = pack_bf16(lo4[2 * (k & 1)], lo4[2 * (k & 1) + 1]);
+              }
+            } else {
+              o = __builtin_bit_cast(u32x4, old[s & 1][v][0]);
+            }
+            if (idx < nvec) __builtin_nontemporal_store(o, grad_last + t * (int64_t)nvec + idx);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one source's rows in registers at a time
+      }
+    }
+  }
+
+  // 6. this workgroup's dL/dw row
+  float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int idx = v * nthr + tid;
+    if (idx < nvec) {
+#pragma unroll
+      for (int h = 0; h < kGv; ++h) reinterpret_cast<f32x4*>(row)[idx * kGv + h] = dw4[v * kGv + h][tid];
+    }
+  }
+}
+
+// out[j] = sum over p = 0 .. rows-1 of in[p][j], in that order.
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ in, int64_t rows, int n,
+                                                          float* __restrict__ out) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) {
+    float acc = 0.f;
+    for (int64_t p = 0; p < rows; ++p) acc += in[p * n + j];
+    out[j] = acc;
+  }
+}
+
+template <bool kBf16, int kV>
+hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
+  const int nvec = a.d / (kBf16 ? 8 : 4);
+  if (a.T > 0) {
+    hipLaunchKernelGGL((aggregate_backward_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                       static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4),
+                       static_cast<const u32x4*>(a.last_source), a.w,
+                       static_cast<const u32x4*>(a.grad_out), reinterpret_cast<f32x4*>(a.grad_sources),
+                       a.grad_stride / 4, a.acc_mask, static_cast<u32x4*>(a.grad_last), a.workspace, a.eps,
+                       1.0f / (float)a.d);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int blocks = (a.d + 255) / 256;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.workspace,
+                     a.T > 0 ? a.grid : (int64_t)0, a.d, a.grad_w);
+  return hipGetLastError();
+}
+
+template <bool kBf16>
+hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
+  switch (a.vecs_per_lane) {
+    case 1: return launch_bwd_v<kBf16, 1>(a, stream);
+    case 2: return launch_bwd_v<kBf16, 2>(a, stream);
+    case 3: return launch_bwd_v<kBf16, 3>(a, stream);
+    case 4: return launch_bwd_v<kBf16, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream) {
+  return a.bf16 ? launch_bwd<true>(a, stream) : launch_bwd<false>(a, stream);
+}
+
+}  // namespace attnres

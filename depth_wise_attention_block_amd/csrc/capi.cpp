@@ -180,6 +180,111 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
                                                                                       : ATTNRES_ELAUNCH;
 }
 
+// Workgroups of the backward pass: as many as fit on the device at once (one
+// per CU for d above 4096, two below), each accumulating dL/dw over its tokens.
+int64_t backward_grid(int64_t T, int cus, int v) {
+  const int64_t resident = (int64_t)cus * (v == 1 ? 2 : 1);
+  return T < resident ? T : resident;
+}
+
+ATTNRES_API int attnres_aggregate_backward_workspace(int64_t T, int32_t d, int32_t dtype, int64_t* bytes) {
+  if (bytes == nullptr) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (T == 0) {
+    *bytes = 0;
+    return ATTNRES_OK;
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  attnres_launch_t cfg;
+  rc = pick_config(1, T, d, dtype, cus, &cfg);
+  if (rc != ATTNRES_OK) return rc;
+  *bytes = backward_grid(T, cus, cfg.vecs_per_lane) * (int64_t)d * 4;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
+                                           const void* last_source, const float* w, const void* grad_out,
+                                           float* grad_sources,
+                                           int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                           float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
+                                           int32_t dtype, void* stream) {
+  if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return ATTNRES_EINVAL;
+  const int64_t row = T * (int64_t)d;
+  if (src_stride == 0) src_stride = row;
+  if (grad_stride == 0) grad_stride = row;
+  if (src_stride < 0 || src_stride > (INT64_C(1) << 40) || grad_stride < 0 || grad_stride > (INT64_C(1) << 40))
+    return ATTNRES_EINVAL;
+  if (S > 1 && (src_stride < row || grad_stride < row)) return ATTNRES_EINVAL;
+  if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
+  if (grad_w == nullptr) return ATTNRES_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(grad_w) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+  const int es = elem_bytes(dtype);
+  const Range r_gw = range(grad_w, (int64_t)d * 4);
+  if (T > 0) {
+    if ((sources == nullptr && !(S == 1 && last_source != nullptr)) || w == nullptr || grad_out == nullptr ||
+        grad_sources == nullptr || workspace == nullptr || workspace_bytes <= 0)
+      return ATTNRES_EINVAL;
+    if (!aligned16(sources) || !aligned16(w) || !aligned16(grad_out) || !aligned16(grad_sources) ||
+        !aligned16(workspace) || (grad_last != nullptr && !aligned16(grad_last)) ||
+        (last_source != nullptr && !aligned16(last_source)))
+      return ATTNRES_EUNSUPPORTED;
+    // rows read through the stride: all S, or S-1 when the last one is given apart
+    const int strided = last_source != nullptr ? S - 1 : S;
+    const Range r_src = strided > 0 ? range(sources, ((int64_t)(strided - 1) * src_stride + row) * es) : Range{0, 0};
+    const Range r_last = last_source != nullptr ? range(last_source, row * es) : Range{0, 0};
+    const Range r_w = range(w, (int64_t)d * 4);
+    const Range r_g = range(grad_out, row * es);
+    const Range r_gs = range(grad_sources, ((int64_t)(S - 1) * grad_stride + row) * 4);
+    const Range r_gl = grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0};
+    const Range r_ws = range(workspace, workspace_bytes);
+    const Range outs[4] = {r_gs, r_gl, r_gw, r_ws};
+    const Range ins[4] = {r_src, r_w, r_g, r_last};
+    for (int i = 0; i < 4; ++i) {
+      for (int k = 0; k < 4; ++k)
+        if (overlap(outs[i], ins[k])) return ATTNRES_EALIAS;
+      for (int k = i + 1; k < 4; ++k)
+        if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
+    }
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  attnres_launch_t cfg;
+  rc = pick_config(S, T, d, dtype, cus, &cfg);
+  if (rc != ATTNRES_OK) return rc;
+  const int64_t grid = backward_grid(T, cus, cfg.vecs_per_lane);
+  if (T > 0 && workspace_bytes < grid * (int64_t)d * 4) return ATTNRES_EINVAL;
+  attnres::BackwardArgs a;
+  a.sources = sources;
+  a.S = S;
+  a.T = T;
+  a.d = d;
+  a.src_stride = src_stride;
+  a.last_source = last_source;
+  a.w = w;
+  a.grad_out = grad_out;
+  a.grad_sources = grad_sources;
+  a.grad_stride = grad_stride;
+  a.acc_mask = accumulate_mask;
+  a.grad_last = grad_last;
+  a.grad_w = grad_w;
+  a.workspace = static_cast<float*>(workspace);
+  a.eps = eps;
+  a.bf16 = dtype == ATTNRES_BF16;
+  a.threads = cfg.threads;
+  a.vecs_per_lane = cfg.vecs_per_lane;
+  a.grid = grid;
+  (void)hipGetLastError();
+  return attnres::launch_aggregate_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                               : ATTNRES_ELAUNCH;
+}
+
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                              const float* w, void* out, float* weights, float eps, void* stream) {
   int rc = check_store(st);
@@ -414,6 +519,35 @@ ATTNRES_API int attnres_store_sources(const attnres_store_t* st) {
   return 1 + st->n_completed + st->partial_valid;
 }
 
+ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_t T, int32_t d, int32_t dtype,
+                                 void* stream) {
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  const int64_t row = T * (int64_t)d;
+  if (row == 0) return ATTNRES_OK;
+  if (b == nullptr || out == nullptr) return ATTNRES_EINVAL;
+  if ((a != nullptr && !aligned16(a)) || !aligned16(b) || !aligned16(out)) return ATTNRES_EUNSUPPORTED;
+  const int es = elem_bytes(dtype);
+  const Range r_out = range(out, row * es);
+  // out may be a itself (in place), not b, and no partial overlap with either
+  if (overlap(r_out, range(b, row * es))) return ATTNRES_EALIAS;
+  if (a != nullptr && a != out && overlap(r_out, range(a, row * es))) return ATTNRES_EALIAS;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  attnres::AccumulateArgs args;
+  args.partial = const_cast<void*>(a);
+  args.layer_out = b;
+  args.out = out;
+  args.elems = row;
+  args.bf16 = dtype == ATTNRES_BF16;
+  args.copy = a == nullptr;
+  args.num_cus = cus;
+  (void)hipGetLastError();
+  return attnres::launch_accumulate(args, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                          : ATTNRES_ELAUNCH;
+}
+
 ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                    void* stream) {
   int rc = check_store(st);
@@ -434,6 +568,7 @@ ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out, i
     attnres::AccumulateArgs a;
     a.partial = static_cast<char*>(st->base) + (int64_t)slot * st->slot_stride * es;
     a.layer_out = layer_out;
+    a.out = nullptr;
     a.elems = row;
     a.bf16 = st->dtype == ATTNRES_BF16;
     a.copy = st->partial_valid == 0;

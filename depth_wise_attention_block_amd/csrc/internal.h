@@ -44,8 +44,9 @@ struct AggregateArgs {
 hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream);
 
 struct AccumulateArgs {
-  void* partial;        // [T][d] slot, updated in place
+  void* partial;        // [T][d] slot (read unless copy)
   const void* layer_out;// [T][d]
+  void* out;            // [T][d] result; nullptr = in place over partial
   int64_t elems;        // T*d
   bool bf16;
   bool copy;            // true: partial = layer_out (first layer of a block)
@@ -100,5 +101,33 @@ struct MergeArgs {
 };
 
 hipError_t launch_block_merge(const MergeArgs& a, hipStream_t stream);
+
+// Backward of one aggregation: float32 source gradients (written or added per
+// source), dL/dw via one float32 row per workgroup in `workspace` reduced in a
+// fixed order, and optionally the last source's new gradient in the source
+// dtype.
+struct BackwardArgs {
+  const void* sources;
+  int S;
+  int64_t T;
+  int d;
+  int64_t src_stride;     // elements
+  const void* last_source;// source S-1 at this address instead, or nullptr
+  const float* w;
+  const void* grad_out;   // [T][d], source dtype
+  float* grad_sources;    // S rows of [T][d] at grad_stride floats
+  int64_t grad_stride;
+  unsigned acc_mask;      // bit s: add into row s
+  void* grad_last;        // [T][d] source dtype, or nullptr
+  float* grad_w;          // [d]
+  float* workspace;       // grid rows of [d]
+  float eps;
+  bool bf16;
+  int threads, vecs_per_lane;
+  int64_t grid;
+};
+
+hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream);
+
 
 }  // namespace attnres

@@ -189,3 +189,83 @@ def run_full_schedule(sources: torch.Tensor, queries: Sequence[torch.Tensor], *,
     if final_query is not None:
         return aggregate(sources[: num_layers + 1], final_query, final_out, final_weights, eps=eps)
     return None
+
+
+def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tensor], queries: Sequence[torch.Tensor],
+                          block_size: int, grad_r, *, final_query: Optional[torch.Tensor] = None,
+                          grad_final: Optional[torch.Tensor] = None, grad_store: Optional[torch.Tensor] = None,
+                          grad_w: Optional[Sequence[torch.Tensor]] = None, grad_w_final: Optional[torch.Tensor] = None,
+                          on_grad: Optional[Callable[[int, torch.Tensor], None]] = None, eps: float = 1e-5):
+    """Backward of ``run_schedule``, layer by layer in reverse, recomputing each
+    block's partial sums (kimi.papertok.ai §4.6: the aggregation is
+    recomputed in the backward pass).
+
+    ``store`` is the forward's store after the pass (h_0 and every block
+    representation; left unchanged).  Each block's partial sums are recomputed
+    into a buffer of their own and passed to the layer's backward as its last
+    source.
+    ``grad_r`` is a sequence of dL/dr_l ``[T, d]`` (store dtype) or a callable
+    ``grad_r(l, dF_l) -> dL/dr_l``: the layer's own backward, given the finished
+    gradient of its output.  Gradients of the sources accumulate in
+    ``grad_store`` ``[1 + blocks, T, d]`` float32: row 0 is dL/dh_0, row n the
+    gradient of block n's representation, which is also the running gradient
+    of its partial sums; each aggregation's backward hands out the finished
+    gradient of the previous layer's output (``on_grad(l, dF_l)``, store dtype,
+    l = L..0 where dF_0 is dL/dh_0 rounded).  Returns ``(grad_store, grad_w,
+    grad_w_final)``.
+    """
+    from .binding import add_rows, aggregate_backward
+
+    L = len(layer_outputs)
+    T, d = store.T, store.d
+    dev, dt = store.slots.device, store.slots.dtype
+    nblocks = (L + block_size - 1) // block_size
+    if store.n_completed != nblocks or store.partial_valid:
+        raise ValueError("store must hold h_0 and every block representation (the forward's end state)")
+    if grad_store is None:
+        grad_store = torch.empty((1 + nblocks, T, d), dtype=torch.float32, device=dev)
+    if grad_w is None:
+        grad_w = [torch.empty(d, dtype=torch.float32, device=dev) for _ in range(L)]
+    if final_query is not None and grad_w_final is None:
+        grad_w_final = torch.empty(d, dtype=torch.float32, device=dev)
+    slots = store.slots
+    dF = torch.empty((T, d), dtype=dt, device=dev)
+    partials = torch.empty((block_size, T, d), dtype=dt, device=dev)  # partials[i-1]: before position i
+    ready = 0            # grad_store rows [0, ready) hold a gradient already
+
+    def mask(S):
+        return (1 << min(S, ready)) - 1
+
+    def dr(l):
+        return grad_r(l, dF) if callable(grad_r) else grad_r[l - 1]
+
+    if final_query is not None:
+        S = 1 + nblocks
+        aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=mask(S),
+                           grad_w=grad_w_final, grad_last=dF, eps=eps)
+        ready = S
+    else:
+        dF.zero_()
+    if on_grad is not None:
+        on_grad(L, dF)
+    for n in range(nblocks, 0, -1):
+        first = (n - 1) * block_size + 1
+        last = min(n * block_size, L)
+        # the block's partial sums, formed exactly as the forward formed them
+        for i in range(2, last - first + 2):
+            add_rows(partials[i - 3] if i > 2 else None, layer_outputs[first + i - 3], partials[i - 2])
+        for l in range(last, first - 1, -1):
+            i = l - first + 1
+            g = dr(l)
+            if i >= 2:
+                S = n + 1
+                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:S], last_source=partials[i - 2],
+                                   accumulate=mask(S), grad_w=grad_w[l - 1], grad_last=dF, eps=eps)
+            else:
+                S = n
+                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:S], accumulate=mask(S),
+                                   grad_w=grad_w[l - 1], grad_last=dF, eps=eps)
+            ready = max(ready, S)
+            if on_grad is not None:
+                on_grad(l - 1, dF)
+    return grad_store, grad_w, grad_w_final

@@ -256,6 +256,60 @@ ATTNRES_API int attnres_block_merge(attnres_store_t* st, const void* layer_out, 
                                     const void* inter, const float* logits, void* out, float* weights,
                                     float eps, void* stream);
 
+/*
+ * attnres_add_rows -- out = a + b element-wise over [T][d] (bf16: one float32
+ * addition, then round to nearest even; f32: one addition), or out = b when a
+ * is NULL: the partial-sum update of attnres_accumulate on plain rows, e.g. to
+ * recompute a block's partial sums for the backward pass (kimi.papertok.ai
+ * §4.6, recomputation).  out may be a (in place) but may not overlap b.
+ */
+ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_t T, int32_t d, int32_t dtype,
+                                 void* stream);
+
+/*
+ * attnres_aggregate_backward -- gradients of one aggregation, recomputing its
+ * forward (training wraps the aggregation in activation checkpointing,
+ * kimi.papertok.ai §4.6).  With g = dL/dr for r = attnres_aggregate(sources, w):
+ *   u_s = g . H_s,  delta_s = a_s (u_s - sum_s' a_s' u_s'),
+ *   dL/dH_s = a_s g + (delta_s / rho_s) w - (delta_s z_s / (d rho_s^2)) H_s,
+ *   dL/dw   = sum over tokens and sources of (delta_s / rho_s) H_s,
+ * with rho_s = sqrt(mean(H_s^2) + eps) and z_s, a_s the forward's logits and
+ * weights: the value path and the softmax / query / key path of the gradient
+ * (llm-atlas.k1412.top/k3, round-06 study).
+ *
+ *   sources, S, T, d, src_stride, w, eps, dtype   as attnres_aggregate, S <= 9.
+ *   last_source     device, [T][d] in dtype, or NULL: when given, source S-1 is
+ *                   read here instead of at (S-1)*src_stride (a recomputed
+ *                   partial sum next to the store's slots); sources may then be
+ *                   NULL for S = 1.
+ *   grad_out        device, [T][d] in dtype: dL/dr.
+ *   grad_sources    device, S rows of [T][d] float32, row s at s*grad_stride
+ *                   floats (0 means T*d); 16-byte aligned.  Row s is overwritten
+ *                   with dL/dH_s, or, when bit s of accumulate_mask is set, has
+ *                   it added (float32).
+ *   grad_last       device, [T][d] in dtype (round to nearest even for bf16), or
+ *                   NULL: receives the new value of grad row S-1 -- in a Block
+ *                   AttnRes backward that is the finished gradient of the
+ *                   previous layer's output.
+ *   grad_w          device, [d] float32, overwritten with dL/dw (zero for T = 0).
+ *   workspace       device, at least attnres_aggregate_backward_workspace()
+ *                   bytes, 16-byte aligned (NULL allowed for T = 0): one
+ *                   float32 row of dL/dw per workgroup, summed in a fixed order,
+ *                   so results are bitwise reproducible on one device.
+ * Outputs may not overlap the inputs or each other (ATTNRES_EALIAS).  Unlike
+ * the forward, T = 0 still launches (to zero grad_w).
+ */
+ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
+                                           const void* last_source, const float* w, const void* grad_out,
+                                           float* grad_sources,
+                                           int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                           float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
+                                           int32_t dtype, void* stream);
+
+/* Workspace bytes attnres_aggregate_backward needs for T tokens of width d on
+ * the current device (host only apart from a device-attribute query). */
+ATTNRES_API int attnres_aggregate_backward_workspace(int64_t T, int32_t d, int32_t dtype, int64_t* bytes);
+
 /* Launch shape the library picks for an aggregation (host only, no HIP call). */
 typedef struct attnres_launch {
   int32_t threads;          /* threads per workgroup (multiple of 64)         */

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -252,3 +252,34 @@ def test_two_phase_checks_and_bookkeeping(lib):
     assert B.lib().attnres_block_prepare(ctypes.byref(st0), None, 1, None, 12, None, 0, None, None, 1e-5,
                                          None) == B.OK
     assert (st0.n_completed, st0.partial_valid) == (1, 0)
+
+
+def test_backward_host_checks(lib):
+    """attnres_aggregate_backward rejects bad arguments before touching the GPU."""
+    GS, GL, GW, WS = 0x60000000, 0x68000000, 0x6C000000, 0x70000000
+
+    def bwd(S=3, T=4, d=8, src=SRC, w=W, g=OUT, gs=GS, gstride=0, gl=None, gw=GW, ws=WS, wsb=1 << 20, eps=1e-5,
+            dtype=B.BF16, src_stride=0, last=None):
+        return B.lib().attnres_aggregate_backward(src, S, T, d, src_stride, last, w, g, gs, gstride, 0, gl, gw, ws,
+                                                  wsb, eps, dtype, None)
+
+    assert bwd(S=0) == B.EINVAL and bwd(S=10) == B.EINVAL          # Block AttnRes sizes only
+    assert bwd(T=-1) == B.EINVAL and bwd(d=12) == B.EUNSUPPORTED
+    assert bwd(eps=-1.0) == B.EINVAL and bwd(eps=float("nan")) == B.EINVAL
+    assert bwd(gw=None) == B.EINVAL and bwd(gw=GW + 2) == B.EUNSUPPORTED
+    assert bwd(src=None) == B.EINVAL and bwd(g=None) == B.EINVAL and bwd(gs=None) == B.EINVAL
+    assert bwd(ws=None) == B.EINVAL and bwd(wsb=0) == B.EINVAL
+    assert bwd(gstride=8) == B.EINVAL and bwd(gstride=4 * 8 + 2) == B.EUNSUPPORTED
+    assert bwd(gs=GS + 8) == B.EUNSUPPORTED and bwd(gl=GL + 8) == B.EUNSUPPORTED
+    assert bwd(gs=SRC + 32) == B.EALIAS and bwd(gl=OUT) == B.EALIAS and bwd(gw=W) == B.EALIAS
+    assert bwd(ws=GS + 64) == B.EALIAS and bwd(gl=GS + 16) == B.EALIAS
+    assert bwd(last=SRC + 8) == B.EUNSUPPORTED and bwd(last=GS) == B.EALIAS
+    assert bwd(S=1, src=None) == B.EINVAL
+
+    add = B.lib().attnres_add_rows
+    assert add(None, None, W, 4, 8, B.BF16, None) == B.EINVAL and add(None, OUT, None, 4, 8, B.BF16, None) == B.EINVAL
+    assert add(SRC + 8, OUT, W, 4, 8, B.BF16, None) == B.EUNSUPPORTED and add(None, OUT, OUT, 4, 8, B.BF16, None) == B.EALIAS
+    assert add(SRC, OUT, SRC + 16, 4, 8, B.BF16, None) == B.EALIAS and add(None, OUT, W, 0, 8, B.BF16, None) == B.OK
+    out = ctypes.c_int64()
+    assert B.lib().attnres_aggregate_backward_workspace(0, 8, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
+    assert B.lib().attnres_aggregate_backward_workspace(4, 8, B.BF16, None) == B.EINVAL

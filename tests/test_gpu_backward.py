@@ -1,0 +1,272 @@
+"""GPU parity of the backward pass: attnres_aggregate_backward against the
+oracle's depth_attention_backward, its exact properties, the row update used to
+recompute partial sums, and the reverse-order Block AttnRes schedule against
+the oracle's run_schedule_backward.
+
+Tolerance (float32 results against the float64 oracle on the same inputs).  The
+kernel forms u_s = g . H_s, the sums of squares and w . H_s in float32 over d
+products, w as bf16 hi + lo (2^-17 relative), then delta_s = a_s (u_s - ubar).
+The error of delta_s is therefore relative to M_s = a_s (|u|_s + sum a |u|),
+with |u|_s = sum_j |g_j H_s,j|, not to delta_s itself (it is a difference).
+Element-wise:
+    |d dH_s[j]| <= c (a_s |g_j| + (M_s / rho_s)(|w_j| + |z_s| |k_s[j]| / d))
+    |d dw[j]|   <= c sum_{t,s} (M_s / rho_s) |H_s[j]|
+with c = 2e-4: float32 accumulation over d = 7168 products is ~sqrt(d) 2^-24 ~
+5e-6 relative in the typical case (d 2^-24 = 4e-4 at worst), the hi + lo query
+~8e-6; c leaves an order of magnitude above the typical case.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from depth_wise_attention_block_amd import binding as B
+from depth_wise_attention_block_amd import schedule, synth
+from oracle import attnres_oracle as orc
+from tests.gpu_util import device, host, note
+
+pytestmark = pytest.mark.gpu
+
+C_BWD = 2e-4
+
+
+def bounds(H, w, g, eps=orc.EPS):
+    """Magnitude bounds of dH [S,T,d] and dw [d] (see the module docstring)."""
+    H = np.asarray(H, np.float64)
+    w = np.asarray(w, np.float64)
+    g = np.asarray(g, np.float64)
+    S, T, d = H.shape
+    rms = np.sqrt(np.mean(H * H, -1, keepdims=True) + eps)            # [S,T,1]
+    keys = H / rms
+    z = (keys @ w).T                                                   # [T,S]
+    a = orc.softmax(z, axis=1)
+    U = np.stack([np.sum(np.abs(g * H[s]), axis=1) for s in range(S)], axis=1)   # [T,S]
+    M = a * (U + np.sum(a * U, axis=1, keepdims=True))                 # [T,S]
+    coef = (M.T[:, :, None] / rms)                                     # [S,T,1]
+    bH = a.T[:, :, None] * np.abs(g)[None] + coef * (np.abs(w)[None, None] + np.abs(z.T)[:, :, None] * np.abs(keys) / d)
+    bw = np.sum(coef * np.abs(H), axis=(0, 1))
+    return bH, bw
+
+
+def check(dH_gpu, dw_gpu, H, w, g, what, prefill=None):
+    """dH (and dw unless dw_gpu is None) against the oracle within the bounds."""
+    dH_ref, dw_ref = orc.depth_attention_backward(H, w, g)
+    if prefill is not None:
+        dH_ref = dH_ref + prefill
+    bH, bw = bounds(H, w, g)
+    errH = np.abs(np.asarray(dH_gpu, np.float64) - dH_ref)
+    # float32 rounding of a result (and of prefill + result) is within the bound's slack
+    limH = C_BWD * bH + 2.0 ** -23 * np.abs(dH_ref)
+    rH = float(np.max(errH / limH))
+    rw = 0.0
+    if dw_gpu is not None:
+        errw = np.abs(np.asarray(dw_gpu, np.float64) - dw_ref)
+        limw = C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref)
+        rw = float(np.max(errw / limw))
+    note(f"{what}: max err / bound dH {rH:.3g} dw {rw:.3g}")
+    assert rH <= 1.0, f"{what}: dH error {np.max(errH):.3e} exceeds the bound (ratio {rH:.3g})"
+    assert rw <= 1.0, f"{what}: dw error exceeds the bound (ratio {rw:.3g})"
+
+
+def inputs(S, T, d, dtype, seed):
+    dev = device()
+    scale = (0.5, 50.0) if dtype == torch.bfloat16 else (0.1, 10.0)
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    H = synth.sources(S, T, d, scale=scale, seed=seed, device=dev, dtype=name)
+    w = synth.query(d, seed=seed, device=dev)
+    g = synth.layer_output(T, d, std=1.0, seed=seed, tag=77, device=dev, dtype=name)
+    return H, w, g
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("S", [1, 2, 5, 9])
+@pytest.mark.parametrize("T,d", [(37, 7168), (5, 264), (300, 7176), (64, 256)])
+def test_backward_matches_oracle(dtype, S, T, d):
+    note(f"backward dtype={dtype} S={S} T={T} d={d}")
+    H, w, g = inputs(S, T, d, dtype, seed=S * 100 + T)
+    dev = H.device
+    # every other source accumulates into a random float32 prefill
+    mask = sum(1 << s for s in range(S) if s % 2 == 1)
+    prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(3), device=dev)
+    grads = prefill.clone()
+    dw = B.aggregate_backward(H, w, g, grads, accumulate=mask)
+    torch.cuda.synchronize()
+    pre = host(prefill)
+    for s in range(S):
+        if not (mask >> s) & 1:
+            pre[s] = 0.0
+    check(host(grads), host(dw), host(H), host(w), host(g), f"S={S} T={T} d={d}", prefill=pre)
+
+
+def test_backward_accumulate_is_one_float32_addition():
+    H, w, g = inputs(6, 33, 1032, torch.bfloat16, seed=5)
+    dev = H.device
+    fresh = torch.empty((6, 33, 1032), dtype=torch.float32, device=dev)
+    B.aggregate_backward(H, w, g, fresh)
+    prefill = torch.randn(fresh.shape, generator=torch.Generator(device=dev).manual_seed(9), device=dev)
+    acc = prefill.clone()
+    B.aggregate_backward(H, w, g, acc, accumulate=(1 << 6) - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, prefill + fresh)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_backward_grad_last_is_the_rounded_last_row(dtype):
+    H, w, g = inputs(4, 41, 520, dtype, seed=6)
+    dev = H.device
+    grads = torch.randn((4, 41, 520), generator=torch.Generator(device=dev).manual_seed(2), device=dev)
+    last = torch.empty((41, 520), dtype=dtype, device=dev)
+    B.aggregate_backward(H, w, g, grads, accumulate=0b1010, grad_last=last)
+    torch.cuda.synchronize()
+    assert torch.equal(last, grads[3].to(dtype))          # torch's conversion rounds to nearest even
+
+
+def test_backward_is_bitwise_deterministic():
+    H, w, g = inputs(9, 700, 7168, torch.bfloat16, seed=7)
+    dev = H.device
+    outs = []
+    for _ in range(2):
+        grads = torch.empty((9, 700, 7168), dtype=torch.float32, device=dev)
+        dw = B.aggregate_backward(H, w, g, grads)
+        outs.append((grads, dw))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_backward_one_source_passes_the_gradient_through(dtype):
+    H, w, g = inputs(1, 50, 264, dtype, seed=8)
+    grads = torch.empty((1, 50, 264), dtype=torch.float32, device=H.device)
+    dw = B.aggregate_backward(H, w, g, grads)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[0], g.float())
+    assert not dw.any()
+
+
+def test_backward_empty_batch_zeroes_grad_w():
+    dev = device()
+    H = torch.empty((3, 0, 256), dtype=torch.bfloat16, device=dev)
+    grads = torch.empty((3, 0, 256), dtype=torch.float32, device=dev)
+    g = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    gw = torch.full((256,), 7.0, device=dev)
+    B.aggregate_backward(H, synth.query(256, device=dev), g, grads, grad_w=gw)
+    torch.cuda.synchronize()
+    assert not gw.any()
+
+
+def test_backward_grid_stride_and_strided_rows():
+    """More tokens than workgroups, sources and gradients at padded row strides."""
+    dev = device()
+    S, T, d = 5, 1500, 264
+    Hbig, w, g = inputs(S, T + 3, d, torch.bfloat16, seed=10)
+    H = Hbig[:, :T]                                      # row stride (T+3)*d
+    g = g[:T].contiguous()
+    gbig = torch.zeros((S, T + 5, d), dtype=torch.float32, device=dev)
+    grads = gbig[:, :T]
+    dw = B.aggregate_backward(H, w, g, grads)
+    torch.cuda.synchronize()
+    check(host(grads), host(dw), host(H), host(w), host(g), "grid-stride")
+    assert not gbig[:, T:].any(), "rows past T were written"
+
+
+def test_backward_last_source_apart_equals_stacked():
+    H, w, g = inputs(4, 90, 1024, torch.bfloat16, seed=12)
+    dev = H.device
+    a = torch.empty((4, 90, 1024), dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    dwa = B.aggregate_backward(H, w, g, a)
+    last = H[3].clone()
+    dwb = B.aggregate_backward(H[:3], w, g, b, last_source=last)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(dwa, dwb)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_add_rows_is_the_partial_update(dtype):
+    dev = device()
+    a = synth.layer_output(77, 1032, std=3.0, seed=1, tag=1, device=dev).to(dtype)
+    b = synth.layer_output(77, 1032, std=0.01, seed=1, tag=2, device=dev).to(dtype)
+    out = torch.empty_like(a)
+    B.add_rows(a, b, out)
+    copy = torch.empty_like(a)
+    B.add_rows(None, b, copy)
+    inplace = a.clone()
+    B.add_rows(inplace, b, inplace)
+    torch.cuda.synchronize()
+    ref = orc.accumulate(host(a), host(b), "bf16" if dtype == torch.bfloat16 else "f32")
+    assert np.array_equal(host(out), ref) and torch.equal(copy, b) and torch.equal(inplace, out)
+
+
+def test_backward_full_size_sampled():
+    """The bench's backward shape (T = 32768, d = 7168, S = 9): sampled tokens'
+    dH against the oracle; dw over a gathered sample against the oracle; and dw
+    of the whole batch equal (to float32 rounding) to the sum of dw over two
+    halves -- properties that hold at any size."""
+    dev = device()
+    S, T, d = 9, 32768, 7168
+    note("backward full size")
+    H, w, g = inputs(S, T, d, torch.bfloat16, seed=21)
+    grads = torch.empty((S, T, d), dtype=torch.float32, device=dev)
+    dw = B.aggregate_backward(H, w, g, grads)
+    rows = synth.token_sample(T, 48, 16, seed=3).to(dev)
+    Hs = H.index_select(1, rows).contiguous()
+    gs = g.index_select(0, rows).contiguous()
+    torch.cuda.synchronize()
+    check(host(grads.index_select(1, rows)), None, host(Hs), host(w), host(gs), "full-size sampled dH")
+    # dw over exactly the sampled tokens, run on the GPU as a small batch
+    small = torch.empty((S, rows.numel(), d), dtype=torch.float32, device=dev)
+    dw_small = B.aggregate_backward(Hs, w, gs, small)
+    torch.cuda.synchronize()
+    check(host(small), host(dw_small), host(Hs), host(w), host(gs), "gathered sample")
+    assert torch.equal(small, grads.index_select(1, rows)), "a token's dH depends only on that token"
+    # linearity over tokens
+    half = T // 2
+    g1 = torch.empty((S, half, d), dtype=torch.float32, device=dev)
+    dw1 = B.aggregate_backward(H[:, :half], w, g[:half].contiguous(), g1)
+    dw2 = B.aggregate_backward(H[:, half:], w, g[half:].contiguous(), g1)
+    torch.cuda.synchronize()
+    tot = (dw1.double() + dw2.double()).cpu().numpy()
+    err = np.max(np.abs(host(dw).astype(np.float64) - tot))
+    assert err <= 1e-5 * np.max(np.abs(tot)), f"dw over the batch vs the two halves: {err:.3e}"
+
+
+@pytest.mark.parametrize("final", [True, False])
+def test_schedule_backward_matches_oracle(final):
+    """10 layers in blocks of 4, every gradient compared with the oracle's
+    run_schedule_backward (dF and dh_0 rounded to bf16 when handed out)."""
+    dev = device()
+    L, bs, T, d = 10, 4, 48, 264
+    note(f"schedule backward final={final}")
+    store = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev)
+    synth.fill_normal_(store.h0, 1.0, seed=2, tag=1)
+    Fs = [synth.layer_output(T, d, std=0.3, seed=2, tag=l, device=dev) for l in range(L)]
+    Ws = [synth.query(d, seed=2, device=dev, tag=l) for l in range(L)]
+    wf = synth.query(d, seed=2, device=dev, tag=500)
+    gr = [synth.layer_output(T, d, std=1.0, seed=2, tag=100 + l, device=dev) for l in range(L)]
+    gf = synth.layer_output(T, d, std=1.0, seed=2, tag=999, device=dev)
+    schedule.run_schedule(store, Fs, Ws, bs, final_query=wf if final else None)
+    handed = {}
+    gs, gw, gwf = schedule.run_schedule_backward(
+        store, Fs, Ws, bs, gr, final_query=wf if final else None, grad_final=gf if final else None,
+        on_grad=lambda l, dF: handed.__setitem__(l, dF.clone()))
+    torch.cuda.synchronize()
+    ref = orc.run_schedule_backward(host(store.h0), [host(F) for F in Fs], [host(w) for w in Ws], bs, "bf16",
+                                    [host(x) for x in gr], final_query=host(wf) if final else None,
+                                    grad_final=host(gf) if final else None)
+    scale = max(np.max(np.abs(x)) for x in ref["dF"] + [ref["dh0"]])
+    # float32 accumulation of up to L+1 aggregations' gradients, then one bf16 rounding
+    for l in range(0, L + 1):
+        want = ref["dh0"] if l == 0 else ref["dF"][l - 1]
+        got = host(handed[l])
+        err = np.abs(got - want)
+        lim = 2.0 ** -8 * np.abs(want) + 1e-4 * scale
+        assert np.all(err <= lim), f"dF_{l}: max error {np.max(err):.3e}"
+    err = np.max(np.abs(host(gs[0]) - ref["dh0"]))
+    assert err <= 1e-4 * scale, f"dh0 row: {err:.3e}"
+    for l in range(L):
+        wscale = np.max(np.abs(ref["dw"][l])) + 1e-30
+        e = np.max(np.abs(host(gw[l]) - ref["dw"][l]))
+        assert e <= 1e-3 * wscale, f"dw layer {l + 1}: {e:.3e} of {wscale:.3e}"
+    if final:
+        e = np.max(np.abs(host(gwf) - ref["dw_final"]))
+        assert e <= 1e-3 * np.max(np.abs(ref["dw_final"])), f"dw final: {e:.3e}"
