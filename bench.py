@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="prefill_t262144",
-                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93", "full_s94"])
+                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93", "full_s94",
+                            "backward_t32768", "schedule_93_backward"])
     p.add_argument("--decode-T", type=int, default=64)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded oracle timing budget")
@@ -121,6 +122,35 @@ def pattern_ceiling(T: int, d: int):
     return json.loads(proc.stdout.strip().splitlines()[-1])
 
 
+def cpu_baseline_backward(wl, budget_s: float, seed: int):
+    """The oracle's backward, as it is, on a bounded token sample."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from depth_wise_attention_block_amd import synth
+    from oracle import attnres_oracle as orc
+
+    rows = synth.token_sample(wl.T, 8192, 0, seed=seed + 19)
+    chunk = 64
+    w = wl.w.float().cpu().numpy()
+    done, elapsed, k = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        while elapsed < budget_s and k * chunk < rows.numel():
+            idx = rows[k * chunk:(k + 1) * chunk].to(wl.H.device)
+            k += 1
+            H = wl.H.index_select(1, idx).float().cpu().numpy()
+            g = wl.g.index_select(0, idx).float().cpu().numpy()
+            t0 = time.perf_counter()
+            orc.depth_attention_backward(H, w, g)
+            elapsed += time.perf_counter() - t0
+            done += idx.numel()
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} tokens of the same step (9-source aggregation backward), float64 NumPy, "
+                      f"one thread, {elapsed:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,7 +160,7 @@ def main():
         sys.exit(2)
 
     ceiling = None
-    if args.workload not in ("schedule_93", "full_s94") and not args.no_pattern_probe:
+    if args.workload in ("prefill_t262144", "layer_t4096", "decode") and not args.no_pattern_probe:
         T_probe = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
         ceiling = pattern_ceiling(T_probe, 7168)
 
@@ -146,7 +176,22 @@ def main():
 
     fused = not args.unfused
     t_setup = time.perf_counter()
-    if args.workload == "full_s94":
+    if args.workload == "backward_t32768":
+        wl = workloads.LayerBackward(32768, seed=args.seed, device=dev)
+        T = wl.T
+        step_bytes = wl.step_bytes()
+        cfg = {"workload": "backward_t32768", "T": T, "d": wl.d, "S": wl.S,
+               "step": "one aggregation backward: recompute, float32 source gradients accumulated, "
+                       "last source's gradient handed out (bf16), dL/dw reduced over tokens"}
+    elif args.workload == "schedule_93_backward":
+        wl = workloads.ScheduleBackward(32768, seed=args.seed, device=dev)
+        T = wl.T
+        step_bytes = wl.step_bytes()
+        cfg = {"workload": "schedule_93_backward", "T": T, "d": wl.d, "layers": wl.layers,
+               "block_size": wl.block_size,
+               "step": "output-layer + 93 aggregation backwards in reverse, partial sums recomputed per block, "
+                       "float32 source gradients, each layer output's gradient handed out"}
+    elif args.workload == "full_s94":
         wl = workloads.ManySources(32768, 94, seed=args.seed, device=dev)
         T = wl.T
         step_bytes = wl.step_bytes()
@@ -184,7 +229,10 @@ def main():
         if args.workload == "schedule_93":
             wl.step(mode=sched_mode)
             return
-        if args.workload == "full_s94":
+        if args.workload == "schedule_93_backward":
+            wl.step()
+            return
+        if args.workload in ("full_s94", "backward_t32768"):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
             if ev:
                 ev[0].record(stream)
@@ -225,21 +273,22 @@ def main():
     wall = time.perf_counter() - t0
 
     detail = {"setup_s": round(setup_s, 1), "fused": fused}
-    if args.workload == "schedule_93":
+    if args.workload in ("schedule_93", "schedule_93_backward"):
         ms_step = wall * 1e3 / args.steps
         achieved = step_bytes / (ms_step * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                 "kernel": "whole schedule (all launches of one pass)", "bytes_per_launch": step_bytes}
         detail["step_gb"] = step_bytes / 1e9
-    elif args.workload == "full_s94":
+    elif args.workload in ("full_s94", "backward_t32768"):
         dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
         ms_step = wall * 1e3 / args.steps
         achieved = step_bytes / (dom_ms * 1e-3) / 1e9
+        kernel = {"full_s94": "aggregate_many_kernel<true, 2>",
+                  "backward_t32768": "aggregate_backward_kernel<true, 2> + reduce_rows_kernel"}[args.workload]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                "kernel": "aggregate_many_kernel<true, 2>", "bytes_per_launch": step_bytes,
-                "avg_launch_ms": round(dom_ms, 4)}
+                "kernel": kernel, "bytes_per_launch": step_bytes, "avg_launch_ms": round(dom_ms, 4)}
     else:
         dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
         if copy_store is not None:
@@ -266,8 +315,10 @@ def main():
                            "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1)})
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload not in ("schedule_93", "full_s94"):
+    if not args.no_cpu_baseline and args.workload in ("prefill_t262144", "layer_t4096", "decode"):
         cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
+    elif not args.no_cpu_baseline and args.workload == "backward_t32768":
+        cpu = cpu_baseline_backward(wl, args.cpu_seconds, args.seed)
 
     line = {
         "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,

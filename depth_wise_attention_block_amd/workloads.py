@@ -187,3 +187,76 @@ class ManySources:
     def step_bytes(self) -> int:
         S, T, d = self.S, self.T, self.d
         return T * (2 * S * d + 2 * d + 4 * S) + 4 * d
+
+
+class LayerBackward:
+    """One aggregation's backward at S = 9 (h_0, seven block representations,
+    the partial sum): recompute the forward, add every source's gradient into
+    its float32 gradient row, hand out the last source's new gradient (bf16),
+    and reduce dL/dw over the tokens -- one ``attnres_aggregate_backward``."""
+
+    def __init__(self, T: int, d: int = 7168, *, seed: int = 0, device="cuda", scale=(0.5, 50.0)):
+        from .binding import backward_workspace_bytes
+        self.T, self.d, self.S = T, d, MAX_SOURCES
+        self.H = synth.sources(self.S, T, d, scale=scale, seed=seed, device=device)
+        self.w = synth.query(d, seed=seed, device=device)
+        self.g = synth.layer_output(T, d, std=1.0, seed=seed, tag=3, device=device)
+        self.grads = torch.zeros((self.S, T, d), dtype=torch.float32, device=device)
+        self.grad_last = torch.empty((T, d), dtype=torch.bfloat16, device=device)
+        self.grad_w = torch.empty(d, dtype=torch.float32, device=device)
+        nbytes = backward_workspace_bytes(T, d)
+        self.workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=device)
+
+    def step(self):
+        from .binding import aggregate_backward
+        aggregate_backward(self.H, self.w, self.g, self.grads, accumulate=(1 << self.S) - 1, grad_w=self.grad_w,
+                           grad_last=self.grad_last, workspace=self.workspace)
+
+    def step_bytes(self) -> int:
+        """Sources and g in, float32 gradient rows read and written, the last
+        source's gradient out (bf16), the query in and dL/dw out."""
+        S, T, d = self.S, self.T, self.d
+        return T * (2 * S * d + 2 * d + 8 * S * d + 2 * d) + 8 * d
+
+
+class ScheduleBackward:
+    """The backward of the whole 93-layer schedule at one batch of tokens: the
+    output layer's aggregation, then layers 93..1 in reverse, each block's
+    partial sums recomputed, every source gradient accumulated in float32 and
+    each layer output's finished gradient handed out (bf16).  The forward
+    (outside the timed region) leaves h_0 and the block representations in the
+    store; dL/dr_l are synthetic inputs."""
+
+    def __init__(self, T: int, d: int = 7168, *, layers: int = 93, block_size: int = 12, seed: int = 0,
+                 device="cuda"):
+        self.fwd = Schedule(T, d, layers=layers, block_size=block_size, seed=seed, device=device)
+        self.T, self.d, self.layers, self.block_size = T, d, layers, block_size
+        self.fwd.step(mode="fused")
+        self.dr = [synth.layer_output(T, d, std=1.0, seed=seed, tag=5000 + l, device=device) for l in range(layers)]
+        self.dr_final = synth.layer_output(T, d, std=1.0, seed=seed, tag=6000, device=device)
+        nblocks = (layers + block_size - 1) // block_size
+        self.grad_store = torch.empty((1 + nblocks, T, d), dtype=torch.float32, device=device)
+        self.grad_w = [torch.empty(d, dtype=torch.float32, device=device) for _ in range(layers)]
+        self.grad_w_final = torch.empty(d, dtype=torch.float32, device=device)
+
+    def step(self, on_grad=None):
+        from .schedule import run_schedule_backward
+        run_schedule_backward(self.fwd.store, self.fwd.F, self.fwd.W, self.block_size, self.dr,
+                              final_query=self.fwd.w_out, grad_final=self.dr_final, grad_store=self.grad_store,
+                              grad_w=self.grad_w, grad_w_final=self.grad_w_final, on_grad=on_grad)
+
+    def step_bytes(self) -> int:
+        T, d, L, bs = self.T, self.d, self.layers, self.block_size
+        row2, row4 = 2 * T * d, 4 * T * d
+        counts = self.fwd.source_counts()
+        nblocks = (L + bs - 1) // bs
+        # output layer: sources and g in, gradient rows written (first touch), dF out
+        total = counts[-1] * row2 + row2 + counts[-1] * row4 + row2 + 8 * d
+        for l in range(1, L + 1):
+            S = counts[l - 1]
+            total += S * row2 + row2 + 2 * S * row4 + row2 + 8 * d
+        for n in range(1, nblocks + 1):           # partial sums recomputed: a copy, then additions
+            B = min(n * bs, L) - (n - 1) * bs
+            if B >= 2:
+                total += 2 * row2 + (B - 2) * 3 * row2
+        return total

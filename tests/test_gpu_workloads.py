@@ -109,3 +109,33 @@ def test_schedule_93_layers_sampled():
             ref["final_r"], ref["final_a"], True, "schedule output layer")
     del wl
     torch.cuda.empty_cache()
+
+
+def test_schedule_93_backward_sampled():
+    """The bench's backward of the 93-layer schedule (T = 32768): every layer
+    output's handed-out gradient (bf16), and dL/dh_0, for sampled tokens
+    against the oracle's schedule backward on those tokens alone (a token's
+    gradients depend on that token only)."""
+    dev = device()
+    T = 32768
+    note(f"schedule backward T={T}: forward, then ~45 GB of upstream gradients")
+    wl = workloads.ScheduleBackward(T, seed=0, device=dev)
+    idx = synth.token_sample(T, 24, 8, seed=2).to(dev)
+    handed = {}
+    wl.step(on_grad=lambda l, dF: handed.__setitem__(l, host(dF.index_select(0, idx))))
+    torch.cuda.synchronize()
+    note(f"schedule backward: GPU done, oracle on {idx.numel()} tokens")
+    fwd = wl.fwd
+    ref = orc.run_schedule_backward(host(fwd.store.h0.index_select(0, idx)),
+                                    [host(F.index_select(0, idx)) for F in fwd.F], [host(w) for w in fwd.W],
+                                    wl.block_size, "bf16", [host(g.index_select(0, idx)) for g in wl.dr],
+                                    final_query=host(fwd.w_out), grad_final=host(wl.dr_final.index_select(0, idx)))
+    scale = max(np.max(np.abs(x)) for x in ref["dF"] + [ref["dh0"]])
+    assert sorted(handed) == list(range(0, wl.layers + 1))
+    for l in range(0, wl.layers + 1):
+        want = ref["dh0"] if l == 0 else ref["dF"][l - 1]
+        err = np.abs(handed[l] - want)
+        lim = 2.0 ** -8 * np.abs(want) + 1e-4 * scale
+        assert np.all(err <= lim), f"dF_{l}: max error {np.max(err):.3e}"
+    del wl
+    torch.cuda.empty_cache()
