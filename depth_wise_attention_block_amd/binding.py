@@ -73,9 +73,15 @@ _SIGNATURES = {
     "attnres_aggregate_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p,
-                                                  ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
                                                   ctypes.c_void_p]),
+    "attnres_block_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_void_p]),
     "attnres_aggregate_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                             ctypes.POINTER(ctypes.c_int64)]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -194,7 +200,8 @@ def add_rows(a: torch.Tensor | None, b: torch.Tensor, out: torch.Tensor, stream=
 
 
 def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.Tensor, grad_sources: torch.Tensor,
-                       *, last_source: torch.Tensor | None = None, accumulate=0, grad_w: torch.Tensor | None = None,
+                       *, last_source: torch.Tensor | None = None, accumulate=0, defer=0,
+                       coef: torch.Tensor | None = None, coef_stride: int = 0, grad_w: torch.Tensor | None = None,
                        grad_last: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                        eps: float = 1e-5, stream=None) -> torch.Tensor:
     """``attnres_aggregate_backward``: writes (or, for the sources whose bit is
@@ -203,7 +210,10 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
     (``grad_w``, float32 ``[d]``).  ``sources`` holds the S rows, or the first
     S-1 when ``last_source`` ``[T, d]`` gives the last one apart.  ``grad_out``
     is dL/dr ``[T, d]`` in the sources' dtype; ``grad_last`` (optional,
-    ``[T, d]`` sources' dtype) receives the new gradient of the last source."""
+    ``[T, d]`` sources' dtype) receives the new gradient of the last source.
+    Sources in the ``defer`` mask keep their gradient rows untouched and write
+    their coefficients to ``coef`` (float32, ``coef_stride`` floats per token,
+    may be a view starting mid-row) for :func:`block_backward`."""
     if grad_sources.dim() != 3 or sources.dim() != 3:
         raise ValueError("sources and grad_sources must be 3-D")
     S, T, d = grad_sources.shape
@@ -233,17 +243,51 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
     if not workspace.is_contiguous() or workspace.device != dev:
         raise ValueError("workspace must be a contiguous device tensor")
     mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
+    if defer and (coef is None or coef.dtype != torch.float32 or coef.device != dev):
+        raise ValueError("deferred sources need a float32 coef buffer on the device")
     src_stride = sources.stride(0) if sources.shape[0] > 1 else T * d
     grad_stride = grad_sources.stride(0) if S > 1 else T * d
     src_ptr = sources.data_ptr() if sources.shape[0] > 0 else None
     rc = lib().attnres_aggregate_backward(
         src_ptr, S, T, d, src_stride, last_source.data_ptr() if last_source is not None else None, w.data_ptr(),
         grad_out.data_ptr(), grad_sources.data_ptr(),
-        grad_stride, mask & 0xFFFFFFFF, grad_last.data_ptr() if grad_last is not None else None, grad_w.data_ptr(),
+        grad_stride, mask & 0xFFFFFFFF, defer & 0xFFFFFFFF, coef.data_ptr() if defer else None, int(coef_stride),
+        grad_last.data_ptr() if grad_last is not None else None, grad_w.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), float(eps), _dtype_code(sources),
         _stream(dev, stream))
     _check("attnres_aggregate_backward", rc)
     return grad_w
+
+
+def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor, grad_sources: torch.Tensor, *,
+                   accumulate=0, grad_last: torch.Tensor | None = None, stream=None) -> None:
+    """``attnres_block_backward``: add the B layers' deferred contributions into
+    the n inter-block gradient rows ``grad_sources`` ``[n, T, d]`` float32.
+    ``sources`` ``[n, T, d]``; ``grad_outs`` / ``queries``: B tensors ``[T, d]``
+    / ``[d]``; ``coef`` float32 ``[T, B, n, 3]``."""
+    n, T, d = grad_sources.shape
+    Bl = len(grad_outs)
+    if sources.shape != grad_sources.shape or len(queries) != Bl:
+        raise ValueError("sources must match grad_sources; one query per upstream gradient")
+    dev = grad_sources.device
+    for name, t in (("sources", sources), ("grad_sources", grad_sources)):
+        if T > 0 and (t.stride(2) != 1 or t.stride(1) != d):
+            raise ValueError(f"each row of {name} must be a contiguous [T, d] block")
+    if coef.dtype != torch.float32 or not coef.is_contiguous() or coef.numel() != T * Bl * n * 3:
+        raise ValueError("coef must be a contiguous float32 [T, B, n, 3] tensor")
+    for g in grad_outs:
+        if g.dtype != sources.dtype or not g.is_contiguous() or g.numel() != T * d:
+            raise ValueError("each upstream gradient must be a contiguous [T, d] tensor like the sources")
+    for w in queries:
+        if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != d:
+            raise ValueError("each query must be a contiguous float32 [d] tensor")
+    garr = (ctypes.c_void_p * Bl)(*[g.data_ptr() for g in grad_outs])
+    warr = (ctypes.c_void_p * Bl)(*[w.data_ptr() for w in queries])
+    mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
+    _check("attnres_block_backward", lib().attnres_block_backward(
+        sources.data_ptr(), n, T, d, sources.stride(0) if n > 1 else T * d, Bl, garr, warr, coef.data_ptr(),
+        grad_sources.data_ptr(), grad_sources.stride(0) if n > 1 else T * d, mask & 0xFFFFFFFF,
+        grad_last.data_ptr() if grad_last is not None else None, _dtype_code(sources), _stream(dev, stream)))
 
 
 def prepared_query_shape(n: int, d: int):

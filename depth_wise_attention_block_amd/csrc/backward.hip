@@ -70,6 +70,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
                           const u32x4* __restrict__ last_src, const float* __restrict__ w,
                           const u32x4* __restrict__ gout,
                           f32x4* __restrict__ grad, int64_t grad_stride_v, unsigned acc_mask,
+                          unsigned defer_mask, float* __restrict__ coef, int64_t coef_stride,
                           u32x4* __restrict__ grad_last, float* __restrict__ dw_rows, float eps, float inv_d) {
   using El = Elems<kBf16>;
   constexpr int kE = El::kE, kGv = El::kG;
@@ -174,6 +175,13 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
     const float delta = a * (ug - ubar);             // dL/dz_s
     const float c1 = delta / rho;                    // coefficient of w (and of H_s in dL/dw)
     const float c3 = c1 * z * inv_d / rho;           // coefficient of H_s in dL/dH_s
+    // deferred sources: their three coefficients go out instead of a gradient row
+    if (wave == 0 && lane < S && ((defer_mask >> lane) & 1u)) {
+      float* cf = coef + t * coef_stride + 3 * lane;
+      cf[0] = a;
+      cf[1] = c1;
+      cf[2] = c3;
+    }
     float as[kMaxSrc], c1s[kMaxSrc], c3s[kMaxSrc];
 #pragma unroll
     for (int s = 0; s < kMaxSrc; ++s) {
@@ -186,7 +194,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
     //    source; the old rows of source s+1 load while source s is formed
     f32x4 old[2][kV][kGv];
     auto load_old = [&](int s, f32x4 (&o)[kV][kGv]) {
-      const bool add = (acc_mask >> s) & 1u;
+      const bool add = ((acc_mask & ~defer_mask) >> s) & 1u;
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
         const int idx = v * nthr + tid;
@@ -234,7 +242,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
           for (int h = 0; h < kGv; ++h) {
             f32x4 o = old[s & 1][v][h];
             o = f32x4{o[0] + r[4 * h], o[1] + r[4 * h + 1], o[2] + r[4 * h + 2], o[3] + r[4 * h + 3]};
-            if (idx < nvec) {
+            if (idx < nvec && !((defer_mask >> s) & 1u)) {
               __builtin_nontemporal_store(o, grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
               old[s & 1][v][h] = o;  // kept for the copy of the last source's gradient
             }
@@ -274,6 +282,109 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
   }
 }
 
+// Deferred gradients of a block's inter-block sources (the sources every layer
+// of the block shares: h_0, b_1 .. b_{n-1}).  Each layer's backward wrote, per
+// token and source, a_{l,s}, c1_{l,s} = delta/rho and c3_{l,s} =
+// delta z/(d rho^2); here, per token and source,
+//     G_s += sum_l (a_{l,s} g_l + c1_{l,s} w_l) - (sum_l c3_{l,s}) H_s,
+// one read-modify-write of each gradient row per block instead of one per
+// layer.  The coefficients of a token are staged in LDS and read as broadcasts.
+template <bool kBf16, int kV>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(kV <= 2 ? 4 : 2)))
+block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec, int64_t src_stride_v,
+                      BlockRows rows, int B, const float* __restrict__ coef, f32x4* __restrict__ grad,
+                      int64_t grad_stride_v, unsigned acc_mask, u32x4* __restrict__ grad_last) {
+  using El = Elems<kBf16>;
+  constexpr int kE = El::kE, kGv = El::kG;
+  __shared__ float cf[2][kMaxBlockLayers * kMaxInterSources * 3];
+  __shared__ float c3sum[2][kMaxInterSources];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int per_tok = B * n * 3;
+
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+    for (int k = tid; k < per_tok; k += nthr) cf[buf][k] = coef[t * per_tok + k];
+    __syncthreads();
+    if (tid < n) {
+      float c3 = 0.f;
+      for (int l = 0; l < B; ++l) c3 += cf[buf][(l * n + tid) * 3 + 2];
+      c3sum[buf][tid] = c3;
+    }
+    __syncthreads();
+    const u32x4* tok = src + t * (int64_t)nvec;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      if (idx >= nvec) continue;
+      float acc[kMaxInterSources][kE];
+#pragma unroll
+      for (int s = 0; s < kMaxInterSources; ++s) {
+        if (s < n) {
+          float xe[kE];
+          unpack<kBf16>(__builtin_nontemporal_load(tok + s * src_stride_v + idx), xe);
+          const float c3 = c3sum[buf][s];
+#pragma unroll
+          for (int h = 0; h < kGv; ++h) {
+            f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+            if ((acc_mask >> s) & 1u)
+              o = __builtin_nontemporal_load(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[s][4 * h + c] = fmaf(-c3, xe[4 * h + c], o[c]);
+          }
+        }
+      }
+      // layer l's g and w rows, the next layer's loading meanwhile
+      u32x4 gn = __builtin_nontemporal_load(static_cast<const u32x4*>(rows.g[0]) + t * (int64_t)nvec + idx);
+      f32x4 wn[kGv];
+#pragma unroll
+      for (int h = 0; h < kGv; ++h) wn[h] = reinterpret_cast<const f32x4*>(rows.w[0])[idx * kGv + h];
+      for (int l = 0; l < B; ++l) {
+        float ge[kE], we[kE];
+        unpack<kBf16>(gn, ge);
+#pragma unroll
+        for (int h = 0; h < kGv; ++h)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) we[4 * h + c] = wn[h][c];
+        if (l + 1 < B) {
+          gn = __builtin_nontemporal_load(static_cast<const u32x4*>(rows.g[l + 1]) + t * (int64_t)nvec + idx);
+#pragma unroll
+          for (int h = 0; h < kGv; ++h) wn[h] = reinterpret_cast<const f32x4*>(rows.w[l + 1])[idx * kGv + h];
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxInterSources; ++s) {
+          if (s < n) {
+            const float a = cf[buf][(l * n + s) * 3], c1 = cf[buf][(l * n + s) * 3 + 1];
+#pragma unroll
+            for (int e = 0; e < kE; ++e) acc[s][e] = fmaf(a, ge[e], fmaf(c1, we[e], acc[s][e]));
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < kMaxInterSources; ++s) {
+        if (s < n) {
+#pragma unroll
+          for (int h = 0; h < kGv; ++h)
+            __builtin_nontemporal_store(f32x4{acc[s][4 * h], acc[s][4 * h + 1], acc[s][4 * h + 2], acc[s][4 * h + 3]},
+                                        grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+          if (grad_last != nullptr && s == n - 1) {
+            u32x4 o;
+            if constexpr (kBf16) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[s][2 * k], acc[s][2 * k + 1]);
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(acc[s][k]);
+            }
+            __builtin_nontemporal_store(o, grad_last + t * (int64_t)nvec + idx);
+          }
+        }
+      }
+    }
+  }
+}
+
 // out[j] = sum over p = 0 .. rows-1 of in[p][j], in that order.
 __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ in, int64_t rows, int n,
                                                           float* __restrict__ out) {
@@ -292,8 +403,8 @@ hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
                        static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4),
                        static_cast<const u32x4*>(a.last_source), a.w,
                        static_cast<const u32x4*>(a.grad_out), reinterpret_cast<f32x4*>(a.grad_sources),
-                       a.grad_stride / 4, a.acc_mask, static_cast<u32x4*>(a.grad_last), a.workspace, a.eps,
-                       1.0f / (float)a.d);
+                       a.grad_stride / 4, a.acc_mask, a.defer_mask, a.coef, a.coef_stride,
+                       static_cast<u32x4*>(a.grad_last), a.workspace, a.eps, 1.0f / (float)a.d);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -314,10 +425,36 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t stream) {
   }
 }
 
+template <bool kBf16, int kV>
+hipError_t launch_block_v(const BlockBackwardArgs& a, hipStream_t stream) {
+  const int nvec = a.d / (kBf16 ? 8 : 4);
+  hipLaunchKernelGGL((block_backward_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+                     static_cast<const u32x4*>(a.sources), a.n, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4), a.rows,
+                     a.B, a.coef, reinterpret_cast<f32x4*>(a.grad_sources), a.grad_stride / 4, a.acc_mask,
+                     static_cast<u32x4*>(a.grad_last));
+  return hipGetLastError();
+}
+
+template <bool kBf16>
+hipError_t launch_block(const BlockBackwardArgs& a, hipStream_t stream) {
+  switch (a.vecs_per_lane) {
+    case 1: return launch_block_v<kBf16, 1>(a, stream);
+    case 2: return launch_block_v<kBf16, 2>(a, stream);
+    case 3: return launch_block_v<kBf16, 3>(a, stream);
+    case 4: return launch_block_v<kBf16, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream) {
   return a.bf16 ? launch_bwd<true>(a, stream) : launch_bwd<false>(a, stream);
+}
+
+hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  return a.bf16 ? launch_block<true>(a, stream) : launch_block<false>(a, stream);
 }
 
 }  // namespace attnres

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "attnres.h"
 #include "internal.h"
@@ -208,7 +209,8 @@ ATTNRES_API int attnres_aggregate_backward_workspace(int64_t T, int32_t d, int32
 ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
                                            const void* last_source, const float* w, const void* grad_out,
                                            float* grad_sources,
-                                           int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                           int64_t grad_stride, uint32_t accumulate_mask, uint32_t defer_mask,
+                                           float* coef, int64_t coef_stride, void* grad_last,
                                            float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
                                            int32_t dtype, void* stream) {
   if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
@@ -224,6 +226,12 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
   if (grad_w == nullptr) return ATTNRES_EINVAL;
   if ((reinterpret_cast<uintptr_t>(grad_w) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+  defer_mask &= (S >= 32) ? 0xFFFFFFFFu : ((1u << S) - 1u);
+  if (defer_mask != 0) {
+    if (coef == nullptr || coef_stride < 3 * (int64_t)S) return ATTNRES_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(coef) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    if (grad_last != nullptr && ((defer_mask >> (S - 1)) & 1u)) return ATTNRES_EINVAL;  // nothing to hand out
+  }
   const int es = elem_bytes(dtype);
   const Range r_gw = range(grad_w, (int64_t)d * 4);
   if (T > 0) {
@@ -243,12 +251,15 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
     const Range r_gs = range(grad_sources, ((int64_t)(S - 1) * grad_stride + row) * 4);
     const Range r_gl = grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0};
     const Range r_ws = range(workspace, workspace_bytes);
-    const Range outs[4] = {r_gs, r_gl, r_gw, r_ws};
+    // coefficients are written for the deferred sources only, up to the highest one
+    const int top = defer_mask != 0 ? 32 - __builtin_clz(defer_mask) : 0;
+    const Range r_cf = defer_mask != 0 ? range(coef, ((T - 1) * coef_stride + 3 * (int64_t)top) * 4) : Range{0, 0};
+    const Range outs[5] = {r_gs, r_gl, r_gw, r_ws, r_cf};
     const Range ins[4] = {r_src, r_w, r_g, r_last};
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
       for (int k = 0; k < 4; ++k)
         if (overlap(outs[i], ins[k])) return ATTNRES_EALIAS;
-      for (int k = i + 1; k < 4; ++k)
+      for (int k = i + 1; k < 5; ++k)
         if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
     }
   }
@@ -272,6 +283,9 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   a.grad_sources = grad_sources;
   a.grad_stride = grad_stride;
   a.acc_mask = accumulate_mask;
+  a.defer_mask = defer_mask;
+  a.coef = coef;
+  a.coef_stride = coef_stride;
   a.grad_last = grad_last;
   a.grad_w = grad_w;
   a.workspace = static_cast<float*>(workspace);
@@ -283,6 +297,69 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   (void)hipGetLastError();
   return attnres::launch_aggregate_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                                : ATTNRES_ELAUNCH;
+}
+
+ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
+                                       int32_t B, const void* const* grad_outs, const float* const* queries,
+                                       const float* coef, float* grad_sources, int64_t grad_stride,
+                                       uint32_t accumulate_mask, void* grad_last, int32_t dtype, void* stream) {
+  if (n < 1 || n > attnres::kMaxInterSources || B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  const int64_t row = T * (int64_t)d;
+  if (src_stride == 0) src_stride = row;
+  if (grad_stride == 0) grad_stride = row;
+  if (src_stride < 0 || grad_stride < 0 || src_stride > (INT64_C(1) << 40) || grad_stride > (INT64_C(1) << 40))
+    return ATTNRES_EINVAL;
+  if (n > 1 && (src_stride < row || grad_stride < row)) return ATTNRES_EINVAL;
+  if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
+  if (T == 0) return ATTNRES_OK;
+  if (sources == nullptr || grad_outs == nullptr || queries == nullptr || coef == nullptr || grad_sources == nullptr)
+    return ATTNRES_EINVAL;
+  const int es = elem_bytes(dtype);
+  const Range r_gs = range(grad_sources, ((int64_t)(n - 1) * grad_stride + row) * 4);
+  const Range r_gl = grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0};
+  if (!aligned16(sources) || !aligned16(grad_sources) || (grad_last != nullptr && !aligned16(grad_last)) ||
+      (reinterpret_cast<uintptr_t>(coef) & 3u) != 0)
+    return ATTNRES_EUNSUPPORTED;
+  std::vector<Range> ins = {range(sources, ((int64_t)(n - 1) * src_stride + row) * es),
+                            range(coef, (int64_t)T * B * n * 3 * 4)};
+  attnres::BlockBackwardArgs a;
+  for (int l = 0; l < B; ++l) {
+    if (grad_outs[l] == nullptr || queries[l] == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(grad_outs[l]) || !aligned16(queries[l])) return ATTNRES_EUNSUPPORTED;
+    ins.push_back(range(grad_outs[l], row * es));
+    ins.push_back(range(queries[l], (int64_t)d * 4));
+    a.rows.g[l] = grad_outs[l];
+    a.rows.w[l] = queries[l];
+  }
+  for (const Range& r : ins)
+    if (overlap(r_gs, r) || overlap(r_gl, r)) return ATTNRES_EALIAS;
+  if (overlap(r_gs, r_gl)) return ATTNRES_EALIAS;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  attnres_launch_t cfg;
+  rc = pick_config(n, T, d, dtype, cus, &cfg);
+  if (rc != ATTNRES_OK) return rc;
+  a.sources = sources;
+  a.n = n;
+  a.T = T;
+  a.d = d;
+  a.src_stride = src_stride;
+  a.B = B;
+  a.coef = coef;
+  a.grad_sources = grad_sources;
+  a.grad_stride = grad_stride;
+  a.acc_mask = accumulate_mask;
+  a.grad_last = grad_last;
+  a.bf16 = dtype == ATTNRES_BF16;
+  a.threads = cfg.threads;
+  a.vecs_per_lane = cfg.vecs_per_lane;
+  a.grid = cfg.grid;
+  (void)hipGetLastError();
+  return attnres::launch_block_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                           : ATTNRES_ELAUNCH;
 }
 
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,

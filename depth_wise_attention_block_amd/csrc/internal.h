@@ -118,6 +118,9 @@ struct BackwardArgs {
   float* grad_sources;    // S rows of [T][d] at grad_stride floats
   int64_t grad_stride;
   unsigned acc_mask;      // bit s: add into row s
+  unsigned defer_mask;    // bit s: leave row s, write source s's coefficients instead
+  float* coef;            // [T] x coef_stride floats: (a, c1, c3) of deferred source s at 3s
+  int64_t coef_stride;
   void* grad_last;        // [T][d] source dtype, or nullptr
   float* grad_w;          // [d]
   float* workspace;       // grid rows of [d]
@@ -128,6 +131,32 @@ struct BackwardArgs {
 };
 
 hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream);
+
+// The deferred inter-block gradients of one block (see block_backward_kernel).
+constexpr int kMaxBlockLayers = 16;
+struct BlockRows {
+  const void* g[kMaxBlockLayers];    // dL/dr of the block's layers, [T][d] source dtype
+  const float* w[kMaxBlockLayers];   // their queries, [d] float32
+};
+struct BlockBackwardArgs {
+  const void* sources;    // n inter-block rows at src_stride elements
+  int n;
+  int64_t T;
+  int d;
+  int64_t src_stride;
+  BlockRows rows;
+  int B;
+  const float* coef;      // [T][B][n][3]
+  float* grad_sources;    // n rows of [T][d] float32 at grad_stride floats
+  int64_t grad_stride;
+  unsigned acc_mask;
+  void* grad_last;        // [T][d] source dtype: the new row n-1, or nullptr
+  bool bf16;
+  int threads, vecs_per_lane;
+  int64_t grid;
+};
+
+hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream);
 
 
 }  // namespace attnres

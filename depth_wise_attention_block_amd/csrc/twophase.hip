@@ -45,20 +45,20 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <int kV>
 constexpr int waves_per_simd2() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
-// The inter-block pass holds kK rows of kV vectors per lane.  With 8 rows at
-// kV = 2 it needs about 150 VGPRs: 3 waves per SIMD and no spills run faster
-// than 4 waves with spills to scratch.  4 rows fit in 128 VGPRs (4 waves).
-// (8 rows at kV = 4, d above 14336, cannot fit in 256 and spill a little.)
+// The inter-block pass holds kK rows of kV vectors per lane.  At kV = 2 both
+// instances run at 4 waves per SIMD (two 7-wave workgroups per CU): 4 rows fit
+// in 128 VGPRs; the 8-row instance spills ~20 loop-invariant values, which
+// measured faster than 3 waves per SIMD without spills.  Wider rows (kV >= 3)
+// get 2 waves per SIMD.
 template <int kV, int kK>
 constexpr int waves_per_simd_prepare() {
-  return kV == 1 ? (kK <= 4 ? 5 : 4) : kV == 2 ? 4 : 2;
+  return kV <= 2 ? 4 : 2;
 }
 
 // Byte selectors of v_perm_b32 (result byte i <- selector byte i; 0-3 pick the
 // second operand's bytes, 4-7 the first's): (a.lo, b.lo) and (a.hi, b.hi).
 constexpr unsigned kSelLo = 0x05040100u, kSelHi = 0x07060302u;
 
-__device__ __forceinline__ unsigned pack2(float a, float b) { return pack_bf16(a, b); }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. kN-1 (compile-time i).
 template <int kN, typename F, int... kIs>

@@ -195,7 +195,8 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
                           block_size: int, grad_r, *, final_query: Optional[torch.Tensor] = None,
                           grad_final: Optional[torch.Tensor] = None, grad_store: Optional[torch.Tensor] = None,
                           grad_w: Optional[Sequence[torch.Tensor]] = None, grad_w_final: Optional[torch.Tensor] = None,
-                          on_grad: Optional[Callable[[int, torch.Tensor], None]] = None, eps: float = 1e-5):
+                          on_grad: Optional[Callable[[int, torch.Tensor], None]] = None, defer: bool = True,
+                          eps: float = 1e-5):
     """Backward of ``run_schedule``, layer by layer in reverse, recomputing each
     block's partial sums (kimi.papertok.ai §4.6: the aggregation is
     recomputed in the backward pass).
@@ -203,18 +204,22 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     ``store`` is the forward's store after the pass (h_0 and every block
     representation; left unchanged).  Each block's partial sums are recomputed
     into a buffer of their own and passed to the layer's backward as its last
-    source.
-    ``grad_r`` is a sequence of dL/dr_l ``[T, d]`` (store dtype) or a callable
-    ``grad_r(l, dF_l) -> dL/dr_l``: the layer's own backward, given the finished
-    gradient of its output.  Gradients of the sources accumulate in
+    source.  ``grad_r`` is a sequence of dL/dr_l ``[T, d]`` (store dtype) or a
+    callable ``grad_r(l, dF_l) -> dL/dr_l``: the layer's own backward, given
+    the finished gradient of its output.  Gradients of the sources accumulate in
     ``grad_store`` ``[1 + blocks, T, d]`` float32: row 0 is dL/dh_0, row n the
     gradient of block n's representation, which is also the running gradient
-    of its partial sums; each aggregation's backward hands out the finished
-    gradient of the previous layer's output (``on_grad(l, dF_l)``, store dtype,
-    l = L..0 where dF_0 is dL/dh_0 rounded).  Returns ``(grad_store, grad_w,
-    grad_w_final)``.
+    of its partial sums.  ``on_grad(l, dF_l)`` receives each layer output's
+    finished gradient (store dtype), l = L..0 where dF_0 is dL/dh_0 rounded.
+
+    With ``defer`` (default) the gradients of a block's inter-block sources
+    (h_0, b_1 .. b_{n-1}, shared by all its layers) are not updated per layer:
+    each layer's backward writes three coefficients per token and source, and
+    one ``attnres_block_backward`` per block applies them -- one
+    read-modify-write of those rows per block instead of one per layer.
+    Returns ``(grad_store, grad_w, grad_w_final)``.
     """
-    from .binding import add_rows, aggregate_backward
+    from .binding import add_rows, aggregate_backward, block_backward
 
     L = len(layer_outputs)
     T, d = store.T, store.d
@@ -230,20 +235,22 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         grad_w_final = torch.empty(d, dtype=torch.float32, device=dev)
     slots = store.slots
     dF = torch.empty((T, d), dtype=dt, device=dev)
-    partials = torch.empty((block_size, T, d), dtype=dt, device=dev)  # partials[i-1]: before position i
-    ready = 0            # grad_store rows [0, ready) hold a gradient already
+    partials = torch.empty((block_size, T, d), dtype=dt, device=dev)  # partials[i-2]: before position i
+    coef_all = (torch.empty(T * block_size * nblocks * 3, dtype=torch.float32, device=dev)
+                if defer else None)
+    holds = [False] * (1 + nblocks)   # which gradient rows already hold a gradient
 
-    def mask(S):
-        return (1 << min(S, ready)) - 1
+    def acc_mask(rows):
+        return sum(1 << k for k, r in enumerate(rows) if holds[r])
 
     def dr(l):
         return grad_r(l, dF) if callable(grad_r) else grad_r[l - 1]
 
     if final_query is not None:
         S = 1 + nblocks
-        aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=mask(S),
+        aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
                            grad_w=grad_w_final, grad_last=dF, eps=eps)
-        ready = S
+        holds[:S] = [True] * S
     else:
         dF.zero_()
     if on_grad is not None:
@@ -251,21 +258,35 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     for n in range(nblocks, 0, -1):
         first = (n - 1) * block_size + 1
         last = min(n * block_size, L)
+        B = last - first + 1
         # the block's partial sums, formed exactly as the forward formed them
-        for i in range(2, last - first + 2):
+        for i in range(2, B + 1):
             add_rows(partials[i - 3] if i > 2 else None, layer_outputs[first + i - 3], partials[i - 2])
+        coef = coef_all[:T * B * n * 3].view(T, B, n, 3) if defer else None
+        block_g = [None] * B
         for l in range(last, first - 1, -1):
             i = l - first + 1
             g = dr(l)
+            block_g[i - 1] = g
+            cf = dict(defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * (i - 1):], coef_stride=3 * n * B) if defer else {}
             if i >= 2:
-                S = n + 1
-                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:S], last_source=partials[i - 2],
-                                   accumulate=mask(S), grad_w=grad_w[l - 1], grad_last=dF, eps=eps)
+                rows = list(range(n + 1))
+                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n + 1], last_source=partials[i - 2],
+                                   accumulate=acc_mask(rows), grad_w=grad_w[l - 1], grad_last=dF, eps=eps, **cf)
+                touched = rows if not defer else [n]
             else:
-                S = n
-                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:S], accumulate=mask(S),
-                                   grad_w=grad_w[l - 1], grad_last=dF, eps=eps)
-            ready = max(ready, S)
-            if on_grad is not None:
+                rows = list(range(n))
+                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n], accumulate=acc_mask(rows),
+                                   grad_w=grad_w[l - 1], grad_last=None if defer else dF, eps=eps, **cf)
+                touched = [] if defer else rows
+            for r in touched:
+                holds[r] = True
+            if on_grad is not None and (i >= 2 or not defer):
                 on_grad(l - 1, dF)
+        if defer:
+            block_backward(slots[:n], block_g, [queries[j - 1] for j in range(first, last + 1)], coef,
+                           grad_store[:n], accumulate=acc_mask(range(n)), grad_last=dF)
+            holds[:n] = [True] * n
+            if on_grad is not None:
+                on_grad(first - 1, dF)
     return grad_store, grad_w, grad_w_final

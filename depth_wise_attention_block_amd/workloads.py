@@ -245,18 +245,33 @@ class ScheduleBackward:
                               final_query=self.fwd.w_out, grad_final=self.dr_final, grad_store=self.grad_store,
                               grad_w=self.grad_w, grad_w_final=self.grad_w_final, on_grad=on_grad)
 
-    def step_bytes(self) -> int:
+    def step_bytes(self, defer: bool = True) -> int:
+        """Algorithmic bytes of one backward pass.  Every layer reads its
+        sources and dL/dr and hands out a gradient; with ``defer`` a layer
+        updates only its partial's gradient row and writes 3 coefficients per
+        token and inter-block source, and one pass per block reads the block's
+        inter-block sources, its dL/dr rows and coefficients and
+        read-modify-writes each inter-block gradient row once; without, every
+        layer read-modify-writes all its sources' gradient rows."""
         T, d, L, bs = self.T, self.d, self.layers, self.block_size
         row2, row4 = 2 * T * d, 4 * T * d
-        counts = self.fwd.source_counts()
         nblocks = (L + bs - 1) // bs
         # output layer: sources and g in, gradient rows written (first touch), dF out
-        total = counts[-1] * row2 + row2 + counts[-1] * row4 + row2 + 8 * d
-        for l in range(1, L + 1):
-            S = counts[l - 1]
-            total += S * row2 + row2 + 2 * S * row4 + row2 + 8 * d
-        for n in range(1, nblocks + 1):           # partial sums recomputed: a copy, then additions
+        S = 1 + nblocks
+        total = S * row2 + row2 + S * row4 + row2 + 8 * d
+        for n in range(1, nblocks + 1):
             B = min(n * bs, L) - (n - 1) * bs
-            if B >= 2:
+            if B >= 2:                                   # partial sums recomputed: a copy, then additions
                 total += 2 * row2 + (B - 2) * 3 * row2
+            for i in range(1, B + 1):
+                S = n + (1 if i >= 2 else 0)
+                total += S * row2 + row2 + 8 * d             # sources, g; query in, dL/dw out
+                if defer:
+                    total += 12 * n * T                      # coefficients of the inter-block sources
+                    if i >= 2:
+                        total += 2 * row4 + row2             # the partial's gradient row, dF out
+                else:
+                    total += 2 * S * row4 + row2             # every gradient row, dF out
+            if defer:                                        # one pass per block
+                total += n * row2 + B * row2 + 12 * n * B * T + 2 * n * row4 + row2 + 4 * d * B
         return total

@@ -287,8 +287,13 @@ ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_
  *                   floats (0 means T*d); 16-byte aligned.  Row s is overwritten
  *                   with dL/dH_s, or, when bit s of accumulate_mask is set, has
  *                   it added (float32).
+ *   defer_mask      bit s: leave grad row s alone and write source s's three
+ *                   coefficients instead, (a_s, delta_s/rho_s, delta_s z_s/(d rho_s^2))
+ *                   as float32 at coef[t*coef_stride + 3s .. 3s+2], for
+ *                   attnres_block_backward to apply later (coef_stride >= 3S).
  *   grad_last       device, [T][d] in dtype (round to nearest even for bf16), or
- *                   NULL: receives the new value of grad row S-1 -- in a Block
+ *                   NULL (required NULL when source S-1 is deferred): receives the
+ *                   new value of grad row S-1 -- in a Block
  *                   AttnRes backward that is the finished gradient of the
  *                   previous layer's output.
  *   grad_w          device, [d] float32, overwritten with dL/dw (zero for T = 0).
@@ -302,9 +307,33 @@ ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_
 ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
                                            const void* last_source, const float* w, const void* grad_out,
                                            float* grad_sources,
-                                           int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                           int64_t grad_stride, uint32_t accumulate_mask, uint32_t defer_mask,
+                                           float* coef, int64_t coef_stride, void* grad_last,
                                            float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
                                            int32_t dtype, void* stream);
+
+/*
+ * attnres_block_backward -- the deferred gradients of a block's inter-block
+ * sources.  In Block AttnRes the n sources h_0, b_1 .. b_{n-1} are shared by
+ * every layer of block n (kimi.papertok.ai §4.3); when the B layers' backwards
+ * defer them (attnres_aggregate_backward, defer_mask), this adds all their
+ * contributions in one pass, per token and source:
+ *   G_s += sum_l (a_{l,s} g_l + c1_{l,s} w_l) - (sum_l c3_{l,s}) H_s
+ *
+ *   sources       device, n rows [T][d] (dtype) at src_stride elements, n <= 8.
+ *   B             layers, 1..16; grad_outs[l] (device [T][d] dtype, dL/dr_l) and
+ *                 queries[l] (device [d] float32) are HOST arrays of B pointers.
+ *   coef          device float32 [T][B][n][3]: layer l's coefficients, as its
+ *                 backward wrote them with coef = coef + 3 n l, coef_stride 3 n B.
+ *   grad_sources  device, n rows [T][d] float32 at grad_stride floats; rows whose
+ *                 bit is set in accumulate_mask are added into, others written.
+ *   grad_last     device [T][d] dtype, or NULL: the new gradient row n-1 (the
+ *                 finished gradient of the previous block's last layer output).
+ */
+ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
+                                       int32_t B, const void* const* grad_outs, const float* const* queries,
+                                       const float* coef, float* grad_sources, int64_t grad_stride,
+                                       uint32_t accumulate_mask, void* grad_last, int32_t dtype, void* stream);
 
 /* Workspace bytes attnres_aggregate_backward needs for T tokens of width d on
  * the current device (host only apart from a device-attribute query). */

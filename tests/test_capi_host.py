@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -258,10 +258,12 @@ def test_backward_host_checks(lib):
     """attnres_aggregate_backward rejects bad arguments before touching the GPU."""
     GS, GL, GW, WS = 0x60000000, 0x68000000, 0x6C000000, 0x70000000
 
+    CF = 0x74000000
+
     def bwd(S=3, T=4, d=8, src=SRC, w=W, g=OUT, gs=GS, gstride=0, gl=None, gw=GW, ws=WS, wsb=1 << 20, eps=1e-5,
-            dtype=B.BF16, src_stride=0, last=None):
-        return B.lib().attnres_aggregate_backward(src, S, T, d, src_stride, last, w, g, gs, gstride, 0, gl, gw, ws,
-                                                  wsb, eps, dtype, None)
+            dtype=B.BF16, src_stride=0, last=None, defer=0, cf=None, cfs=0):
+        return B.lib().attnres_aggregate_backward(src, S, T, d, src_stride, last, w, g, gs, gstride, 0, defer, cf,
+                                                  cfs, gl, gw, ws, wsb, eps, dtype, None)
 
     assert bwd(S=0) == B.EINVAL and bwd(S=10) == B.EINVAL          # Block AttnRes sizes only
     assert bwd(T=-1) == B.EINVAL and bwd(d=12) == B.EUNSUPPORTED
@@ -275,6 +277,23 @@ def test_backward_host_checks(lib):
     assert bwd(ws=GS + 64) == B.EALIAS and bwd(gl=GS + 16) == B.EALIAS
     assert bwd(last=SRC + 8) == B.EUNSUPPORTED and bwd(last=GS) == B.EALIAS
     assert bwd(S=1, src=None) == B.EINVAL
+    assert bwd(defer=0b011, cf=None, cfs=9) == B.EINVAL and bwd(defer=0b011, cf=CF, cfs=8) == B.EINVAL
+    assert bwd(defer=0b011, cf=CF + 2, cfs=9) == B.EUNSUPPORTED
+    assert bwd(defer=0b100, cf=CF, cfs=9, gl=GL) == B.EINVAL          # the last source is deferred
+    assert bwd(defer=0b011, cf=GS + 4, cfs=9) == B.EALIAS and bwd(defer=0b011, cf=SRC, cfs=9) == B.EALIAS
+
+    Arr = ctypes.c_void_p * 2
+    G2, W2 = Arr(OUT, OUT + 4096), Arr(W, W + 4096)
+
+    def blk(n=3, T=4, d=8, src=SRC, Bl=2, gs_=G2, ws_=W2, cf=CF, grads=GS, gl=None, dtype=B.BF16, gstride=0):
+        return B.lib().attnres_block_backward(src, n, T, d, 0, Bl, gs_, ws_, cf, grads, gstride, 0, gl, dtype, None)
+
+    assert blk(n=0) == B.EINVAL and blk(n=9) == B.EINVAL and blk(Bl=0) == B.EINVAL and blk(Bl=17) == B.EINVAL
+    assert blk(T=0) == B.OK and blk(d=12) == B.EUNSUPPORTED and blk(gstride=8) == B.EINVAL
+    assert blk(src=None) == B.EINVAL and blk(cf=None) == B.EINVAL and blk(grads=None) == B.EINVAL
+    assert blk(gs_=Arr(OUT, 0)) == B.EINVAL and blk(ws_=Arr(W, W + 8)) == B.EUNSUPPORTED
+    assert blk(grads=GS + 8) == B.EUNSUPPORTED and blk(cf=CF + 2) == B.EUNSUPPORTED
+    assert blk(grads=SRC) == B.EALIAS and blk(gl=OUT + 4096) == B.EALIAS and blk(grads=CF) == B.EALIAS
 
     add = B.lib().attnres_add_rows
     assert add(None, None, W, 4, 8, B.BF16, None) == B.EINVAL and add(None, OUT, None, 4, 8, B.BF16, None) == B.EINVAL

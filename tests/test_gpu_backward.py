@@ -230,13 +230,15 @@ def test_backward_full_size_sampled():
     assert err <= 1e-5 * np.max(np.abs(tot)), f"dw over the batch vs the two halves: {err:.3e}"
 
 
+@pytest.mark.parametrize("defer", [True, False], ids=["deferred", "per_layer"])
 @pytest.mark.parametrize("final", [True, False])
-def test_schedule_backward_matches_oracle(final):
+def test_schedule_backward_matches_oracle(final, defer):
     """10 layers in blocks of 4, every gradient compared with the oracle's
-    run_schedule_backward (dF and dh_0 rounded to bf16 when handed out)."""
+    run_schedule_backward (dF and dh_0 rounded to bf16 when handed out); the
+    inter-block gradients deferred to one pass per block, or updated per layer."""
     dev = device()
     L, bs, T, d = 10, 4, 48, 264
-    note(f"schedule backward final={final}")
+    note(f"schedule backward final={final} defer={defer}")
     store = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev)
     synth.fill_normal_(store.h0, 1.0, seed=2, tag=1)
     Fs = [synth.layer_output(T, d, std=0.3, seed=2, tag=l, device=dev) for l in range(L)]
@@ -248,7 +250,7 @@ def test_schedule_backward_matches_oracle(final):
     handed = {}
     gs, gw, gwf = schedule.run_schedule_backward(
         store, Fs, Ws, bs, gr, final_query=wf if final else None, grad_final=gf if final else None,
-        on_grad=lambda l, dF: handed.__setitem__(l, dF.clone()))
+        on_grad=lambda l, dF: handed.__setitem__(l, dF.clone()), defer=defer)
     torch.cuda.synchronize()
     ref = orc.run_schedule_backward(host(store.h0), [host(F) for F in Fs], [host(w) for w in Ws], bs, "bf16",
                                     [host(x) for x in gr], final_query=host(wf) if final else None,
@@ -270,3 +272,40 @@ def test_schedule_backward_matches_oracle(final):
     if final:
         e = np.max(np.abs(host(gwf) - ref["dw_final"]))
         assert e <= 1e-3 * np.max(np.abs(ref["dw_final"])), f"dw final: {e:.3e}"
+
+
+def test_block_backward_equals_per_layer_updates():
+    """One block of B = 6 layers over n = 5 inter-block sources (+ a partial):
+    deferring the inter-block gradients to attnres_block_backward gives the
+    per-layer result up to float32 summation order; the partial's gradient row
+    and dL/dw are identical."""
+    dev = device()
+    n, Bl, T, d = 5, 6, 70, 1032
+    H, _, _ = inputs(n, T, d, torch.bfloat16, seed=31)
+    part = synth.layer_output(T, d, std=2.0, seed=31, tag=9, device=dev)
+    Ws = [synth.query(d, seed=31, device=dev, tag=l) for l in range(Bl)]
+    Gs = [synth.layer_output(T, d, std=1.0, seed=31, tag=50 + l, device=dev) for l in range(Bl)]
+    prefill = torch.randn((n + 1, T, d), generator=torch.Generator(device=dev).manual_seed(4), device=dev)
+    ref = prefill.clone()
+    got = prefill.clone()
+    coef = torch.empty((T, Bl, n, 3), dtype=torch.float32, device=dev)
+    dws_ref, dws_got = [], []
+    last_ref = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    last_got = torch.empty_like(last_ref)
+    for l in range(Bl):
+        dws_ref.append(B.aggregate_backward(H, Ws[l], Gs[l], ref, last_source=part, accumulate=(1 << (n + 1)) - 1,
+                                            grad_last=last_ref))
+        dws_got.append(B.aggregate_backward(H, Ws[l], Gs[l], got, last_source=part, accumulate=(1 << (n + 1)) - 1,
+                                            defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * l:],
+                                            coef_stride=3 * n * Bl, grad_last=last_got))
+    torch.cuda.synchronize()
+    assert torch.equal(last_ref, last_got) and torch.equal(ref[n], got[n]), "partial row"
+    assert all(torch.equal(a, b) for a, b in zip(dws_ref, dws_got)), "dL/dw"
+    assert torch.equal(got[:n], prefill[:n]), "deferred rows must be untouched before the block pass"
+    emit = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    B.block_backward(H, Gs, Ws, coef, got[:n], accumulate=(1 << n) - 1, grad_last=emit)
+    torch.cuda.synchronize()
+    diff = (got[:n] - ref[:n]).abs().max().item()
+    scale = ref[:n].abs().max().item()
+    assert diff <= 1e-5 * scale, f"deferred vs per-layer: {diff:.3e} of {scale:.3e}"
+    assert torch.equal(emit, got[n - 1].to(torch.bfloat16))
