@@ -77,6 +77,9 @@ _SIGNATURES = {
                                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
                                                   ctypes.c_void_p]),
+    "attnres_partial_sums": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_void_p]),
     "attnres_block_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
@@ -257,6 +260,26 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
         _stream(dev, stream))
     _check("attnres_aggregate_backward", rc)
     return grad_w
+
+
+def partial_sums(layer_outs, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """``attnres_partial_sums``: ``out[k]`` = F_0 + ... + F_k as the store forms
+    them; ``layer_outs`` is a list of ``[T, d]`` tensors, ``out`` ``[count, T, d]``
+    (rows contiguous, any row stride)."""
+    count = len(layer_outs)
+    if count == 0 or out.dim() != 3 or out.shape[0] < count:
+        raise ValueError("out must be [>= count, T, d]")
+    _, T, d = out.shape
+    for F in layer_outs:
+        if F.dtype != out.dtype or not F.is_contiguous() or tuple(F.shape) != (T, d):
+            raise ValueError("each layer output must be a contiguous [T, d] tensor like out")
+    if T > 0 and (out.stride(2) != 1 or out.stride(1) != d):
+        raise ValueError("each row of out must be a contiguous [T, d] block")
+    arr = (ctypes.c_void_p * count)(*[F.data_ptr() for F in layer_outs])
+    _check("attnres_partial_sums", lib().attnres_partial_sums(arr, count, T, d, out.data_ptr(),
+                                                              out.stride(0) if count > 1 else T * d,
+                                                              _dtype_code(out), _stream(out.device, stream)))
+    return out
 
 
 def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor, grad_sources: torch.Tensor, *,

@@ -385,13 +385,55 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
   }
 }
 
-// out[j] = sum over p = 0 .. rows-1 of in[p][j], in that order.
+// out[j] = sum over p < rows of in[p][j] in a fixed order: slice k of 8 sums
+// rows k, k+8, k+16, ... in turn, then the 8 slice sums are added in order.
+// A block covers 32 columns with 8 slices each.
 __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ in, int64_t rows, int n,
                                                           float* __restrict__ out) {
-  for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) {
-    float acc = 0.f;
-    for (int64_t p = 0; p < rows; ++p) acc += in[p * n + j];
-    out[j] = acc;
+  __shared__ float part[8][32];
+  const int col = threadIdx.x & 31, slice = threadIdx.x >> 5;
+  const int j = blockIdx.x * 32 + col;
+  float acc = 0.f;
+  if (j < n) {
+    int64_t p = slice;
+    for (; p + 24 < rows; p += 32) {       // four independent loads in flight
+      const float a0 = in[p * n + j], a1 = in[(p + 8) * n + j], a2 = in[(p + 16) * n + j],
+                  a3 = in[(p + 24) * n + j];
+      acc = (((acc + a0) + a1) + a2) + a3;
+    }
+    for (; p < rows; p += 8) acc += in[p * n + j];
+  }
+  part[slice][col] = acc;
+  __syncthreads();
+  if (slice == 0 && j < n) {
+    float tot = part[0][col];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) tot += part[k][col];
+    out[j] = tot;
+  }
+}
+
+// The running partial sums of a block's layer outputs, formed exactly as the
+// store forms them (each step one float32 addition, then for bf16 one rounding
+// to nearest even): out[0] = F_0, out[k] = out[k-1] + F_k.  One pass: every
+// layer output read once and every partial written once.
+template <bool kBf16>
+__global__ void __launch_bounds__(256) partial_sums_kernel(BlockRows rows, int count, int64_t nvec,
+                                                           u32x4* __restrict__ out, int64_t out_stride_v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+    u32x4 f[kMaxBlockLayers];
+#pragma unroll
+    for (int k = 0; k < kMaxBlockLayers; ++k)
+      if (k < count) f[k] = __builtin_nontemporal_load(static_cast<const u32x4*>(rows.g[k]) + i);
+    u32x4 acc = f[0];
+    __builtin_nontemporal_store(acc, out + i);
+#pragma unroll
+    for (int k = 1; k < kMaxBlockLayers; ++k) {
+      if (k < count) {
+        acc = add_rows(acc, f[k], kBf16);
+        __builtin_nontemporal_store(acc, out + k * out_stride_v + i);
+      }
+    }
   }
 }
 
@@ -408,7 +450,7 @@ hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  int blocks = (a.d + 255) / 256;
+  const int blocks = (a.d + 31) / 32;
   hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.workspace,
                      a.T > 0 ? a.grid : (int64_t)0, a.d, a.grad_w);
   return hipGetLastError();
@@ -455,6 +497,21 @@ hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream) 
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   return a.bf16 ? launch_block<true>(a, stream) : launch_block<false>(a, stream);
+}
+
+hipError_t launch_partial_sums(const PartialSumsArgs& a, hipStream_t stream) {
+  const int64_t nvec = a.elems / (a.bf16 ? 8 : 4);
+  if (nvec == 0) return hipSuccess;
+  int64_t grid = (nvec + 255) / 256;
+  const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 8;
+  if (grid > cap) grid = cap;
+  if (a.bf16)
+    hipLaunchKernelGGL((partial_sums_kernel<true>), dim3((unsigned)grid), dim3(256), 0, stream, a.rows, a.count,
+                       nvec, static_cast<u32x4*>(a.out), a.out_stride / 8);
+  else
+    hipLaunchKernelGGL((partial_sums_kernel<false>), dim3((unsigned)grid), dim3(256), 0, stream, a.rows, a.count,
+                       nvec, static_cast<u32x4*>(a.out), a.out_stride / 4);
+  return hipGetLastError();
 }
 
 }  // namespace attnres

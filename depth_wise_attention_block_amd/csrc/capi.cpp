@@ -362,6 +362,41 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
                                                                                            : ATTNRES_ELAUNCH;
 }
 
+ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t count, int64_t T, int32_t d, void* out,
+                                     int64_t out_stride, int32_t dtype, void* stream) {
+  if (count < 1 || count > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  const int64_t row = T * (int64_t)d;
+  if (out_stride == 0) out_stride = row;
+  if (out_stride < 0 || out_stride > (INT64_C(1) << 40) || (count > 1 && out_stride < row)) return ATTNRES_EINVAL;
+  if (out_stride % elems_per_vec(dtype) != 0) return ATTNRES_EUNSUPPORTED;
+  if (row == 0) return ATTNRES_OK;
+  if (layer_outs == nullptr || out == nullptr) return ATTNRES_EINVAL;
+  if (!aligned16(out)) return ATTNRES_EUNSUPPORTED;
+  const int es = elem_bytes(dtype);
+  const Range r_out = range(out, ((int64_t)(count - 1) * out_stride + row) * es);
+  attnres::PartialSumsArgs a;
+  for (int k = 0; k < count; ++k) {
+    if (layer_outs[k] == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(layer_outs[k])) return ATTNRES_EUNSUPPORTED;
+    if (overlap(r_out, range(layer_outs[k], row * es))) return ATTNRES_EALIAS;
+    a.rows.g[k] = layer_outs[k];
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  a.count = count;
+  a.elems = row;
+  a.out = out;
+  a.out_stride = out_stride;
+  a.bf16 = dtype == ATTNRES_BF16;
+  a.num_cus = cus;
+  (void)hipGetLastError();
+  return attnres::launch_partial_sums(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                         : ATTNRES_ELAUNCH;
+}
+
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                              const float* w, void* out, float* weights, float eps, void* stream) {
   int rc = check_store(st);

@@ -158,5 +158,18 @@ struct BlockBackwardArgs {
 
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream);
 
+// Running partial sums of up to kMaxBlockLayers rows (rows.g holds the inputs).
+struct PartialSumsArgs {
+  BlockRows rows;
+  int count;
+  int64_t elems;        // T*d
+  void* out;            // count rows at out_stride elements
+  int64_t out_stride;
+  bool bf16;
+  int num_cus;
+};
+
+hipError_t launch_partial_sums(const PartialSumsArgs& a, hipStream_t stream);
+
 
 }  // namespace attnres

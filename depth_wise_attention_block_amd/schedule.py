@@ -204,7 +204,7 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     ``store`` is the forward's store after the pass (h_0 and every block
     representation; left unchanged).  Each block's partial sums are recomputed
     into a buffer of their own and passed to the layer's backward as its last
-    source.  ``grad_r`` is a sequence of dL/dr_l ``[T, d]`` (store dtype) or a
+    source (one ``attnres_partial_sums`` pass per block).  ``grad_r`` is a sequence of dL/dr_l ``[T, d]`` (store dtype) or a
     callable ``grad_r(l, dF_l) -> dL/dr_l``: the layer's own backward, given
     the finished gradient of its output.  Gradients of the sources accumulate in
     ``grad_store`` ``[1 + blocks, T, d]`` float32: row 0 is dL/dh_0, row n the
@@ -219,7 +219,7 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     read-modify-write of those rows per block instead of one per layer.
     Returns ``(grad_store, grad_w, grad_w_final)``.
     """
-    from .binding import add_rows, aggregate_backward, block_backward
+    from .binding import aggregate_backward, block_backward, partial_sums
 
     L = len(layer_outputs)
     T, d = store.T, store.d
@@ -260,8 +260,8 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         last = min(n * block_size, L)
         B = last - first + 1
         # the block's partial sums, formed exactly as the forward formed them
-        for i in range(2, B + 1):
-            add_rows(partials[i - 3] if i > 2 else None, layer_outputs[first + i - 3], partials[i - 2])
+        if B >= 2:
+            partial_sums([layer_outputs[j - 1] for j in range(first, last)], partials)
         coef = coef_all[:T * B * n * 3].view(T, B, n, 3) if defer else None
         block_g = [None] * B
         for l in range(last, first - 1, -1):

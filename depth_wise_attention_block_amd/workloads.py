@@ -261,8 +261,8 @@ class ScheduleBackward:
         total = S * row2 + row2 + S * row4 + row2 + 8 * d
         for n in range(1, nblocks + 1):
             B = min(n * bs, L) - (n - 1) * bs
-            if B >= 2:                                   # partial sums recomputed: a copy, then additions
-                total += 2 * row2 + (B - 2) * 3 * row2
+            if B >= 2:                                   # partial sums recomputed in one pass
+                total += 2 * (B - 1) * row2
             for i in range(1, B + 1):
                 S = n + (1 if i >= 2 else 0)
                 total += S * row2 + row2 + 8 * d             # sources, g; query in, dL/dw out

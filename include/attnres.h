@@ -267,6 +267,20 @@ ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_
                                  void* stream);
 
 /*
+ * attnres_partial_sums -- the running partial sums of a block's layer outputs,
+ * as the store forms them one update at a time: out[0] = F_0, out[k] =
+ * out[k-1] + F_k (bf16: one float32 addition, then round to nearest even), in
+ * one pass -- e.g. to recompute a block's partial sums for the backward pass
+ * (kimi.papertok.ai §4.6).
+ *   layer_outs  HOST array of count (1..16) device pointers, [T][d] in dtype,
+ *               16-byte aligned.
+ *   out         device, count rows [T][d] in dtype at out_stride elements (0
+ *               means T*d); may not overlap the inputs.
+ */
+ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t count, int64_t T, int32_t d, void* out,
+                                     int64_t out_stride, int32_t dtype, void* stream);
+
+/*
  * attnres_aggregate_backward -- gradients of one aggregation, recomputing its
  * forward (training wraps the aggregation in activation checkpointing,
  * kimi.papertok.ai §4.6).  With g = dL/dr for r = attnres_aggregate(sources, w):

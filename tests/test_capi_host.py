@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -302,3 +302,16 @@ def test_backward_host_checks(lib):
     out = ctypes.c_int64()
     assert B.lib().attnres_aggregate_backward_workspace(0, 8, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
     assert B.lib().attnres_aggregate_backward_workspace(4, 8, B.BF16, None) == B.EINVAL
+
+
+def test_partial_sums_host_checks(lib):
+    Arr = ctypes.c_void_p * 3
+    F3 = Arr(SRC, SRC + 4096, SRC + 8192)
+
+    def ps(arr=F3, count=3, T=4, d=8, out=OUT, stride=0, dtype=B.BF16):
+        return B.lib().attnres_partial_sums(arr, count, T, d, out, stride, dtype, None)
+
+    assert ps(count=0) == B.EINVAL and ps(count=17) == B.EINVAL and ps(d=12) == B.EUNSUPPORTED
+    assert ps(T=0) == B.OK and ps(stride=8) == B.EINVAL and ps(out=None) == B.EINVAL
+    assert ps(out=OUT + 8) == B.EUNSUPPORTED and ps(arr=Arr(SRC, 0, SRC)) == B.EINVAL
+    assert ps(arr=Arr(SRC, SRC + 8, SRC)) == B.EUNSUPPORTED and ps(out=SRC + 4096) == B.EALIAS

@@ -309,3 +309,20 @@ def test_block_backward_equals_per_layer_updates():
     scale = ref[:n].abs().max().item()
     assert diff <= 1e-5 * scale, f"deferred vs per-layer: {diff:.3e} of {scale:.3e}"
     assert torch.equal(emit, got[n - 1].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("count", [1, 2, 11, 16])
+def test_partial_sums_are_the_store_updates(dtype, count):
+    """attnres_partial_sums equals the oracle's update chain bit for bit."""
+    dev = device()
+    T, d = 37, 520
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    Fs = [synth.layer_output(T, d, std=0.1 + k, seed=4, tag=k, device=dev, dtype=name) for k in range(count)]
+    out = torch.empty((16, T, d), dtype=dtype, device=dev)
+    B.partial_sums(Fs, out)
+    torch.cuda.synchronize()
+    part = None
+    for k in range(count):
+        part = orc.accumulate(part, host(Fs[k]), name)
+        assert np.array_equal(host(out[k]), part), f"partial {k}"
