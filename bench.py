@@ -50,6 +50,9 @@ def parse():
                    help="schedule_93 only: per-layer launches (unfused / fused) or the two-phase schedule")
     p.add_argument("--unfused", action="store_true",
                    help="time attnres_accumulate + attnres_aggregate as two launches instead of the fused one")
+    p.add_argument("--rotate", type=int, default=0,
+                   help="input sets to cycle through (default: 3 for layer_t4096 -- 1.76 GB, beyond the 256 MB "
+                        "Infinity Cache -- else 1)")
     p.add_argument("--with-copy", action="store_true",
                    help="also run one plain copy of T*d bf16 per step outside the timed region "
                         "(reference kernel for the HBM byte counters)")
@@ -210,9 +213,11 @@ def main():
                         "unfused": "93 x (aggregate + partial update) + output-layer aggregate"}[sched_mode]}
     else:
         T = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
-        wl = workloads.LayerStep(T, seed=args.seed, device=dev)
+        rotate = args.rotate or (3 if args.workload == "layer_t4096" else 1)
+        wls = [workloads.LayerStep(T, seed=args.seed + k, device=dev) for k in range(rotate)]
+        wl = wls[0]
         step_bytes = wl.step_bytes(fused)
-        cfg = {"workload": args.workload, "T": T, "d": wl.d, "S": 9,
+        cfg = {"workload": args.workload, "T": T, "d": wl.d, "S": 9, "input_sets": rotate,
                "step": ("one fused launch: partial += layer output, then aggregate over 9 sources" if fused else
                         "attnres_accumulate (partial += layer output), then attnres_aggregate over 9 sources")}
     copy_store = None
@@ -224,8 +229,13 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     dom_events, acc_events = [], []   # dominant kernel; stand-alone update (unfused only)
+    step_no = [0]
 
     def one_step(timed: bool):
+        nonlocal wl
+        if args.workload in ("prefill_t262144", "layer_t4096", "decode"):
+            wl = wls[step_no[0] % len(wls)]
+            step_no[0] += 1
         if args.workload == "schedule_93":
             wl.step(mode=sched_mode)
             return
@@ -313,6 +323,27 @@ def main():
             acc_ms = sum(a.elapsed_time(b) for a, b in acc_events) / len(acc_events)
             detail.update({"accumulate_ms": round(acc_ms, 4),
                            "accumulate_gbps": round(wl.accumulate_bytes() / (acc_ms * 1e-3) / 1e9, 1)})
+
+    if args.workload == "decode":
+        # latency per fused call: hot (inputs still in the caches) and cold (a
+        # 512 MB write between calls evicts the 256 MB Infinity Cache)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        lat = {"hot": [], "cold": []}
+        for mode in ("hot", "cold"):
+            for _ in range(200):
+                if mode == "cold":
+                    flush.fill_(1)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record(stream)
+                wl.fused()
+                ev[1].record(stream)
+                lat[mode].append(ev)
+        torch.cuda.synchronize()
+        for mode, evs in lat.items():
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            detail[f"latency_us_{mode}_median"] = round(us[len(us) // 2], 2)
+            detail[f"latency_us_{mode}_min"] = round(us[0], 2)
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline and args.workload in ("prefill_t262144", "layer_t4096", "decode"):
