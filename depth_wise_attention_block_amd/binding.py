@@ -83,8 +83,11 @@ _SIGNATURES = {
     "attnres_block_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int32,
-                                              ctypes.c_void_p]),
+                                              ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_int32, ctypes.c_void_p]),
+    "attnres_block_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "attnres_aggregate_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                             ctypes.POINTER(ctypes.c_int64)]),
     "attnres_aggregate_config": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -190,6 +193,14 @@ def backward_workspace_bytes(T: int, d: int, dtype=torch.bfloat16) -> int:
     return out.value
 
 
+def block_workspace_bytes(T: int, d: int, B: int, dtype=torch.bfloat16) -> int:
+    """``attnres_block_backward_workspace`` on the current device."""
+    out = ctypes.c_int64()
+    _check("attnres_block_backward_workspace",
+           lib().attnres_block_backward_workspace(T, d, B, _DTYPE_CODE[dtype], ctypes.byref(out)))
+    return out.value
+
+
 def add_rows(a: torch.Tensor | None, b: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
     """``attnres_add_rows``: ``out = a + b`` as the partial-sum update forms it
     (``out = b`` when ``a`` is None); rows ``[T, d]``, contiguous."""
@@ -216,7 +227,8 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
     ``[T, d]`` sources' dtype) receives the new gradient of the last source.
     Sources in the ``defer`` mask keep their gradient rows untouched and write
     their coefficients to ``coef`` (float32, ``coef_stride`` floats per token,
-    may be a view starting mid-row) for :func:`block_backward`."""
+    may be a view starting mid-row) for :func:`block_backward`, which also adds
+    their share of dL/dw: the returned ``grad_w`` sums the other sources only."""
     if grad_sources.dim() != 3 or sources.dim() != 3:
         raise ValueError("sources and grad_sources must be 3-D")
     S, T, d = grad_sources.shape
@@ -282,16 +294,18 @@ def partial_sums(layer_outs, out: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
-def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor, grad_sources: torch.Tensor, *,
-                   accumulate=0, grad_last: torch.Tensor | None = None, stream=None) -> None:
+def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor, grad_sources: torch.Tensor,
+                   grad_ws, *, accumulate=0, grad_last: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None) -> None:
     """``attnres_block_backward``: add the B layers' deferred contributions into
-    the n inter-block gradient rows ``grad_sources`` ``[n, T, d]`` float32.
-    ``sources`` ``[n, T, d]``; ``grad_outs`` / ``queries``: B tensors ``[T, d]``
-    / ``[d]``; ``coef`` float32 ``[T, B, n, 3]``."""
+    the n inter-block gradient rows ``grad_sources`` ``[n, T, d]`` float32, and
+    the deferred sources' share of each layer's dL/dw into ``grad_ws[l]``
+    (float32 ``[d]``).  ``sources`` ``[n, T, d]``; ``grad_outs`` / ``queries``:
+    B tensors ``[T, d]`` / ``[d]``; ``coef`` float32 ``[T, B, n, 3]``."""
     n, T, d = grad_sources.shape
     Bl = len(grad_outs)
-    if sources.shape != grad_sources.shape or len(queries) != Bl:
-        raise ValueError("sources must match grad_sources; one query per upstream gradient")
+    if sources.shape != grad_sources.shape or len(queries) != Bl or len(grad_ws) != Bl:
+        raise ValueError("sources must match grad_sources; one query and one dL/dw row per upstream gradient")
     dev = grad_sources.device
     for name, t in (("sources", sources), ("grad_sources", grad_sources)):
         if T > 0 and (t.stride(2) != 1 or t.stride(1) != d):
@@ -301,16 +315,24 @@ def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor
     for g in grad_outs:
         if g.dtype != sources.dtype or not g.is_contiguous() or g.numel() != T * d:
             raise ValueError("each upstream gradient must be a contiguous [T, d] tensor like the sources")
-    for w in queries:
-        if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != d:
-            raise ValueError("each query must be a contiguous float32 [d] tensor")
+    for name, rows in (("query", queries), ("dL/dw row", grad_ws)):
+        for w in rows:
+            if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != d or w.device != dev:
+                raise ValueError(f"each {name} must be a contiguous float32 [d] tensor on {dev}")
+    if workspace is None:
+        nbytes = block_workspace_bytes(T, d, Bl, sources.dtype)
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=dev)
+    if not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous device tensor")
     garr = (ctypes.c_void_p * Bl)(*[g.data_ptr() for g in grad_outs])
     warr = (ctypes.c_void_p * Bl)(*[w.data_ptr() for w in queries])
+    dwarr = (ctypes.c_void_p * Bl)(*[w.data_ptr() for w in grad_ws])
     mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
     _check("attnres_block_backward", lib().attnres_block_backward(
         sources.data_ptr(), n, T, d, sources.stride(0) if n > 1 else T * d, Bl, garr, warr, coef.data_ptr(),
         grad_sources.data_ptr(), grad_sources.stride(0) if n > 1 else T * d, mask & 0xFFFFFFFF,
-        grad_last.data_ptr() if grad_last is not None else None, _dtype_code(sources), _stream(dev, stream)))
+        grad_last.data_ptr() if grad_last is not None else None, dwarr, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _dtype_code(sources), _stream(dev, stream)))
 
 
 def prepared_query_shape(n: int, d: int):

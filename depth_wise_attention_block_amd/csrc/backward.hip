@@ -38,8 +38,8 @@ namespace {
 constexpr int kMaxSrc = 9;  // ATTNRES_MAX_SOURCES
 
 // Registers: all S sources, g and the query stay in registers for the whole
-// token (~190 VGPRs at kV = 2), so one 7-wave workgroup fits per CU; 2 waves
-// per SIMD is then the same occupancy as 3 and leaves room to avoid spills.
+// token (~190 VGPRs at kV = 2), so one 7-wave workgroup fits per CU; 2 waves per
+// SIMD is then the same occupancy as 3 and leaves room to avoid spills.
 template <int kV>
 constexpr int waves_per_simd_bwd() { return kV == 1 ? 4 : 2; }
 
@@ -64,8 +64,25 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&e)[Elems<kBf16>::kE]) {
   }
 }
 
+// dL/dw: each lane keeps its running sums for its own elements in LDS (one row
+// of f32x4 per vector) and adds one token's share, summed in registers over the
+// sources, per trip.
+template <int kV, int kGv>
+__device__ __forceinline__ void add_token_dw(f32x4 (*dw4)[64 * kMaxWaves], int tid, const float (&dtok)[kV][4 * kGv]) {
+#pragma unroll
+  for (int v = 0; v < kV; ++v)
+#pragma unroll
+    for (int h = 0; h < kGv; ++h) {
+      f32x4 acc = dw4[v * kGv + h][tid];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += dtok[v][4 * h + c];
+      dw4[v * kGv + h][tid] = acc;
+    }
+}
+
 template <bool kBf16, int kV>
-__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_bwd<kV>())))
+__global__ void __launch_bounds__(64 * kMaxWaves)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd_bwd<kV>())))
 aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                           const u32x4* __restrict__ last_src, const float* __restrict__ w,
                           const u32x4* __restrict__ gout,
@@ -207,6 +224,11 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
       }
     };
     load_old(0, old[0]);
+    float dtok[kV][kE];
+#pragma unroll
+    for (int v = 0; v < kV; ++v)
+#pragma unroll
+      for (int e = 0; e < kE; ++e) dtok[v][e] = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxSrc; ++s) {
       if (s < S) {
@@ -230,13 +252,11 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
           }
 #pragma unroll
           for (int e = 0; e < kE; ++e) r[e] = fmaf(as[s], ge[e], fmaf(c1s[s], wf[e], -c3s[s] * xe[e]));
-          // dL/dw += c1_s H_s for this lane's elements
+          // this token's share of dL/dw: sum_s c1_s H_s for this lane's elements,
+          // over the sources not deferred (the block pass adds the others')
+          if (!((defer_mask >> s) & 1u)) {
 #pragma unroll
-          for (int h = 0; h < kGv; ++h) {
-            f32x4 acc = dw4[v * kGv + h][tid];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = fmaf(c1s[s], xe[4 * h + c], acc[c]);
-            dw4[v * kGv + h][tid] = acc;
+            for (int e = 0; e < kE; ++e) dtok[v][e] = fmaf(c1s[s], xe[e], dtok[v][e]);
           }
 #pragma unroll
           for (int h = 0; h < kGv; ++h) {
@@ -268,6 +288,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
         __builtin_amdgcn_sched_barrier(0);  // one source's rows in registers at a time
       }
     }
+    add_token_dw<kV, kGv>(dw4, tid, dtok);
   }
 
   // 6. this workgroup's dL/dw row
@@ -278,6 +299,209 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
     if (idx < nvec) {
 #pragma unroll
       for (int h = 0; h < kGv; ++h) reinterpret_cast<f32x4*>(row)[idx * kGv + h] = dw4[v * kGv + h][tid];
+    }
+  }
+}
+
+// The backward when every source but the last is deferred (each layer of a
+// block defers the block's shared inter-block sources): only the last source's
+// gradient row is formed, and only its share of dL/dw -- the deferred sources'
+// shares are summed with their gradient rows in the block pass.  So after the
+// statistics nothing but the last row is needed: the rows stream once through
+// a three-row register ring, the last one is kept, and the kernel fits two
+// workgroups per CU.
+template <bool kBf16, int kV>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(kV <= 2 ? 4 : 2)))
+aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
+                               const u32x4* __restrict__ last_src, const float* __restrict__ w,
+                               const u32x4* __restrict__ gout, f32x4* __restrict__ grad, int64_t grad_stride_v,
+                               unsigned acc_mask, unsigned defer_mask, float* __restrict__ coef,
+                               int64_t coef_stride, u32x4* __restrict__ grad_last, float* __restrict__ dw_rows,
+                               float eps, float inv_d) {
+  using El = Elems<kBf16>;
+  constexpr int kE = El::kE, kGv = El::kG;
+  constexpr int kRing = 3;
+  __shared__ float red[2][kMaxWaves][3][16];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int s16 = lane & 15;
+  const bool write_last = !((defer_mask >> (S - 1)) & 1u);
+
+  Query<kBf16, kV> q;
+  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
+  float dw[kV][kE];  // this lane's running share of dL/dw
+#pragma unroll
+  for (int v = 0; v < kV; ++v)
+#pragma unroll
+    for (int e = 0; e < kE; ++e) dw[v][e] = 0.f;
+
+  int buf = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+    const u32x4* tok = src + t * (int64_t)nvec;
+    auto load_row = [&](int s, u32x4 (&xr)[kV]) {
+      const u32x4* row = (last_src != nullptr && s == S - 1) ? last_src + t * (int64_t)nvec : tok + s * src_stride_v;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int idx = v * nthr + tid;
+        xr[v] = idx < nvec ? __builtin_nontemporal_load(row + idx) : u32x4{0, 0, 0, 0};
+      }
+    };
+
+    u32x4 g[kV], xl[kV];
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      g[v] = idx < nvec ? __builtin_nontemporal_load(gout + t * (int64_t)nvec + idx) : u32x4{0, 0, 0, 0};
+    }
+
+    // 1. statistics, the rows streaming through the ring (kRing - 1 ahead)
+    u32x4 ring[kRing][kV];
+#pragma unroll
+    for (int r = 0; r + 1 < kRing; ++r)
+      if (r < S) load_row(r, ring[r]);
+    float gss = 0.f, gdt = 0.f, gug = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSrc; ++s) {
+      if (s < S) {
+        if (s + kRing - 1 < S) load_row(s + kRing - 1, ring[(s + kRing - 1) % kRing]);
+        const int slot = s % kRing;
+        float ss = 0.f, dt = 0.f, ug = 0.f;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          if constexpr (kBf16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = dot2(ring[slot][v][k], ring[slot][v][k], ss);
+              dt = dot2(ring[slot][v][k], q.hi[v][k], dt);
+              dt = dot2(ring[slot][v][k], q.lo[v][k], dt);
+              ug = dot2(ring[slot][v][k], g[v][k], ug);
+            }
+          } else {
+            const f32x4 xf = __builtin_bit_cast(f32x4, ring[slot][v]);
+            const f32x4 gf = __builtin_bit_cast(f32x4, g[v]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              ss = fmaf(xf[k], xf[k], ss);
+              dt = fmaf(xf[k], q.f[v][k], dt);
+              ug = fmaf(xf[k], gf[k], ug);
+            }
+          }
+          if (s == S - 1) xl[v] = ring[slot][v];
+        }
+        gss = put_lane(wave_sum(ss), s, gss, s16);
+        gdt = put_lane(wave_sum(dt), s, gdt, s16);
+        gug = put_lane(wave_sum(ug), s, gug, s16);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the last row's old gradient loads while the statistics are reduced
+    f32x4 oldl[kV][kGv];
+    {
+      const bool add = write_last && ((acc_mask >> (S - 1)) & 1u);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int idx = v * nthr + tid;
+#pragma unroll
+        for (int h = 0; h < kGv; ++h) {
+          oldl[v][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (add && idx < nvec)
+            oldl[v][h] =
+                __builtin_nontemporal_load(grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+        }
+      }
+    }
+    if (lane < 16) {
+      red[buf][wave][0][lane] = gss;
+      red[buf][wave][1][lane] = gdt;
+      red[buf][wave][2][lane] = gug;
+    }
+    __syncthreads();
+
+    // 2. softmax and coefficients (as the general kernel)
+    float z = -INFINITY, rho = 1.f, ug = 0.f;
+    if (s16 < S) {
+      float ss = 0.f, dt = 0.f;
+      for (int k = 0; k < nwaves; ++k) {
+        ss += red[buf][k][0][s16];
+        dt += red[buf][k][1][s16];
+        ug += red[buf][k][2][s16];
+      }
+      rho = sqrtf(ss * inv_d + eps);
+      z = dt / rho;
+    }
+    const float m = row_max16(z);
+    const float p = (s16 < S) ? expf(z - m) : 0.f;
+    const float a = p / row_sum16(p);
+    const float ubar = row_sum16(a * ug);
+    const float delta = a * (ug - ubar);
+    const float c1 = delta / rho;
+    const float c3 = c1 * z * inv_d / rho;
+    if (wave == 0 && lane < S && ((defer_mask >> lane) & 1u)) {
+      float* cf = coef + t * coef_stride + 3 * lane;
+      cf[0] = a;
+      cf[1] = c1;
+      cf[2] = c3;
+    }
+
+    // 3. the last source: its share of dL/dw, its gradient row and the copy
+    if (write_last) {
+      const float aL = lane_bcast(a, S - 1), c1L = lane_bcast(c1, S - 1), c3L = lane_bcast(c3, S - 1);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int idx = v * nthr + tid;
+        float xe[kE], ge[kE], wf[kE];
+        unpack<kBf16>(xl[v], xe);
+        unpack<kBf16>(g[v], ge);
+        if constexpr (kBf16) {
+          float lo[kE];
+          unpack<true>(q.hi[v], wf);
+          unpack<true>(q.lo[v], lo);
+#pragma unroll
+          for (int e = 0; e < kE; ++e) wf[e] += lo[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) wf[e] = q.f[v][e];
+        }
+#pragma unroll
+        for (int e = 0; e < kE; ++e) dw[v][e] = fmaf(c1L, xe[e], dw[v][e]);
+        f32x4 o[kGv];
+#pragma unroll
+        for (int h = 0; h < kGv; ++h) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * h + c;
+            o[h][c] = oldl[v][h][c] + fmaf(aL, ge[e], fmaf(c1L, wf[e], -c3L * xe[e]));
+          }
+          if (idx < nvec)
+            __builtin_nontemporal_store(o[h], grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+        }
+        if (grad_last != nullptr && idx < nvec) {
+          u32x4 ob;
+          if constexpr (kBf16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ob[k] = pack_bf16(o[k >> 1][2 * (k & 1)], o[k >> 1][2 * (k & 1) + 1]);
+          } else {
+            ob = __builtin_bit_cast(u32x4, o[0]);
+          }
+          __builtin_nontemporal_store(ob, grad_last + t * (int64_t)nvec + idx);
+        }
+      }
+    }
+  }
+
+  float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int idx = v * nthr + tid;
+    if (idx < nvec) {
+#pragma unroll
+      for (int h = 0; h < kGv; ++h)
+        reinterpret_cast<f32x4*>(row)[idx * kGv + h] =
+            f32x4{dw[v][4 * h], dw[v][4 * h + 1], dw[v][4 * h + 2], dw[v][4 * h + 3]};
     }
   }
 }
@@ -385,23 +609,142 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
   }
 }
 
-// out[j] = sum over p < rows of in[p][j] in a fixed order: slice k of 8 sums
-// rows k, k+8, k+16, ... in turn, then the 8 slice sums are added in order.
-// A block covers 32 columns with 8 slices each.
-__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ in, int64_t rows, int n,
-                                                          float* __restrict__ out) {
+// The deferred sources' share of each layer's dL/dw,
+//     dw_l = sum over tokens t and inter-block sources s of c1_{t,l,s} H_s[t],
+// is a dense contraction -- [layers] x [(token, source) pairs] x [d] -- and
+// runs on the matrix cores as float32 MFMA 16x16x4: M = 16 layer slots, N = 16
+// columns, K = 4 (token, source) pairs per step.  Lane L takes K slot L/16: it
+// supplies the coefficient of layer L%16 (operand A) and 8 consecutive
+// elements of that pair's source row (operand B of 8 column tiles: tile q
+// holds columns col0 + 8 j + q, j = L%16).  The kN sources of a token take
+// kNp slots (1, 2, 4 or 8; the padding slots read coefficient 0), so a lane's
+// source is fixed -- or alternates between two, for kNp = 8 -- and only the
+// token advances, by a uniform stride.  A workgroup of kDwWaves waves covers
+// kDwWaves * 128 columns for one group of strided tokens (tg of ntg) and
+// writes its partial rows to dw_part[tg][l][d] for a fixed-order sum.
+// Coefficients past the group's tokens or of layer slots past B come from a
+// buffer load out of range (zero); rows are clamped to valid ones.  Every load
+// is unconditional, so a ring of kDwRing steps stays in flight.
+constexpr int kDwWaves = 4;
+constexpr int kDwCols = 128;  // columns per wave
+constexpr int kDwRing = 4;
+
+template <bool kBf16, int kN>
+__global__ void __launch_bounds__(64 * kDwWaves)
+block_dw_kernel(const void* __restrict__ src, int64_t T, int d, int64_t src_stride, int B,
+                const float* __restrict__ coef, float* __restrict__ dw_part, int ncolblocks) {
+  constexpr int kNp = kN == 1 ? 1 : kN == 2 ? 2 : kN <= 4 ? 4 : 8;   // source slots per token
+  constexpr int kTokPerStep = kNp <= 4 ? 4 / kNp : 1;
+  constexpr int kStepsPerTok = kNp == 8 ? 2 : 1;
+  static_assert(kDwRing % kStepsPerTok == 0, "a ring slot keeps its source");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cb = blockIdx.x % ncolblocks;
+  const unsigned tg = blockIdx.x / ncolblocks;
+  const unsigned ntg = gridDim.x / ncolblocks;
+  const int j = lane & 15, kq = lane >> 4;
+  const int col0 = (cb * kDwWaves + wave) * kDwCols;
+  const bool col_ok = col0 + 8 * j < d;
+  const int e = col_ok ? col0 + 8 * j : d - 8;          // clamped: such lanes write nothing
+  const unsigned ntok = (unsigned)((T - tg + ntg - 1) / ntg);   // tokens of this group (tg < T)
+  const unsigned per_tok = (unsigned)B * kN * 3;
+  const unsigned tsub = kNp <= 4 ? kq / kNp : 0;        // token within a step
+  const int slot = kNp <= 4 ? kq % kNp : kq;            // source slot (+4 on odd steps for kNp = 8)
+  int64_t hbase[kStepsPerTok];
+  unsigned cbase[kStepsPerTok];
+  bool cval[kStepsPerTok];
+#pragma unroll
+  for (int p = 0; p < kStepsPerTok; ++p) {
+    const int sp = slot + 4 * p;
+    hbase[p] = (int64_t)(sp < kN ? sp : kN - 1) * src_stride + e;
+    cbase[p] = (unsigned)((j * kN + sp) * 3 + 1);
+    cval[p] = sp < kN && j < B;
+  }
+  const unsigned steps =
+      ((ntok + kTokPerStep - 1) / kTokPerStep * kStepsPerTok + kDwRing - 1) / kDwRing * kDwRing;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(coef), 0, (int)((unsigned)T * per_tok * 4u), 0x00020000);
+
+  // operands of step i (parity p = i % kStepsPerTok, static in the ring), raw:
+  // they are widened to float32 only when used, so the loads stay in flight
+  constexpr int kW = kBf16 ? 1 : 2;   // 16-byte words of 8 elements
+  auto load_step = [&](unsigned i, int p, unsigned& a, u32x4 (&hv)[kW]) {
+    const unsigned tok = i / kStepsPerTok * kTokPerStep + tsub;
+    const bool tv = tok < ntok;
+    const unsigned t = tg + (tv ? tok : ntok - 1) * ntg;
+    const unsigned coff = (tv && cval[p]) ? (t * per_tok + cbase[p]) * 4u : 0x80000000u;
+    a = __builtin_amdgcn_raw_buffer_load_b32(crs, coff, 0, 0);
+    const int64_t off = hbase[p] + (int64_t)((uint64_t)t * (unsigned)d);
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const char*>(src) + off * (kBf16 ? 2 : 4));
+#pragma unroll
+    for (int w = 0; w < kW; ++w) hv[w] = __builtin_nontemporal_load(q + w);
+  };
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned ra[kDwRing];
+  u32x4 rh[kDwRing][kW];
+#pragma unroll
+  for (int r = 0; r < kDwRing; ++r) load_step(r, r % kStepsPerTok, ra[r], rh[r]);
+  for (unsigned i0 = 0; i0 < steps; i0 += kDwRing) {
+#pragma unroll
+    for (int r = 0; r < kDwRing; ++r) {
+      const float a = __uint_as_float(ra[r]);
+      float h[8];
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          h[2 * k] = bf16_lo(rh[r][0][k]);
+          h[2 * k + 1] = bf16_hi(rh[r][0][k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = __uint_as_float(rh[r][k >> 2][k & 3]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, h[q], acc[q], 0, 0, 0);
+      // the slot is refilled after its last use, so the loads land in the
+      // ring's own registers (no copy that would wait for them)
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(i0 + r + kDwRing, r % kStepsPerTok, ra[r], rh[r]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // lane L holds rows 4 (L/16) + v of each tile, column j
+  if (col_ok) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int l = 4 * kq + v;
+      if (l < B) {
+        float* row = dw_part + ((int64_t)tg * B + l) * d + col0 + 8 * j;
+        *reinterpret_cast<f32x4*>(row) = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
+        *reinterpret_cast<f32x4*>(row + 4) = f32x4{acc[4][v], acc[5][v], acc[6][v], acc[7][v]};
+      }
+    }
+  }
+}
+
+// out.p[l][j] (+)= sum over r < rows of in[l * layer_stride + r * row_stride + j]
+// in a fixed order: slice k of 8 sums rows k, k+8, k+16, ... in turn, then the
+// 8 slice sums are added in order.  A block covers 32 columns with 8 slices
+// each; blockIdx.y is l.
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ in, int64_t rows,
+                                                          int64_t row_stride, int64_t layer_stride, int n,
+                                                          OutRows out, bool add) {
   __shared__ float part[8][32];
   const int col = threadIdx.x & 31, slice = threadIdx.x >> 5;
   const int j = blockIdx.x * 32 + col;
+  const float* base = in + blockIdx.y * layer_stride + j;
   float acc = 0.f;
   if (j < n) {
     int64_t p = slice;
     for (; p + 24 < rows; p += 32) {       // four independent loads in flight
-      const float a0 = in[p * n + j], a1 = in[(p + 8) * n + j], a2 = in[(p + 16) * n + j],
-                  a3 = in[(p + 24) * n + j];
+      const float a0 = base[p * row_stride], a1 = base[(p + 8) * row_stride], a2 = base[(p + 16) * row_stride],
+                  a3 = base[(p + 24) * row_stride];
       acc = (((acc + a0) + a1) + a2) + a3;
     }
-    for (; p < rows; p += 8) acc += in[p * n + j];
+    for (; p < rows; p += 8) acc += base[p * row_stride];
   }
   part[slice][col] = acc;
   __syncthreads();
@@ -409,7 +752,8 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
     float tot = part[0][col];
 #pragma unroll
     for (int k = 1; k < 8; ++k) tot += part[k][col];
-    out[j] = tot;
+    float* o = out.p[blockIdx.y] + j;
+    *o = add ? *o + tot : tot;
   }
 }
 
@@ -441,7 +785,8 @@ template <bool kBf16, int kV>
 hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
   const int nvec = a.d / (kBf16 ? 8 : 4);
   if (a.T > 0) {
-    hipLaunchKernelGGL((aggregate_backward_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
+    auto kernel = a.last_only ? aggregate_backward_last_kernel<kBf16, kV> : aggregate_backward_kernel<kBf16, kV>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
                        static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4),
                        static_cast<const u32x4*>(a.last_source), a.w,
                        static_cast<const u32x4*>(a.grad_out), reinterpret_cast<f32x4*>(a.grad_sources),
@@ -450,9 +795,10 @@ hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int blocks = (a.d + 31) / 32;
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.workspace,
-                     a.T > 0 ? a.grid : (int64_t)0, a.d, a.grad_w);
+  OutRows out{};
+  out.p[0] = a.grad_w;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((a.d + 31) / 32)), dim3(256), 0, stream, a.workspace,
+                     a.T > 0 ? a.grid : (int64_t)0, (int64_t)a.d, (int64_t)0, a.d, out, false);
   return hipGetLastError();
 }
 
@@ -479,14 +825,37 @@ hipError_t launch_block_v(const BlockBackwardArgs& a, hipStream_t stream) {
 
 template <bool kBf16>
 hipError_t launch_block(const BlockBackwardArgs& a, hipStream_t stream) {
+  hipError_t e;
   switch (a.vecs_per_lane) {
-    case 1: return launch_block_v<kBf16, 1>(a, stream);
-    case 2: return launch_block_v<kBf16, 2>(a, stream);
-    case 3: return launch_block_v<kBf16, 3>(a, stream);
-    case 4: return launch_block_v<kBf16, 4>(a, stream);
+    case 1: e = launch_block_v<kBf16, 1>(a, stream); break;
+    case 2: e = launch_block_v<kBf16, 2>(a, stream); break;
+    case 3: e = launch_block_v<kBf16, 3>(a, stream); break;
+    case 4: e = launch_block_v<kBf16, 4>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  // the deferred sources' share of dL/dw, then its fixed-order sum into each layer's row
+  const dim3 grid((unsigned)(a.dw_groups * a.dw_colblocks)), block(64 * kDwWaves);
+  switch (a.n) {
+#define ATTNRES_DW_CASE(N)                                                                                      \
+  case N:                                                                                                       \
+    hipLaunchKernelGGL((block_dw_kernel<kBf16, N>), grid, block, 0, stream, a.sources, a.T, a.d, a.src_stride, \
+                       a.B, a.coef, a.workspace, a.dw_colblocks);                                              \
+    break;
+    ATTNRES_DW_CASE(1) ATTNRES_DW_CASE(2) ATTNRES_DW_CASE(3) ATTNRES_DW_CASE(4)
+    ATTNRES_DW_CASE(5) ATTNRES_DW_CASE(6) ATTNRES_DW_CASE(7) ATTNRES_DW_CASE(8)
+#undef ATTNRES_DW_CASE
+    default: return hipErrorInvalidValue;
+  }
+  static_assert(kMaxInterSources == 8, "one instance per source count");
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((a.d + 31) / 32), (unsigned)a.B), dim3(256), 0, stream,
+                     a.workspace, a.dw_groups, (int64_t)a.B * a.d, (int64_t)a.d, a.d, a.grad_w, true);
+  return hipGetLastError();
 }
+
+static_assert(kDwWaves * kDwCols == kBlockDwCols, "columns per dL/dw workgroup");
 
 }  // namespace
 

@@ -67,7 +67,9 @@ int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus,
 }
 
 // Compute units of the current device, queried once per device.
-int device_cus(int* out) {
+// A device attribute of the current device, queried once per device.
+template <int kSlot>
+int device_attr(hipDeviceAttribute_t attr, int* out) {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ATTNRES_ELAUNCH;
@@ -78,13 +80,14 @@ int device_cus(int* out) {
       return ATTNRES_OK;
     }
   }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return ATTNRES_ELAUNCH;
-  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  *out = cus;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) return ATTNRES_ELAUNCH;
+  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  *out = v;
   return ATTNRES_OK;
 }
+
+int device_cus(int* out) { return device_attr<0>(hipDeviceAttributeMultiprocessorCount, out); }
 
 int check_store(const attnres_store_t* st) {
   if (st == nullptr) return ATTNRES_EINVAL;
@@ -181,10 +184,15 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
                                                                                       : ATTNRES_ELAUNCH;
 }
 
-// Workgroups of the backward pass: as many as fit on the device at once (one
-// per CU for d above 4096, two below), each accumulating dL/dw over its tokens.
-int64_t backward_grid(int64_t T, int cus, int v) {
-  const int64_t resident = (int64_t)cus * (v == 1 ? 2 : 1);
+// Workgroups of the backward pass: as many as fit on the device at once, each
+// accumulating dL/dw over its tokens.  The general kernel holds every source
+// row in registers: two workgroups per CU for d up to 4096, one above.  The
+// kernel for the case where only the last row is written streams the rows and
+// fits two per CU up to d = 8192.
+int backward_per_cu(int v, bool last_only) { return (v == 1 || (last_only && v == 2)) ? 2 : 1; }
+
+int64_t backward_grid(int64_t T, int cus, int per_cu) {
+  const int64_t resident = (int64_t)cus * per_cu;
   return T < resident ? T : resident;
 }
 
@@ -202,7 +210,7 @@ ATTNRES_API int attnres_aggregate_backward_workspace(int64_t T, int32_t d, int32
   attnres_launch_t cfg;
   rc = pick_config(1, T, d, dtype, cus, &cfg);
   if (rc != ATTNRES_OK) return rc;
-  *bytes = backward_grid(T, cus, cfg.vecs_per_lane) * (int64_t)d * 4;
+  *bytes = backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, true)) * (int64_t)d * 4;
   return ATTNRES_OK;
 }
 
@@ -269,7 +277,9 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   attnres_launch_t cfg;
   rc = pick_config(S, T, d, dtype, cus, &cfg);
   if (rc != ATTNRES_OK) return rc;
-  const int64_t grid = backward_grid(T, cus, cfg.vecs_per_lane);
+  const unsigned all = S >= 32 ? 0xFFFFFFFFu : ((1u << S) - 1u);
+  const bool last_only = ((~defer_mask & all) & ~(1u << (S - 1))) == 0;
+  const int64_t grid = backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, last_only));
   if (T > 0 && workspace_bytes < grid * (int64_t)d * 4) return ATTNRES_EINVAL;
   attnres::BackwardArgs a;
   a.sources = sources;
@@ -291,6 +301,7 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   a.workspace = static_cast<float*>(workspace);
   a.eps = eps;
   a.bf16 = dtype == ATTNRES_BF16;
+  a.last_only = last_only;
   a.threads = cfg.threads;
   a.vecs_per_lane = cfg.vecs_per_lane;
   a.grid = grid;
@@ -299,10 +310,35 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
                                                                                                : ATTNRES_ELAUNCH;
 }
 
+// Token groups of the block pass's dL/dw contraction: about four workgroups per
+// CU over the column blocks, and never more groups than tokens.
+int64_t block_dw_groups(int64_t T, int d, int cus) {
+  const int64_t colblocks = (d + attnres::kBlockDwCols - 1) / attnres::kBlockDwCols;
+  const int64_t want = ((int64_t)cus * 4 + colblocks - 1) / colblocks;
+  return T < want ? (T > 0 ? T : 1) : want;
+}
+
+ATTNRES_API int attnres_block_backward_workspace(int64_t T, int32_t d, int32_t B, int32_t dtype, int64_t* bytes) {
+  if (bytes == nullptr || B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (d % 8 != 0) return ATTNRES_EUNSUPPORTED;
+  if (T == 0) {
+    *bytes = 0;
+    return ATTNRES_OK;
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  *bytes = block_dw_groups(T, d, cus) * B * (int64_t)d * 4;
+  return ATTNRES_OK;
+}
+
 ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
                                        int32_t B, const void* const* grad_outs, const float* const* queries,
                                        const float* coef, float* grad_sources, int64_t grad_stride,
-                                       uint32_t accumulate_mask, void* grad_last, int32_t dtype, void* stream) {
+                                       uint32_t accumulate_mask, void* grad_last, float* const* grad_ws,
+                                       void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream) {
   if (n < 1 || n > attnres::kMaxInterSources || B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
   int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
@@ -313,35 +349,52 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
     return ATTNRES_EINVAL;
   if (n > 1 && (src_stride < row || grad_stride < row)) return ATTNRES_EINVAL;
   if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
+  // the dL/dw contraction takes 8 columns per lane and addresses the
+  // coefficients with 32-bit byte offsets
+  if (d % 8 != 0 || T * B * n * 12 >= (INT64_C(1) << 31)) return ATTNRES_EUNSUPPORTED;
   if (T == 0) return ATTNRES_OK;
-  if (sources == nullptr || grad_outs == nullptr || queries == nullptr || coef == nullptr || grad_sources == nullptr)
+  if (sources == nullptr || grad_outs == nullptr || queries == nullptr || coef == nullptr ||
+      grad_sources == nullptr || grad_ws == nullptr || workspace == nullptr)
     return ATTNRES_EINVAL;
   const int es = elem_bytes(dtype);
-  const Range r_gs = range(grad_sources, ((int64_t)(n - 1) * grad_stride + row) * 4);
-  const Range r_gl = grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0};
-  if (!aligned16(sources) || !aligned16(grad_sources) || (grad_last != nullptr && !aligned16(grad_last)) ||
-      (reinterpret_cast<uintptr_t>(coef) & 3u) != 0)
+  if (!aligned16(sources) || !aligned16(grad_sources) || !aligned16(workspace) ||
+      (grad_last != nullptr && !aligned16(grad_last)) || (reinterpret_cast<uintptr_t>(coef) & 3u) != 0)
     return ATTNRES_EUNSUPPORTED;
   std::vector<Range> ins = {range(sources, ((int64_t)(n - 1) * src_stride + row) * es),
                             range(coef, (int64_t)T * B * n * 3 * 4)};
+  std::vector<Range> outs = {range(grad_sources, ((int64_t)(n - 1) * grad_stride + row) * 4),
+                             grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0},
+                             range(workspace, workspace_bytes)};
   attnres::BlockBackwardArgs a;
+  for (int l = 0; l < attnres::kMaxBlockLayers; ++l) {
+    a.rows.g[l] = nullptr;
+    a.rows.w[l] = nullptr;
+    a.grad_w.p[l] = nullptr;
+  }
   for (int l = 0; l < B; ++l) {
-    if (grad_outs[l] == nullptr || queries[l] == nullptr) return ATTNRES_EINVAL;
-    if (!aligned16(grad_outs[l]) || !aligned16(queries[l])) return ATTNRES_EUNSUPPORTED;
+    if (grad_outs[l] == nullptr || queries[l] == nullptr || grad_ws[l] == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(grad_outs[l]) || !aligned16(queries[l]) || !aligned16(grad_ws[l])) return ATTNRES_EUNSUPPORTED;
     ins.push_back(range(grad_outs[l], row * es));
     ins.push_back(range(queries[l], (int64_t)d * 4));
+    outs.push_back(range(grad_ws[l], (int64_t)d * 4));
     a.rows.g[l] = grad_outs[l];
     a.rows.w[l] = queries[l];
+    a.grad_w.p[l] = grad_ws[l];
   }
-  for (const Range& r : ins)
-    if (overlap(r_gs, r) || overlap(r_gl, r)) return ATTNRES_EALIAS;
-  if (overlap(r_gs, r_gl)) return ATTNRES_EALIAS;
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTNRES_EALIAS;
+    for (size_t k = i + 1; k < outs.size(); ++k)
+      if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
+  }
   int cus = 0;
   rc = device_cus(&cus);
   if (rc != ATTNRES_OK) return rc;
   attnres_launch_t cfg;
   rc = pick_config(n, T, d, dtype, cus, &cfg);
   if (rc != ATTNRES_OK) return rc;
+  const int64_t groups = block_dw_groups(T, d, cus);
+  if (workspace_bytes < groups * B * (int64_t)d * 4) return ATTNRES_EINVAL;
   a.sources = sources;
   a.n = n;
   a.T = T;
@@ -353,10 +406,13 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
   a.grad_stride = grad_stride;
   a.acc_mask = accumulate_mask;
   a.grad_last = grad_last;
+  a.workspace = static_cast<float*>(workspace);
   a.bf16 = dtype == ATTNRES_BF16;
   a.threads = cfg.threads;
   a.vecs_per_lane = cfg.vecs_per_lane;
   a.grid = cfg.grid;
+  a.dw_colblocks = (d + attnres::kBlockDwCols - 1) / attnres::kBlockDwCols;
+  a.dw_groups = groups;
   (void)hipGetLastError();
   return attnres::launch_block_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                            : ATTNRES_ELAUNCH;

@@ -126,6 +126,7 @@ struct BackwardArgs {
   float* workspace;       // grid rows of [d]
   float eps;
   bool bf16;
+  bool last_only;         // every row but the last deferred: the streaming kernel
   int threads, vecs_per_lane;
   int64_t grid;
 };
@@ -138,6 +139,15 @@ struct BlockRows {
   const void* g[kMaxBlockLayers];    // dL/dr of the block's layers, [T][d] source dtype
   const float* w[kMaxBlockLayers];   // their queries, [d] float32
 };
+// Output rows of a per-layer reduction (one [d] float32 row per layer).
+struct OutRows {
+  float* p[kMaxBlockLayers];
+};
+
+// The deferred sources' dL/dw share is an MFMA contraction over column blocks of
+// kBlockDwCols and `dw_groups` strided token groups.
+constexpr int kBlockDwCols = 512;
+
 struct BlockBackwardArgs {
   const void* sources;    // n inter-block rows at src_stride elements
   int n;
@@ -151,12 +161,17 @@ struct BlockBackwardArgs {
   int64_t grad_stride;
   unsigned acc_mask;
   void* grad_last;        // [T][d] source dtype: the new row n-1, or nullptr
+  OutRows grad_w;         // B rows [d] float32, each added to
+  float* workspace;       // [dw_groups][B][d] float32
   bool bf16;
   int threads, vecs_per_lane;
-  int64_t grid;
+  int64_t grid;           // workgroups of the gradient-row pass
+  int dw_colblocks;       // ceil(d / kBlockDwCols)
+  int64_t dw_groups;      // token groups of the dL/dw pass
 };
 
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream);
+
 
 // Running partial sums of up to kMaxBlockLayers rows (rows.g holds the inputs).
 struct PartialSumsArgs {

@@ -216,7 +216,10 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     (h_0, b_1 .. b_{n-1}, shared by all its layers) are not updated per layer:
     each layer's backward writes three coefficients per token and source, and
     one ``attnres_block_backward`` per block applies them -- one
-    read-modify-write of those rows per block instead of one per layer.
+    read-modify-write of those rows per block instead of one per layer -- and
+    adds those sources' share of each layer's dL/dw.  The final aggregation's
+    sources h_0 .. b_{N-1} are the last block's inter-block sources, so it joins
+    that block's pass as one more layer.
     Returns ``(grad_store, grad_w, grad_w_final)``.
     """
     from .binding import aggregate_backward, block_backward, partial_sums
@@ -236,9 +239,10 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     slots = store.slots
     dF = torch.empty((T, d), dtype=dt, device=dev)
     partials = torch.empty((block_size, T, d), dtype=dt, device=dev)  # partials[i-2]: before position i
-    coef_all = (torch.empty(T * block_size * nblocks * 3, dtype=torch.float32, device=dev)
+    coef_all = (torch.empty(T * (block_size + 1) * nblocks * 3, dtype=torch.float32, device=dev)
                 if defer else None)
     holds = [False] * (1 + nblocks)   # which gradient rows already hold a gradient
+    final_in_block = defer and final_query is not None
 
     def acc_mask(rows):
         return sum(1 << k for k, r in enumerate(rows) if holds[r])
@@ -246,11 +250,27 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     def dr(l):
         return grad_r(l, dF) if callable(grad_r) else grad_r[l - 1]
 
+    def block_layers(n):
+        return min(n * block_size, L) - (n - 1) * block_size + (1 if final_in_block and n == nblocks else 0)
+
+    def block_coef(n):
+        Bc = block_layers(n)
+        return coef_all[:T * Bc * n * 3].view(T, Bc, n, 3)
+
     if final_query is not None:
         S = 1 + nblocks
-        aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
-                           grad_w=grad_w_final, grad_last=dF, eps=eps)
-        holds[:S] = [True] * S
+        if final_in_block:
+            # h_0 .. b_{N-1} deferred to the last block's pass (its last layer
+            # slot); only b_N's gradient row is written here
+            N, Bc = nblocks, block_layers(nblocks)
+            aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=0,
+                               defer=(1 << N) - 1, coef=block_coef(N).view(-1)[3 * N * (Bc - 1):],
+                               coef_stride=3 * N * Bc, grad_w=grad_w_final, grad_last=dF, eps=eps)
+            holds[N] = True
+        else:
+            aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
+                               grad_w=grad_w_final, grad_last=dF, eps=eps)
+            holds[:S] = [True] * S
     else:
         dF.zero_()
     if on_grad is not None:
@@ -262,13 +282,14 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         # the block's partial sums, formed exactly as the forward formed them
         if B >= 2:
             partial_sums([layer_outputs[j - 1] for j in range(first, last)], partials)
-        coef = coef_all[:T * B * n * 3].view(T, B, n, 3) if defer else None
+        coef = block_coef(n) if defer else None
+        Bc = coef.shape[1] if defer else B
         block_g = [None] * B
         for l in range(last, first - 1, -1):
             i = l - first + 1
             g = dr(l)
             block_g[i - 1] = g
-            cf = dict(defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * (i - 1):], coef_stride=3 * n * B) if defer else {}
+            cf = dict(defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * (i - 1):], coef_stride=3 * n * Bc) if defer else {}
             if i >= 2:
                 rows = list(range(n + 1))
                 aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n + 1], last_source=partials[i - 2],
@@ -284,8 +305,12 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
             if on_grad is not None and (i >= 2 or not defer):
                 on_grad(l - 1, dF)
         if defer:
-            block_backward(slots[:n], block_g, [queries[j - 1] for j in range(first, last + 1)], coef,
-                           grad_store[:n], accumulate=acc_mask(range(n)), grad_last=dF)
+            qs = [queries[j - 1] for j in range(first, last + 1)]
+            dws = [grad_w[j - 1] for j in range(first, last + 1)]
+            if Bc > B:   # the final aggregation, in the last slot
+                block_g, qs, dws = block_g + [grad_final], qs + [final_query], dws + [grad_w_final]
+            block_backward(slots[:n], block_g, qs, coef, grad_store[:n], dws, accumulate=acc_mask(range(n)),
+                           grad_last=dF)
             holds[:n] = [True] * n
             if on_grad is not None:
                 on_grad(first - 1, dF)

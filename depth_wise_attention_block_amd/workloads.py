@@ -250,15 +250,21 @@ class ScheduleBackward:
         sources and dL/dr and hands out a gradient; with ``defer`` a layer
         updates only its partial's gradient row and writes 3 coefficients per
         token and inter-block source, and one pass per block reads the block's
-        inter-block sources, its dL/dr rows and coefficients and
-        read-modify-writes each inter-block gradient row once; without, every
-        layer read-modify-writes all its sources' gradient rows."""
+        inter-block sources, its dL/dr rows and coefficients and writes each
+        inter-block gradient row once (read-modify-write, except in the last
+        block, whose rows the deferred output layer leaves untouched); the
+        output layer is one more layer of the last block's pass.  Without
+        ``defer`` every layer read-modify-writes all its sources' gradient rows.
+        Not counted: the second read of a block's inter-block sources by the
+        dL/dw contraction (an implementation choice, n rows per block)."""
         T, d, L, bs = self.T, self.d, self.layers, self.block_size
         row2, row4 = 2 * T * d, 4 * T * d
         nblocks = (L + bs - 1) // bs
-        # output layer: sources and g in, gradient rows written (first touch), dF out
+        # output layer: sources and g in, dF out; gradient rows written first touch
+        # (only b_N's when the other sources are deferred to the last block's pass)
         S = 1 + nblocks
-        total = S * row2 + row2 + S * row4 + row2 + 8 * d
+        total = S * row2 + row2 + row2 + 8 * d
+        total += (row4 + 12 * nblocks * T) if defer else S * row4
         for n in range(1, nblocks + 1):
             B = min(n * bs, L) - (n - 1) * bs
             if B >= 2:                                   # partial sums recomputed in one pass
@@ -272,6 +278,8 @@ class ScheduleBackward:
                         total += 2 * row4 + row2             # the partial's gradient row, dF out
                 else:
                     total += 2 * S * row4 + row2             # every gradient row, dF out
-            if defer:                                        # one pass per block
-                total += n * row2 + B * row2 + 12 * n * B * T + 2 * n * row4 + row2 + 4 * d * B
+            if defer:                                        # one pass per block (+ the output layer in the last)
+                Bc = B + (1 if n == nblocks else 0)
+                rows = n * row4 if n == nblocks else 2 * n * row4
+                total += n * row2 + Bc * row2 + 12 * n * Bc * T + rows + row2 + 12 * d * Bc
         return total

@@ -310,7 +310,10 @@ ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t coun
  *                   new value of grad row S-1 -- in a Block
  *                   AttnRes backward that is the finished gradient of the
  *                   previous layer's output.
- *   grad_w          device, [d] float32, overwritten with dL/dw (zero for T = 0).
+ *   grad_w          device, [d] float32, overwritten with dL/dw summed over the
+ *                   sources not in defer_mask (zero for T = 0); a deferred
+ *                   source's share, sum over tokens of (delta_s/rho_s) H_s, is
+ *                   added by attnres_block_backward with its gradient row.
  *   workspace       device, at least attnres_aggregate_backward_workspace()
  *                   bytes, 16-byte aligned (NULL allowed for T = 0): one
  *                   float32 row of dL/dw per workgroup, summed in a fixed order,
@@ -333,21 +336,36 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
  * defer them (attnres_aggregate_backward, defer_mask), this adds all their
  * contributions in one pass, per token and source:
  *   G_s += sum_l (a_{l,s} g_l + c1_{l,s} w_l) - (sum_l c3_{l,s}) H_s
+ * and to each layer's dL/dw the deferred sources' share:
+ *   dw_l += sum over tokens and s of c1_{l,s} H_s
  *
  *   sources       device, n rows [T][d] (dtype) at src_stride elements, n <= 8.
- *   B             layers, 1..16; grad_outs[l] (device [T][d] dtype, dL/dr_l) and
- *                 queries[l] (device [d] float32) are HOST arrays of B pointers.
+ *   B             layers, 1..16; grad_outs[l] (device [T][d] dtype, dL/dr_l),
+ *                 queries[l] (device [d] float32) and grad_ws[l] (device [d]
+ *                 float32, added to) are HOST arrays of B pointers.  A "layer"
+ *                 may be any aggregation over these sources (e.g. the final
+ *                 one of the network).
  *   coef          device float32 [T][B][n][3]: layer l's coefficients, as its
  *                 backward wrote them with coef = coef + 3 n l, coef_stride 3 n B.
  *   grad_sources  device, n rows [T][d] float32 at grad_stride floats; rows whose
  *                 bit is set in accumulate_mask are added into, others written.
  *   grad_last     device [T][d] dtype, or NULL: the new gradient row n-1 (the
  *                 finished gradient of the previous block's last layer output).
+ *   workspace     device, at least attnres_block_backward_workspace() bytes,
+ *                 16-byte aligned: partial dL/dw rows, summed in a fixed order
+ *                 (bitwise reproducible on one device).
+ * Outputs may not overlap the inputs or each other (ATTNRES_EALIAS).  Needs d a
+ * multiple of 8 and T*B*n*12 < 2^31 (else ATTNRES_EUNSUPPORTED).
  */
 ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
                                        int32_t B, const void* const* grad_outs, const float* const* queries,
                                        const float* coef, float* grad_sources, int64_t grad_stride,
-                                       uint32_t accumulate_mask, void* grad_last, int32_t dtype, void* stream);
+                                       uint32_t accumulate_mask, void* grad_last, float* const* grad_ws,
+                                       void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
+
+/* Workspace bytes attnres_block_backward needs for T tokens of width d and B
+ * layers on the current device (host only apart from a device-attribute query). */
+ATTNRES_API int attnres_block_backward_workspace(int64_t T, int32_t d, int32_t B, int32_t dtype, int64_t* bytes);
 
 /* Workspace bytes attnres_aggregate_backward needs for T tokens of width d on
  * the current device (host only apart from a device-attribute query). */

@@ -267,14 +267,17 @@ def run_full_schedule(h0, layer_outputs, queries, final_query=None, eps: float =
 # rule through the forward's steps, in the forward's order.
 # ----------------------------------------------------------------------------
 
-def depth_attention_backward(H, w, g, eps: float = EPS):
+def depth_attention_backward(H, w, g, eps: float = EPS, per_source: bool = False):
     """Gradients of ``L = sum_t g[t] . r[t]`` for ``r, a = depth_attention(H, w)``.
 
     Args:
       H: ``[S, T, d]`` sources; w: ``[d]`` query; g: ``[T, d]`` upstream
          gradient dL/dr.  Any real dtype, upcast to float64.
+      per_source: also return each source's share of dL/dw -- the gradient
+         reaching w through that source's logit alone, ``sum_t dz_s k_s``.
     Returns:
-      ``(dH, dw)``: ``[S, T, d]`` and ``[d]`` (summed over tokens), float64.
+      ``(dH, dw)``: ``[S, T, d]`` and ``[d]`` (summed over tokens), float64;
+      with ``per_source``, ``(dH, dw, dw_src)`` with ``dw_src`` ``[S, d]``.
     """
     H = np.asarray(H, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
@@ -296,13 +299,15 @@ def depth_attention_backward(H, w, g, eps: float = EPS):
     dz = a * (da - np.sum(a * da, axis=1, keepdims=True))          # [T, S]
     # logits = keys . w
     dw = np.zeros(d)
+    dw_src = np.zeros((S, d))
     dkeys = np.zeros_like(H)
     for s in range(S):
-        dw += np.sum(dz[:, s:s + 1] * keys[s], axis=0)
+        dw_src[s] = np.sum(dz[:, s:s + 1] * keys[s], axis=0)
+        dw += dw_src[s]
         dkeys[s] = dz[:, s:s + 1] * w
     # keys = H / sqrt(mean(H^2) + eps): dH = (dkeys - keys * mean(dkeys * keys)) / rms
     dH += (dkeys - keys * np.mean(dkeys * keys, axis=-1, keepdims=True)) / rms
-    return dH, dw
+    return (dH, dw, dw_src) if per_source else (dH, dw)
 
 
 def layer_sources(h0, layer_outputs, block_size: int, dtype: str):

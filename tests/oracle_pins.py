@@ -298,3 +298,28 @@ def pin_backward_invariants(bwd, seed=14):
 
 BACKWARD_PINS = (pin_backward_library, pin_backward_finite_difference, pin_backward_closed_forms,
                  pin_backward_invariants)
+
+
+def library_backward_per_source(H, w, g, eps=EPS):
+    """Each source's share of dL/dw by autograd: one copy of the query per source
+    logit, keys from torch ``rms_norm``, softmax and weighted sum from torch."""
+    Ht = torch.tensor(np.asarray(H, np.float64))
+    S, T, d = Ht.shape
+    Wt = torch.tensor(np.repeat(np.asarray(w, np.float64)[None], S, axis=0), requires_grad=True)   # [S, d]
+    keys = F.rms_norm(Ht, (d,), eps=eps)                                    # [S, T, d]
+    z = torch.stack([keys[s] @ Wt[s] for s in range(S)], dim=1)             # [T, S]
+    a = torch.softmax(z, dim=1)
+    r = sum(a[:, s:s + 1] * Ht[s] for s in range(S))
+    (r * torch.as_tensor(np.asarray(g, np.float64))).sum().backward()
+    return Wt.grad.numpy()
+
+
+def pin_backward_per_source(bwd_src, seed=15):
+    """``bwd_src(H, w, g, eps) -> (dw, dw_src)``: the per-source shares equal
+    autograd through per-source query copies and sum to dL/dw."""
+    H = synth.sources(5, 12, 48, scale=(0.01, 20.0), seed=seed, dtype="f32").double().numpy()
+    w = synth.query(48, seed=seed).double().numpy()
+    g = np.random.default_rng(seed).normal(size=(12, 48))
+    dw, dw_src = bwd_src(H, w, g, EPS)
+    _close(dw_src, library_backward_per_source(H, w, g, EPS), rtol=1e-11, what="per-source dw vs autograd")
+    _close(dw_src.sum(axis=0), dw, rtol=1e-12, what="per-source shares sum to dw")

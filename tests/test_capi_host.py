@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -283,17 +283,23 @@ def test_backward_host_checks(lib):
     assert bwd(defer=0b011, cf=GS + 4, cfs=9) == B.EALIAS and bwd(defer=0b011, cf=SRC, cfs=9) == B.EALIAS
 
     Arr = ctypes.c_void_p * 2
-    G2, W2 = Arr(OUT, OUT + 4096), Arr(W, W + 4096)
+    G2, W2, DW2 = Arr(OUT, OUT + 4096), Arr(W, W + 4096), Arr(GW, GW + 4096)
 
-    def blk(n=3, T=4, d=8, src=SRC, Bl=2, gs_=G2, ws_=W2, cf=CF, grads=GS, gl=None, dtype=B.BF16, gstride=0):
-        return B.lib().attnres_block_backward(src, n, T, d, 0, Bl, gs_, ws_, cf, grads, gstride, 0, gl, dtype, None)
+    def blk(n=3, T=4, d=8, src=SRC, Bl=2, gs_=G2, ws_=W2, cf=CF, grads=GS, gl=None, dtype=B.BF16, gstride=0,
+            dws=DW2, wk=WS, wkb=1 << 20):
+        return B.lib().attnres_block_backward(src, n, T, d, 0, Bl, gs_, ws_, cf, grads, gstride, 0, gl, dws, wk,
+                                              wkb, dtype, None)
 
     assert blk(n=0) == B.EINVAL and blk(n=9) == B.EINVAL and blk(Bl=0) == B.EINVAL and blk(Bl=17) == B.EINVAL
     assert blk(T=0) == B.OK and blk(d=12) == B.EUNSUPPORTED and blk(gstride=8) == B.EINVAL
     assert blk(src=None) == B.EINVAL and blk(cf=None) == B.EINVAL and blk(grads=None) == B.EINVAL
+    assert blk(dws=None) == B.EINVAL and blk(wk=None) == B.EINVAL and blk(dws=Arr(GW, 0)) == B.EINVAL
     assert blk(gs_=Arr(OUT, 0)) == B.EINVAL and blk(ws_=Arr(W, W + 8)) == B.EUNSUPPORTED
     assert blk(grads=GS + 8) == B.EUNSUPPORTED and blk(cf=CF + 2) == B.EUNSUPPORTED
+    assert blk(dws=Arr(GW, GW + 8)) == B.EUNSUPPORTED and blk(wk=WS + 8) == B.EUNSUPPORTED
     assert blk(grads=SRC) == B.EALIAS and blk(gl=OUT + 4096) == B.EALIAS and blk(grads=CF) == B.EALIAS
+    assert blk(dws=Arr(GW, W)) == B.EALIAS and blk(dws=Arr(GW, GW)) == B.EALIAS and blk(wk=GS) == B.EALIAS
+    assert blk(dws=Arr(GW, WS + 64)) == B.EALIAS
 
     add = B.lib().attnres_add_rows
     assert add(None, None, W, 4, 8, B.BF16, None) == B.EINVAL and add(None, OUT, None, 4, 8, B.BF16, None) == B.EINVAL
@@ -302,6 +308,10 @@ def test_backward_host_checks(lib):
     out = ctypes.c_int64()
     assert B.lib().attnres_aggregate_backward_workspace(0, 8, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
     assert B.lib().attnres_aggregate_backward_workspace(4, 8, B.BF16, None) == B.EINVAL
+    wsb = B.lib().attnres_block_backward_workspace
+    assert wsb(0, 8, 3, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
+    assert wsb(4, 8, 0, B.BF16, ctypes.byref(out)) == B.EINVAL and wsb(4, 8, 17, B.BF16, ctypes.byref(out)) == B.EINVAL
+    assert wsb(4, 12, 3, B.BF16, ctypes.byref(out)) == B.EUNSUPPORTED and wsb(4, 8, 3, B.BF16, None) == B.EINVAL
 
 
 def test_partial_sums_host_checks(lib):

@@ -274,11 +274,48 @@ def test_schedule_backward_matches_oracle(final, defer):
         assert e <= 1e-3 * np.max(np.abs(ref["dw_final"])), f"dw final: {e:.3e}"
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("S,defer,T,d", [(9, 0xFF, 37, 7168), (4, 0b0101, 45, 1032), (3, 0b111, 20, 264),
+                                         (2, 0b01, 300, 7176)])
+def test_deferred_backward_matches_oracle(dtype, S, defer, T, d):
+    """Deferred sources: their rows stay untouched and their coefficients,
+    recombined as a_s g + c1_s w - c3_s H_s, give the oracle's dH_s; the other
+    rows match the oracle; dL/dw is the oracle's share of the other sources."""
+    note(f"deferred backward dtype={dtype} S={S} defer={defer:#x} T={T} d={d}")
+    H, w, g = inputs(S, T, d, dtype, seed=S * 7 + T)
+    dev = H.device
+    prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(5), device=dev)
+    grads = prefill.clone()
+    coef = torch.full((T, 3 * S), float("nan"), dtype=torch.float32, device=dev)
+    dw = B.aggregate_backward(H, w, g, grads, defer=defer, coef=coef, coef_stride=3 * S)
+    torch.cuda.synchronize()
+    Hh, wh, gh = host(H), host(w), host(g)
+    dH_ref, _, dw_src = orc.depth_attention_backward(Hh, wh, gh, per_source=True)
+    bH, bw = bounds(Hh, wh, gh)
+    cf = host(coef).astype(np.float64).reshape(T, S, 3)
+    got = host(grads)
+    for s in range(S):
+        if (defer >> s) & 1:
+            assert torch.equal(grads[s], prefill[s]), f"deferred row {s} was written"
+            rec = cf[:, s, 0:1] * gh + cf[:, s, 1:2] * wh[None] - cf[:, s, 2:3] * Hh[s]
+        else:
+            assert np.all(np.isnan(cf[:, s])), f"coefficients written for source {s}, which is not deferred"
+            rec = got[s]
+        err = np.abs(rec - dH_ref[s])
+        lim = C_BWD * bH[s] + 2.0 ** -23 * np.abs(dH_ref[s])
+        assert np.all(err <= lim), f"source {s}: ratio {np.max(err / lim):.3g}"
+    share = sum(dw_src[s] for s in range(S) if not (defer >> s) & 1) if defer != (1 << S) - 1 else np.zeros(d)
+    errw = np.abs(host(dw).astype(np.float64) - share)
+    limw = C_BWD * bw + 2.0 ** -23 * np.abs(share)
+    assert np.all(errw <= limw), f"dw share: ratio {np.max(errw / limw):.3g}"
+
+
 def test_block_backward_equals_per_layer_updates():
     """One block of B = 6 layers over n = 5 inter-block sources (+ a partial):
     deferring the inter-block gradients to attnres_block_backward gives the
-    per-layer result up to float32 summation order; the partial's gradient row
-    and dL/dw are identical."""
+    per-layer result up to float32 summation order -- the gradient rows and,
+    once the block pass adds the deferred sources' share, dL/dw; the partial's
+    gradient row is identical."""
     dev = device()
     n, Bl, T, d = 5, 6, 70, 1032
     H, _, _ = inputs(n, T, d, torch.bfloat16, seed=31)
@@ -300,15 +337,57 @@ def test_block_backward_equals_per_layer_updates():
                                             coef_stride=3 * n * Bl, grad_last=last_got))
     torch.cuda.synchronize()
     assert torch.equal(last_ref, last_got) and torch.equal(ref[n], got[n]), "partial row"
-    assert all(torch.equal(a, b) for a, b in zip(dws_ref, dws_got)), "dL/dw"
     assert torch.equal(got[:n], prefill[:n]), "deferred rows must be untouched before the block pass"
     emit = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
-    B.block_backward(H, Gs, Ws, coef, got[:n], accumulate=(1 << n) - 1, grad_last=emit)
+    B.block_backward(H, Gs, Ws, coef, got[:n], dws_got, accumulate=(1 << n) - 1, grad_last=emit)
     torch.cuda.synchronize()
     diff = (got[:n] - ref[:n]).abs().max().item()
     scale = ref[:n].abs().max().item()
     assert diff <= 1e-5 * scale, f"deferred vs per-layer: {diff:.3e} of {scale:.3e}"
     assert torch.equal(emit, got[n - 1].to(torch.bfloat16))
+    for l in range(Bl):
+        e = (dws_got[l] - dws_ref[l]).abs().max().item()
+        assert e <= 1e-4 * dws_ref[l].abs().max().item(), f"dL/dw layer {l}: {e:.3e}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("n,Bl,T,d", [(1, 1, 9, 8), (8, 16, 33, 2056), (3, 13, 300, 7168), (7, 2, 5, 1024)])
+def test_block_backward_matches_oracle(dtype, n, Bl, T, d):
+    """attnres_block_backward on coefficients the oracle fixes: for each layer
+    the per-layer coefficients are those of an aggregation over the n sources
+    (written by a deferred attnres_aggregate_backward, checked above), and the
+    block pass must leave each G_s equal to prefill + sum_l dH_{l,s} of the
+    oracle and add each layer's full dL/dw -- shapes with a ragged d slice, the
+    most layers and sources, and a single element group."""
+    note(f"block backward dtype={dtype} n={n} B={Bl} T={T} d={d}")
+    H, _, _ = inputs(n, T, d, dtype, seed=n * 31 + Bl)
+    dev = H.device
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    Ws = [synth.query(d, seed=n, device=dev, tag=l) for l in range(Bl)]
+    Gs = [synth.layer_output(T, d, std=1.0, seed=n, tag=60 + l, device=dev, dtype=name) for l in range(Bl)]
+    prefill = torch.randn((n, T, d), generator=torch.Generator(device=dev).manual_seed(6), device=dev)
+    grads = prefill.clone()
+    coef = torch.empty((T, Bl, n, 3), dtype=torch.float32, device=dev)
+    scratch = torch.zeros((n, T, d), dtype=torch.float32, device=dev)
+    dws = []
+    for l in range(Bl):
+        dws.append(B.aggregate_backward(H, Ws[l], Gs[l], scratch, defer=(1 << n) - 1,
+                                        coef=coef.view(-1)[3 * n * l:], coef_stride=3 * n * Bl))
+    B.block_backward(H, Gs, Ws, coef, grads, dws, accumulate=(1 << n) - 1)
+    torch.cuda.synchronize()
+    Hh = host(H)
+    ref = host(prefill).astype(np.float64)
+    bH_tot = np.zeros_like(ref)
+    for l in range(Bl):
+        dH, dw_ref = orc.depth_attention_backward(Hh, host(Ws[l]), host(Gs[l]))
+        bH, bw = bounds(Hh, host(Ws[l]), host(Gs[l]))
+        ref += dH
+        bH_tot += bH
+        e = np.abs(host(dws[l]).astype(np.float64) - dw_ref)
+        assert np.all(e <= C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref)), f"dL/dw layer {l}"
+    err = np.abs(host(grads) - ref)
+    lim = C_BWD * bH_tot + 2.0 ** -22 * np.abs(ref) + 2.0 ** -23 * np.abs(host(prefill))
+    assert np.all(err <= lim), f"gradient rows: ratio {np.max(err / lim):.3g}"
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

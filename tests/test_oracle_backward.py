@@ -79,6 +79,27 @@ def test_planted_backward_mistake_is_caught(name):
     assert failures, f"planted mistake {name!r} passed every backward pin"
 
 
+def test_oracle_per_source_query_shares_pinned():
+    def shares(H, w, g, eps):
+        _, dw, dw_src = orc.depth_attention_backward(H, w, g, eps, per_source=True)
+        return dw, dw_src
+    pins.pin_backward_per_source(shares)
+
+
+def test_planted_per_source_mistake_is_caught():
+    """Shares taken along the raw sources instead of the keys fail the pin."""
+    def wrong(H, w, g, eps):
+        H = np.asarray(H, np.float64)
+        _, dw = orc.depth_attention_backward(H, w, g, eps)
+        _, a = orc.depth_attention(H, w, eps)
+        da = np.stack([np.sum(np.asarray(g) * H[s], axis=1) for s in range(H.shape[0])], axis=1)
+        dz = a * (da - np.sum(a * da, axis=1, keepdims=True))
+        raw = np.stack([np.sum(dz[:, s:s + 1] * H[s], axis=0) for s in range(H.shape[0])])
+        return dw, raw
+    with pytest.raises(AssertionError):
+        pins.pin_backward_per_source(wrong)
+
+
 def _torch_schedule_grads(h0, Fs, Ws, block_size, g_r, w_final, g_final, eps=orc.EPS):
     """Autograd through Block AttnRes written with torch sums, rms_norm and sdpa
     in float64 (exact sums: the inputs are small integers)."""
