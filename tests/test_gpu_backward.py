@@ -275,19 +275,25 @@ def test_schedule_backward_matches_oracle(final, defer):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("S,defer,T,d", [(9, 0xFF, 37, 7168), (4, 0b0101, 45, 1032), (3, 0b111, 20, 264),
-                                         (2, 0b01, 300, 7176)])
-def test_deferred_backward_matches_oracle(dtype, S, defer, T, d):
+@pytest.mark.parametrize("S,defer,T,d,acc", [(9, 0xFF, 37, 7168, 0), (9, 0xFF, 37, 7168, 0x100),
+                                             (4, 0b0101, 45, 1032, 0b1010), (3, 0b111, 20, 264, 0),
+                                             (2, 0b01, 300, 7176, 0b10), (1, 0b0, 9, 7168, 1)])
+def test_deferred_backward_matches_oracle(dtype, S, defer, T, d, acc):
     """Deferred sources: their rows stay untouched and their coefficients,
     recombined as a_s g + c1_s w - c3_s H_s, give the oracle's dH_s; the other
-    rows match the oracle; dL/dw is the oracle's share of the other sources."""
-    note(f"deferred backward dtype={dtype} S={S} defer={defer:#x} T={T} d={d}")
+    rows match the oracle (added into the prefill where ``acc`` says so), the
+    handed-out copy of the last row is its rounding, and dL/dw is the oracle's
+    share of the other sources."""
+    note(f"deferred backward dtype={dtype} S={S} defer={defer:#x} T={T} d={d} acc={acc:#x}")
     H, w, g = inputs(S, T, d, dtype, seed=S * 7 + T)
     dev = H.device
     prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(5), device=dev)
     grads = prefill.clone()
     coef = torch.full((T, 3 * S), float("nan"), dtype=torch.float32, device=dev)
-    dw = B.aggregate_backward(H, w, g, grads, defer=defer, coef=coef, coef_stride=3 * S)
+    last_deferred = (defer >> (S - 1)) & 1
+    hand = None if last_deferred else torch.empty((T, d), dtype=dtype, device=dev)
+    dw = B.aggregate_backward(H, w, g, grads, accumulate=acc, defer=defer, coef=coef, coef_stride=3 * S,
+                              grad_last=hand)
     torch.cuda.synchronize()
     Hh, wh, gh = host(H), host(w), host(g)
     dH_ref, _, dw_src = orc.depth_attention_backward(Hh, wh, gh, per_source=True)
@@ -300,10 +306,12 @@ def test_deferred_backward_matches_oracle(dtype, S, defer, T, d):
             rec = cf[:, s, 0:1] * gh + cf[:, s, 1:2] * wh[None] - cf[:, s, 2:3] * Hh[s]
         else:
             assert np.all(np.isnan(cf[:, s])), f"coefficients written for source {s}, which is not deferred"
-            rec = got[s]
+            rec = got[s] - (host(prefill[s]) if (acc >> s) & 1 else 0.0)
         err = np.abs(rec - dH_ref[s])
-        lim = C_BWD * bH[s] + 2.0 ** -23 * np.abs(dH_ref[s])
+        lim = C_BWD * bH[s] + 2.0 ** -22 * (np.abs(dH_ref[s]) + np.abs(host(prefill[s])))
         assert np.all(err <= lim), f"source {s}: ratio {np.max(err / lim):.3g}"
+    if hand is not None:
+        assert torch.equal(hand, grads[S - 1].to(dtype)), "handed-out gradient is not the row's rounding"
     share = sum(dw_src[s] for s in range(S) if not (defer >> s) & 1) if defer != (1 << S) - 1 else np.zeros(d)
     errw = np.abs(host(dw).astype(np.float64) - share)
     limw = C_BWD * bw + 2.0 ** -23 * np.abs(share)
