@@ -20,9 +20,17 @@
 // per-source coefficients, broadcast with readlane.  The float32 source
 // gradients are then written (or added into, per source) one source at a
 // time, the next source's old rows loading while the current one is formed.
-// dL/dw is accumulated per lane (in LDS) over the workgroup's tokens and
-// written as one float32 row per workgroup; reduce_rows_kernel sums those rows
-// in a fixed order, so the result is deterministic for a given grid.
+// dL/dw is accumulated per lane over the workgroup's tokens and written as one
+// float32 row per workgroup; reduce_rows_kernel sums those rows in a fixed
+// order, so the result is deterministic for a given grid.
+//
+// Deferred sources (the inter-block sources every layer of a block shares)
+// leave their gradient rows alone: the layer writes their coefficients
+// (a_s, delta_s/rho_s, delta_s z_s/(d rho_s^2)) and block_backward_kernel
+// applies all the block's layers at once, while block_dw_kernel (MFMA) adds
+// their share of each layer's dL/dw.  When every source but the last is
+// deferred, aggregate_backward_last_kernel streams the rows once and keeps
+// only the last.
 //
 // HBM bytes per token at S sources, bf16, all gradients accumulated:
 //   2 S d (sources) + 2 d (g) + 8 S d (old and new float32 gradients)
