@@ -133,6 +133,51 @@ def test_backward_is_bitwise_deterministic():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_deferred_backward_and_block_pass_are_bitwise_deterministic():
+    """The streaming kernel (every source but the last deferred) and the block
+    pass with its dL/dw contraction give bit-identical results run to run."""
+    n, Bl, T, d = 6, 5, 300, 7168
+    H, _, _ = inputs(n + 1, T, d, torch.bfloat16, seed=17)
+    dev = H.device
+    Ws = [synth.query(d, seed=17, device=dev, tag=l) for l in range(Bl)]
+    Gs = [synth.layer_output(T, d, std=1.0, seed=17, tag=90 + l, device=dev) for l in range(Bl)]
+    runs = []
+    for _ in range(2):
+        grads = torch.zeros((n + 1, T, d), dtype=torch.float32, device=dev)
+        coef = torch.empty((T, Bl, n, 3), dtype=torch.float32, device=dev)
+        dws = [B.aggregate_backward(H, Ws[l], Gs[l], grads, accumulate=1 << n, defer=(1 << n) - 1,
+                                    coef=coef.view(-1)[3 * n * l:], coef_stride=3 * n * Bl) for l in range(Bl)]
+        B.block_backward(H[:n], Gs, Ws, coef, grads[:n], dws)
+        runs.append((grads, coef, dws))
+    torch.cuda.synchronize()
+    (g0, c0, w0), (g1, c1, w1) = runs
+    assert torch.equal(g0, g1) and torch.equal(c0, c1)
+    assert all(torch.equal(a, b) for a, b in zip(w0, w1))
+
+
+def test_backward_workspace_too_small_is_rejected():
+    """Both backward entry points check the workspace size against the launch
+    they would make and launch nothing when it is short."""
+    n, Bl, T, d = 3, 2, 64, 1024
+    H, w, g = inputs(n, T, d, torch.bfloat16, seed=18)
+    dev = H.device
+    grads = torch.zeros((n, T, d), dtype=torch.float32, device=dev)
+    need = B.backward_workspace_bytes(T, d)
+    short = torch.empty(max(need // 4 - 4, 4), dtype=torch.float32, device=dev)
+    with pytest.raises(B.AttnResError) as exc:
+        B.aggregate_backward(H, w, g, grads, workspace=short)
+    assert exc.value.status == B.EINVAL
+    coef = torch.zeros((T, Bl, n, 3), dtype=torch.float32, device=dev)
+    dws = [torch.zeros(d, dtype=torch.float32, device=dev) for _ in range(Bl)]
+    need = B.block_workspace_bytes(T, d, Bl)
+    short = torch.empty(max(need // 4 - 4, 4), dtype=torch.float32, device=dev)
+    with pytest.raises(B.AttnResError) as exc:
+        B.block_backward(H, [g] * Bl, [w] * Bl, coef, grads, dws, workspace=short)
+    assert exc.value.status == B.EINVAL
+    torch.cuda.synchronize()
+    assert not grads.any() and not any(x.any() for x in dws), "nothing may run on a rejected call"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_backward_one_source_passes_the_gradient_through(dtype):
     H, w, g = inputs(1, 50, 264, dtype, seed=8)
