@@ -11,7 +11,7 @@
 //     dL/dH_s = a_s g + (delta_s / rho_s) w - (delta_s z_s / (d rho_s^2)) H_s,
 //     dL/dw  += sum_s (delta_s / rho_s) H_s,
 // the first term being the value path and the other two the softmax / query /
-// key path of the gradient (llm-atlas.k1412.top/k3, round-06 study).
+// key path of the gradient (llm-atlas.k1412.top/k3, study of the spike trajectory x backward path).
 //
 // One pass per token, like the forward: each lane loads its V 16-byte pieces
 // of every source and of g at once; three reductions per source (sum of

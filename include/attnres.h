@@ -289,7 +289,7 @@ ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t coun
  *   dL/dw   = sum over tokens and sources of (delta_s / rho_s) H_s,
  * with rho_s = sqrt(mean(H_s^2) + eps) and z_s, a_s the forward's logits and
  * weights: the value path and the softmax / query / key path of the gradient
- * (llm-atlas.k1412.top/k3, round-06 study).
+ * (llm-atlas.k1412.top/k3, study of the spike trajectory x backward path).
  *
  *   sources, S, T, d, src_stride, w, eps, dtype   as attnres_aggregate, S <= 9.
  *   last_source     device, [T][d] in dtype, or NULL: when given, source S-1 is

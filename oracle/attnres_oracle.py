@@ -19,8 +19,8 @@ Pages cited below (titles as published; section, equation or figure named):
           (RMSNorm eps is 1e-5 throughout the model).
 * [ATLAS] llm-atlas.k1412.top/k3 -- card "07 ATTENTION RESIDUALS" (the
           alpha_{i->l} formula; 8 layer blocks + embedding = 9 sources), the
-          "save per block" source-count widget, and the round-08 uniform-mixer
-          study (zero logits give weight 1/N).
+          "save per block" source-count widget, and the study of the parameter-free
+          uniform mixer (zero logits give weight 1/N).
 
 Readings where the pages are silent or garbled (each also listed in the design
 notes): eps sits inside the square root; the RMSNorm has no gain; there is no
@@ -30,7 +30,7 @@ outputs; a bf16 store forms each partial sum in float32 and rounds it to bf16
 with round-to-nearest-even.  Backward: the pages give no formula, only that
 training recomputes the aggregation ([TUT] §4.6) and that the gradient
 reaches a source along a value path and a softmax/query/key path ([ATLAS]
-round-06 study, spike trajectory x backward path); the gradient here is the exact
+study of the spike trajectory x backward path); the gradient here is the exact
 derivative of the forward definition, and the rounding of a stored sum passes
 gradients through unchanged.
 
@@ -263,7 +263,7 @@ def run_full_schedule(h0, layer_outputs, queries, final_query=None, eps: float =
 # schedule.  The pages fix no formula; training recomputes the aggregation
 # ([TUT] §4.6), and the gradient reaches each source along a value path (the
 # weight times the upstream gradient) and along the softmax / query / key path
-# ([ATLAS] round-06 study, spike trajectory x backward path).  Written as the chain
+# ([ATLAS] study of the spike trajectory x backward path).  Written as the chain
 # rule through the forward's steps, in the forward's order.
 # ----------------------------------------------------------------------------
 

@@ -11,7 +11,7 @@ in ``test_oracle_pins.py`` must fail at least one.  Facts used:
 * a library reduction: ``torch.nn.functional.rms_norm`` for the keys and
   ``scaled_dot_product_attention`` (scale 1) for softmax and weighted sum;
 * closed forms: one source, a zero query (the uniform mixer of llm-atlas's
-  round-08 study), identical sources, two sources (a logistic), a huge query
+  uniform-mixer study), identical sources, two sources (a logistic), a huge query
   (one-hot);
 * invariants: weights non-negative summing to one (§2 of the blog above),
   keys blind to a positive rescaling (kimi.papertok.ai ch. 0 §0.11),

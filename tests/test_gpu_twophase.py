@@ -168,7 +168,7 @@ def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
 @pytest.mark.parametrize("two_phase_from", [1, None])
 def test_sublayer_granularity_schedule(two_phase_from):
     """One aggregation per residual sublayer (attention and MLP each with its own
-    query), as in the round-04 reduced mechanism probe of llm-atlas.k1412.top/k3
+    query), as in the reduced mechanism probe of llm-atlas.k1412.top/k3
     (16 transformer blocks, 32 residual sublayers): 20 layers = 40 sublayer
     steps in blocks of 10 layers = 20 steps.  Two-phase blocks then hold 20
     queries, more than one inter-block pass takes: the schedule runs two passes
