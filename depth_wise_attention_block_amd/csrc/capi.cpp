@@ -67,9 +67,7 @@ int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus,
 }
 
 // Compute units of the current device, queried once per device.
-// A device attribute of the current device, queried once per device.
-template <int kSlot>
-int device_attr(hipDeviceAttribute_t attr, int* out) {
+int device_cus(int* out) {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ATTNRES_ELAUNCH;
@@ -80,14 +78,13 @@ int device_attr(hipDeviceAttribute_t attr, int* out) {
       return ATTNRES_OK;
     }
   }
-  int v = 0;
-  if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) return ATTNRES_ELAUNCH;
-  if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
-  *out = v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return ATTNRES_ELAUNCH;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
   return ATTNRES_OK;
 }
-
-int device_cus(int* out) { return device_attr<0>(hipDeviceAttributeMultiprocessorCount, out); }
 
 int check_store(const attnres_store_t* st) {
   if (st == nullptr) return ATTNRES_EINVAL;
