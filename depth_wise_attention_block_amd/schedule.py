@@ -7,8 +7,13 @@ partial, and the block's last layer closes it (§4.6: the representation is
 produced once at the boundary and then stays resident).  The output layer
 aggregates h_0 and every block representation (§4.3, last paragraph).
 
-Each step is one ``attnres_aggregate`` and one ``attnres_accumulate`` call;
-the only host work is deciding the finalize flag.
+``run_schedule`` drives the forward through the C ABI -- per layer (an
+aggregation and a partial-sum update, or both fused in one launch) or, from a
+chosen block on, two-phase (one pass over a block's inter-block sources for
+all its queries, then one merge per layer); ``run_full_schedule`` drives Full
+AttnRes; ``run_schedule_backward`` the backward in reverse layer order.  The
+only host work is bookkeeping: which sources a layer sees, the finalize flags
+and the buffers.
 """
 
 from __future__ import annotations
