@@ -12,9 +12,15 @@ so both time and check exactly the same launches.
 * ``Schedule``: the whole 93-layer depth path at one batch of tokens -- every
   layer's aggregation and partial-sum update with block closing every 12
   layers, then the output layer's aggregation over h_0 and the 8 block
-  representations.
+  representations (per layer, fused, or two-phase from block 3).
+* ``ManySources``: one Full AttnRes aggregation over many sources.
+* ``LayerBackward``: the backward of one 9-source aggregation.
+* ``ScheduleBackward``: the whole 93-layer depth path in reverse -- the output
+  layer, then every layer with each block's partial sums recomputed and its
+  inter-block gradients deferred to one pass per block.
 
-Inputs come from :mod:`.synth` (seeded, generated on the device).
+Each class gives ``step`` and ``step_bytes`` (the algorithmic HBM bytes of a
+step).  Inputs come from :mod:`.synth` (seeded, generated on the device).
 """
 
 from __future__ import annotations
