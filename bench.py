@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="prefill_t262144",
-                   choices=["prefill_t262144", "layer_t4096", "decode", "schedule_93", "full_s94",
+                   choices=["prefill_t262144", "layer_t4096", "decode", "decode_93", "schedule_93", "full_s94",
                             "backward_t32768", "schedule_93_backward"])
     p.add_argument("--decode-T", type=int, default=64)
     p.add_argument("--seed", type=int, default=0)
@@ -154,6 +154,52 @@ def cpu_baseline_backward(wl, budget_s: float, seed: int):
                       f"one thread, {elapsed:.1f} s"}
 
 
+def bench_decode_93(args, dev):
+    """The whole 93-layer depth path for a decode batch (T = --decode-T tokens):
+    one pass = 94 aggregations (93 fused update + aggregate launches and the
+    output layer), launched eagerly from Python or replayed as one HIP graph."""
+    import torch
+
+    from depth_wise_attention_block_amd import workloads
+
+    wl = workloads.Schedule(args.decode_T, seed=args.seed, device=dev)
+    T = wl.T
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    eager_ms = timed(lambda: wl.step(mode="fused"))
+    graph = wl.capture("fused")
+    graph_ms = timed(graph.replay)
+    step_bytes = wl.step_bytes("fused")
+    achieved = step_bytes / (graph_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(T / (graph_ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_93", "T": T, "d": wl.d, "layers": wl.layers, "block_size": wl.block_size,
+                   "step": "one decode pass through the 93-layer depth path (94 aggregations), replayed as a "
+                           "HIP graph"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "whole pass (launch-bound at this size)", "bytes_per_launch": step_bytes},
+        "cpu_baseline": None,
+        "detail": {"eager_ms_per_pass": round(eager_ms, 4), "graph_ms_per_pass": round(graph_ms, 4),
+                   "launches_per_pass": len(wl.source_counts()),
+                   "graph_us_per_aggregation": round(graph_ms * 1e3 / len(wl.source_counts()), 2)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,6 +222,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     binding.lib()
+    if args.workload == "decode_93":
+        print(json.dumps(bench_decode_93(args, dev)), flush=True)
+        return
 
     fused = not args.unfused
     t_setup = time.perf_counter()

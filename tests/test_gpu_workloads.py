@@ -139,3 +139,32 @@ def test_schedule_93_backward_sampled():
         assert np.all(err <= lim), f"dF_{l}: max error {np.max(err):.3e}"
     del wl
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,mode", [(1, "fused"), (64, "fused"), (64, "two_phase")])
+def test_schedule_graph_replays_equal_eager(T, mode):
+    """The decode pass captured as one HIP graph: every replay -- with eager
+    work and synchronisations in between -- leaves the same residuals, weights,
+    output-layer result and store (block representations) as the eager pass,
+    bit for bit."""
+    note(f"schedule graph T={T} mode={mode}")
+    wl = workloads.Schedule(T, seed=5, device=device())
+    wl.step(mode=mode)
+    torch.cuda.synchronize()
+    def bits(t):
+        return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+    ref = [t.clone() for t in (wl.out, wl.weights, wl.final_out, wl.final_weights, wl.store.slots)]
+    graph = wl.capture(mode)
+    scratch = torch.empty((T, wl.d), dtype=torch.bfloat16, device=wl.out.device)
+    for rep in range(4):
+        for t in (wl.out, wl.weights, wl.final_out, wl.final_weights):
+            t.fill_(float("nan"))
+        wl.store.slots[1:].fill_(float("nan"))                 # everything but h_0 is recomputed
+        torch.cuda.synchronize()
+        graph.replay()
+        scratch.copy_(wl.F[rep])                                  # eager work between replays
+        torch.cuda.synchronize()
+        got = (wl.out, wl.weights, wl.final_out, wl.final_weights, wl.store.slots)
+        for name, a, b in zip(("out", "weights", "final_out", "final_weights", "slots"), ref, got):
+            assert torch.equal(bits(a), bits(b)), f"replay {rep}: {name} differs from the eager pass"
