@@ -22,6 +22,7 @@ MAX_SOURCES = 9            # Block AttnRes store slots
 MAX_SOURCES_FULL = 256     # one aggregation (Full AttnRes / sublayer granularity)
 MAX_INTER_SOURCES = 8      # two-phase: inter-block sources per pass
 MAX_BLOCK_QUERIES = 16     # two-phase: layer queries per pass
+MAX_D_BF16, MAX_D_F32 = 16384, 8192   # widest rows (ATTNRES_MAX_D_BF16 / _F32)
 OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
 

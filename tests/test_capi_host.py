@@ -325,3 +325,15 @@ def test_partial_sums_host_checks(lib):
     assert ps(T=0) == B.OK and ps(stride=8) == B.EINVAL and ps(out=None) == B.EINVAL
     assert ps(out=OUT + 8) == B.EUNSUPPORTED and ps(arr=Arr(SRC, 0, SRC)) == B.EINVAL
     assert ps(arr=Arr(SRC, SRC + 8, SRC)) == B.EUNSUPPORTED and ps(out=SRC + 4096) == B.EALIAS
+
+
+def test_binding_limits_match_the_header():
+    """The binding's size limits are the header's #defines."""
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                             "attnres.h")).read()
+    defines = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (ATTNRES_\w+) (\d+)", text)}
+    assert defines["ATTNRES_MAX_SOURCES"] == B.MAX_SOURCES
+    assert defines["ATTNRES_MAX_SOURCES_FULL"] == B.MAX_SOURCES_FULL
+    assert defines["ATTNRES_MAX_INTER_SOURCES"] == B.MAX_INTER_SOURCES
+    assert defines["ATTNRES_MAX_BLOCK_QUERIES"] == B.MAX_BLOCK_QUERIES
+    assert defines["ATTNRES_MAX_D_BF16"] == B.MAX_D_BF16 and defines["ATTNRES_MAX_D_F32"] == B.MAX_D_F32

@@ -28,11 +28,15 @@ def run(H: torch.Tensor, w: torch.Tensor, **kw):
 ])
 def test_ragged_shapes_match_oracle(dtype, S, T, d):
     dev = device()
-    if dtype == "f32" and d > 8192:
-        pytest.skip("fp32 rows above 8192 elements are outside the supported range")
     note(f"aggregate {dtype} S={S} T={T} d={d}")
     H = synth.sources(S, T, d, scale=(0.5, 50.0), seed=S * 131 + T, dtype=dtype, device=dev)
     w = synth.query(d, seed=T, device=dev)
+    if dtype == "f32" and d > B.MAX_D_F32:
+        # float32 rows wider than the supported maximum are refused before any launch
+        with pytest.raises(B.AttnResError) as exc:
+            run(H, w)
+        assert exc.value.status == B.EUNSUPPORTED
+        return
     out, a = run(H, w)
     r_ref, a_ref = oracle_aggregate(host(H), host(w))
     compare(host(out), host(a), r_ref, a_ref, dtype == "bf16", f"{dtype} S={S} T={T} d={d}")
