@@ -55,13 +55,15 @@ def check(dH_gpu, dw_gpu, H, w, g, what, prefill=None):
         dH_ref = dH_ref + prefill
     bH, bw = bounds(H, w, g)
     errH = np.abs(np.asarray(dH_gpu, np.float64) - dH_ref)
-    # float32 rounding of a result (and of prefill + result) is within the bound's slack
-    limH = C_BWD * bH + 2.0 ** -23 * np.abs(dH_ref)
+    # float32 rounding of a result (and of prefill + result) is within the bound's slack; below
+    # float32's smallest normal a result cannot be carried at all (one-hot weights leave terms of
+    # 1e-115 in float64 that are 0 in float32)
+    limH = C_BWD * bH + 2.0 ** -23 * np.abs(dH_ref) + np.finfo(np.float32).tiny
     rH = float(np.max(errH / limH))
     rw = 0.0
     if dw_gpu is not None:
         errw = np.abs(np.asarray(dw_gpu, np.float64) - dw_ref)
-        limw = C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref)
+        limw = C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref) + np.finfo(np.float32).tiny
         rw = float(np.max(errw / limw))
     note(f"{what}: max err / bound dH {rH:.3g} dw {rw:.3g}")
     assert rH <= 1.0, f"{what}: dH error {np.max(errH):.3e} exceeds the bound (ratio {rH:.3g})"
@@ -458,3 +460,30 @@ def test_partial_sums_are_the_store_updates(dtype, count):
     for k in range(count):
         part = orc.accumulate(part, host(Fs[k]), name)
         assert np.array_equal(host(out[k]), part), f"partial {k}"
+
+
+@pytest.mark.parametrize("case", ["zero_query", "identical_sources", "tiny_source", "zero_source", "huge_query"])
+def test_backward_degenerate_cases(case):
+    """The method's degenerate inputs through the backward, against the oracle
+    within the same bound: a zero query (uniform weights, no key-path term from
+    the logits), identical sources (equal logits), a source whose mean square
+    is near eps, an all-zero source (key 0, logit 0), and a huge query
+    (one-hot weights, the softmax gradient vanishing)."""
+    note(f"backward degenerate {case}")
+    S, T, d = 5, 40, 1032
+    H, w, g = inputs(S, T, d, torch.float32, seed=44)
+    if case == "zero_query":
+        w = torch.zeros_like(w)
+    elif case == "identical_sources":
+        H = H[:1].repeat(S, 1, 1).contiguous()
+    elif case == "tiny_source":
+        H[2] *= 3e-3 / H[2].pow(2).mean(dim=-1, keepdim=True).sqrt()
+    elif case == "zero_source":
+        H[1].zero_()
+    elif case == "huge_query":
+        w = w * 1e4
+    grads = torch.empty((S, T, d), dtype=torch.float32, device=H.device)
+    dw = B.aggregate_backward(H, w, g, grads)
+    torch.cuda.synchronize()
+    check(host(grads), host(dw), host(H), host(w), host(g), f"degenerate {case}")
+    assert torch.isfinite(grads).all() and torch.isfinite(dw).all()
