@@ -1,0 +1,128 @@
+"""Seeded random shapes through the hot path against the oracle: the
+aggregation over strided sources, the fused update + aggregation (bit-exact
+against the pair of separate calls and within the parity bar of the oracle),
+and the aggregation backward with random accumulate / defer masks.  Every case
+prints its parameters before it runs."""
+
+import numpy as np
+import pytest
+import torch
+
+from depth_wise_attention_block_amd import binding as B
+from depth_wise_attention_block_amd import synth
+from oracle import attnres_oracle as orc
+from tests.gpu_util import compare, device, host, note, oracle_aggregate
+from tests.test_gpu_backward import C_BWD, bounds
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        vec = 8 if dtype == "bf16" else 4
+        d = int(vec * rng.integers(1, (8192 if dtype == "bf16" else 4096) // vec + 1))
+        if rng.random() < 0.3:
+            d = 7168
+        S = int(rng.integers(1, 10))
+        T = int(rng.integers(0, 200))
+        pad = int(vec * rng.integers(0, 64)) if rng.random() < 0.5 else 0
+        out.append((k, dtype, S, T, d, pad, int(rng.integers(0, 2 ** 31))))
+    return out
+
+
+def _sources(S, T, d, pad, dtype, seed, dev):
+    """S rows of [T, d] at a row stride of T*d + pad (pad = 0: contiguous)."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    base = torch.empty(S * (T * d + pad) + 16, dtype=tdt, device=dev)
+    H = base[: S * (T * d + pad)].view(S, T * d + pad)[:, : T * d].view(S, T, d) if S * T * d else \
+        torch.empty((S, T, d), dtype=tdt, device=dev)
+    if S * T * d:
+        H.copy_(synth.sources(S, T, d, scale=(0.2, 30.0), seed=seed, dtype=dtype, device=dev))
+    return H
+
+
+@pytest.mark.parametrize("case", _cases(24, 2024), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}-pad{c[5]}")
+def test_random_aggregate(case):
+    k, dtype, S, T, d, pad, seed = case
+    note(f"random aggregate #{k}: {dtype} S={S} T={T} d={d} pad={pad}")
+    dev = device()
+    H = _sources(S, T, d, pad, dtype, seed, dev)
+    w = synth.query(d, seed=seed, device=dev)
+    out, a = B.aggregate(H, w)
+    torch.cuda.synchronize()
+    if T == 0:
+        return
+    r_ref, a_ref = oracle_aggregate(host(H), host(w))
+    compare(host(out), host(a), r_ref, a_ref, dtype == "bf16", f"random #{k}")
+
+
+@pytest.mark.parametrize("case", _cases(16, 77), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
+def test_random_fused_update(case):
+    k, dtype, S, T, d, _, seed = case
+    dev = device()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(seed)
+    # a store state with room for the update: n_done completed blocks (<= 7),
+    # an open partial or not (its first layer: the update is a copy), closing or not
+    n_done = min(S - 1, 7)
+    partial_valid = bool(rng.random() < 0.7)
+    finalize = bool(rng.random() < 0.3)
+    note(f"random fused #{k}: {dtype} T={T} d={d} n_done={n_done} partial={partial_valid} finalize={finalize}")
+    stores = [B.SourceStore(T, d, s_max=9, dtype=tdt, device=dev) for _ in range(2)]
+    init = synth.sources(9, T, d, scale=(0.2, 30.0), seed=seed, dtype=dtype, device=dev)
+    for st in stores:
+        st.slots.copy_(init)
+        st.set_state(n_done, partial_valid)
+    F = synth.layer_output(T, d, std=1.0, seed=seed, tag=3, device=dev, dtype=dtype)
+    w = synth.query(d, seed=seed, device=dev)
+    out_f, a_f = stores[0].accumulate_aggregate(F, finalize, w)
+    stores[1].accumulate(F, finalize_block=finalize)
+    out_p, a_p = stores[1].aggregate(w)
+    torch.cuda.synchronize()
+    assert torch.equal(stores[0].slots, stores[1].slots), "store rows differ from the separate update"
+    assert torch.equal(out_f, out_p) and torch.equal(a_f, a_p), "fused result differs from the pair"
+    if T:
+        H = host(stores[1].sources())
+        r_ref, a_ref = oracle_aggregate(H, host(w))
+        compare(host(out_f), host(a_f), r_ref, a_ref, dtype == "bf16", f"random fused #{k}")
+
+
+@pytest.mark.parametrize("case", _cases(16, 99), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
+def test_random_backward(case):
+    k, dtype, S, T, d, pad, seed = case
+    rng = np.random.default_rng(seed)
+    acc = int(rng.integers(0, 2 ** S))
+    defer = int(rng.integers(0, 2 ** S)) if rng.random() < 0.5 else 0
+    note(f"random backward #{k}: {dtype} S={S} T={T} d={d} pad={pad} acc={acc:#x} defer={defer:#x}")
+    dev = device()
+    H = _sources(S, T, d, pad, dtype, seed, dev)
+    w = synth.query(d, seed=seed, device=dev)
+    g = synth.layer_output(T, d, std=1.0, seed=seed, tag=4, device=dev, dtype=dtype)
+    prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(seed % 1000), device=dev)
+    grads = prefill.clone()
+    coef = torch.zeros((max(T, 1), 3 * S), dtype=torch.float32, device=dev)
+    dw = B.aggregate_backward(H, w, g, grads, accumulate=acc, defer=defer, coef=coef if defer else None,
+                              coef_stride=3 * S)
+    torch.cuda.synchronize()
+    if T == 0:
+        assert not dw.any()
+        return
+    Hh, wh, gh = host(H), host(w), host(g)
+    dH_ref, _, dw_src = orc.depth_attention_backward(Hh, wh, gh, per_source=True)
+    bH, bw = bounds(Hh, wh, gh)
+    got, cf = host(grads), host(coef).astype(np.float64).reshape(T, S, 3)
+    tiny = np.finfo(np.float32).tiny
+    for s in range(S):
+        if (defer >> s) & 1:
+            assert torch.equal(grads[s], prefill[s]), f"deferred row {s} written"
+            rec = cf[:, s, 0:1] * gh + cf[:, s, 1:2] * wh[None] - cf[:, s, 2:3] * Hh[s]
+        else:
+            rec = got[s] - (host(prefill[s]) if (acc >> s) & 1 else 0.0)
+        lim = C_BWD * bH[s] + 2.0 ** -22 * (np.abs(dH_ref[s]) + np.abs(host(prefill[s]))) + tiny
+        assert np.all(np.abs(rec - dH_ref[s]) <= lim), f"source {s}: ratio {np.max(np.abs(rec - dH_ref[s]) / lim):.3g}"
+    share = sum((dw_src[s] for s in range(S) if not (defer >> s) & 1), np.zeros(d))
+    limw = C_BWD * bw + 2.0 ** -23 * np.abs(share) + tiny
+    assert np.all(np.abs(host(dw).astype(np.float64) - share) <= limw), "dw share"
