@@ -50,8 +50,17 @@ constexpr int kUpdateNone = 0, kUpdateCopy = 1, kUpdateAdd = 2;
 template <int kV>
 constexpr int waves_per_simd() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
 
-template <bool kBf16, int kV, int kUpdate>
-__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kV>())))
+// Instances bounded at kSmallSrc sources hold fewer rows per lane and are built
+// for more waves per SIMD: with only a few rows per token, the bytes a CU keeps
+// in flight come from more resident workgroups rather than from more rows.
+constexpr int kSmallSrc = 4;
+template <int kV, int kMaxS>
+constexpr int waves_per_simd_s() {
+  return kMaxS > kSmallSrc ? waves_per_simd<kV>() : kV == 1 ? 7 : kV == 2 ? 6 : kV == 3 ? 4 : 3;
+}
+
+template <bool kBf16, int kV, int kUpdate, int kMaxS>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_s<kV, kMaxS>())))
 aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
                  float eps, float inv_d, const u32x4* __restrict__ layer_out) {
@@ -71,14 +80,14 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
     u32x4* tok = src + t * (int64_t)nvec;
-    const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxSrc;  // the updated slot, if any
+    const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxS;  // the updated slot, if any
 
     // 1. issue every load of this token: S sources x V vectors per lane (for
     //    the updated slot: the layer output, and the old slot row when adding)
-    u32x4 x[kMaxSrc][kV];
+    u32x4 x[kMaxS][kV];
     u32x4 f[kV];
 #pragma unroll
-    for (int s = 0; s < kMaxSrc; ++s) {
+    for (int s = 0; s < kMaxS; ++s) {
       if (s < S) {
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
@@ -103,7 +112,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
     if constexpr (kUpdate != kUpdateNone) {
       // new slot row = old + layer output (or the layer output), written back
 #pragma unroll
-      for (int s = 0; s < kMaxSrc; ++s) {
+      for (int s = 0; s < kMaxS; ++s) {
         if (s == s_upd) {
 #pragma unroll
           for (int v = 0; v < kV; ++v) {
@@ -118,7 +127,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
     // 2. per-lane partial statistics, then wave sums
     float gss = 0.f, gdt = 0.f;  // lane s of the row: source s's wave sums
 #pragma unroll
-    for (int s = 0; s < kMaxSrc; ++s) {
+    for (int s = 0; s < kMaxS; ++s) {
       if (s < S) {
         float ss = 0.f, dt = 0.f;
 #pragma unroll
@@ -168,9 +177,9 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
     if (weights != nullptr && wave == 0 && lane < S) weights[t * S + lane] = a;
 
     // 5. weighted sum of the raw sources in float32, one rounding to the output
-    float as[kMaxSrc];
+    float as[kMaxS];
 #pragma unroll
-    for (int s = 0; s < kMaxSrc; ++s) as[s] = (s < S) ? lane_bcast(a, s) : 0.f;
+    for (int s = 0; s < kMaxS; ++s) as[s] = (s < S) ? lane_bcast(a, s) : 0.f;
 
     u32x4* orow = out + t * (int64_t)nvec;
 #pragma unroll
@@ -184,7 +193,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
           acc[2 * k + 1] = as[0] * bf16_hi(x[0][v][k]);
         }
 #pragma unroll
-        for (int s = 1; s < kMaxSrc; ++s) {
+        for (int s = 1; s < kMaxS; ++s) {
           if (s < S) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -200,7 +209,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
       } else {
         f32x4 acc = as[0] * __builtin_bit_cast(f32x4, x[0][v]);
 #pragma unroll
-        for (int s = 1; s < kMaxSrc; ++s) {
+        for (int s = 1; s < kMaxS; ++s) {
           if (s < S) {
             const f32x4 xf = __builtin_bit_cast(f32x4, x[s][v]);
 #pragma unroll
@@ -371,15 +380,21 @@ hipError_t launch_many(const AggregateArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool kBf16, int kV, int kUpdate>
-hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
+template <bool kBf16, int kV, int kUpdate, int kMaxS>
+hipError_t launch_s(const AggregateArgs& a, hipStream_t stream) {
   const int epv = kBf16 ? 8 : 4;
   const int nvec = a.d / epv;
-  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
-                     static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec, a.src_stride / epv, a.w,
-                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
+  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS>), dim3((unsigned)a.grid), dim3(a.threads), 0,
+                     stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
+                     a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
                      static_cast<const u32x4*>(a.layer_out));
   return hipGetLastError();
+}
+
+template <bool kBf16, int kV, int kUpdate>
+hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
+  return a.S <= kSmallSrc ? launch_s<kBf16, kV, kUpdate, kSmallSrc>(a, stream)
+                          : launch_s<kBf16, kV, kUpdate, kMaxSrc>(a, stream);
 }
 
 hipError_t launch_many_v(const AggregateArgs& a, hipStream_t stream) {
