@@ -356,7 +356,7 @@ def main():
         else:
             ms_step = wall * 1e3 / args.steps
         dom_bytes = wl.fused_bytes() if fused else wl.aggregate_bytes()
-        kernel = "aggregate_kernel<true, 2, 2>" if fused else "aggregate_kernel<true, 2, 0>"
+        kernel = "aggregate_kernel<true, 2, 2, 9>" if fused else "aggregate_kernel<true, 2, 0, 9>"
         achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": counter_traffic(kernel, T),

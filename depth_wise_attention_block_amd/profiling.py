@@ -41,9 +41,9 @@ def algorithmic_bytes(kernel: str, T: int, d: int, S: int):
     """(read, write) bytes each kernel must move at S sources, bf16, or None."""
     row = 2 * T * d
     table = {
-        "aggregate_kernel<true, 2, 0>": (S * row + 4 * d, row + 4 * T * S),
-        "aggregate_kernel<true, 2, 1>": ((S - 1) * row + row + 4 * d, 2 * row + 4 * T * S),
-        "aggregate_kernel<true, 2, 2>": ((S - 1) * row + 2 * row + 4 * d, 2 * row + 4 * T * S),
+        "aggregate_kernel<true, 2, 0, 9>": (S * row + 4 * d, row + 4 * T * S),
+        "aggregate_kernel<true, 2, 1, 9>": ((S - 1) * row + row + 4 * d, 2 * row + 4 * T * S),
+        "aggregate_kernel<true, 2, 2, 9>": ((S - 1) * row + 2 * row + 4 * d, 2 * row + 4 * T * S),
         "accumulate_kernel<true, false>": (2 * row, row),
         "accumulate_kernel<true, true>": (row, row),
     }

@@ -24,7 +24,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 def test_counter_traffic_requires_the_measured_source(tmp_path, monkeypatch):
     from depth_wise_attention_block_amd.profiling import aggregate_source_digest
 
-    kernel = "aggregate_kernel<true, 2, 2>"
+    kernel = "aggregate_kernel<true, 2, 2, 9>"
     summary = {"workload": {"T": 262144, "d": 7168, "S": 9}, "aggregate_source_sha256": aggregate_source_digest(),
                "kernels": {kernel: {"traffic_bytes_per_launch": 123.0}}}
     path = tmp_path / "counters.json"
