@@ -24,6 +24,10 @@
  *   - Return value: ATTNRES_OK or a negative status.  All argument checks run
  *     on the host before anything is enqueued; a failed check enqueues nothing
  *     and makes no HIP call.  Nothing is thrown across the ABI.
+ *   - Once its checks pass, a call reads (and so clears) the calling thread's
+ *     HIP last-error state before it launches, so that ATTNRES_ELAUNCH
+ *     reports its own launches only: a caller that wants the error of an
+ *     earlier launch of its own reads hipGetLastError() before calling here.
  *   - Element layout is row-major; bf16 is IEEE binary32's top 16 bits.
  */
 #ifndef ATTNRES_H
