@@ -50,13 +50,15 @@ constexpr int kUpdateNone = 0, kUpdateCopy = 1, kUpdateAdd = 2;
 template <int kV>
 constexpr int waves_per_simd() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
 
-// Instances bounded at kSmallSrc sources hold fewer rows per lane and are built
-// for more waves per SIMD: with only a few rows per token, the bytes a CU keeps
-// in flight come from more resident workgroups rather than from more rows.
+// Instances bounded at kSmallSrc (or 2) sources hold fewer rows per lane and
+// are built for more waves per SIMD: with only a few rows per token, the bytes
+// a CU keeps in flight come from more resident workgroups rather than from
+// more rows.
 constexpr int kSmallSrc = 4;
 template <int kV, int kMaxS>
 constexpr int waves_per_simd_s() {
-  return kMaxS > kSmallSrc ? waves_per_simd<kV>() : kV == 1 ? 7 : kV == 2 ? 6 : kV == 3 ? 4 : 3;
+  return kMaxS > kSmallSrc ? waves_per_simd<kV>() : kMaxS <= 2 ? (kV == 1 ? 8 : kV == 2 ? 8 : kV == 3 ? 5 : 4)
+                                                  : kV == 1 ? 7 : kV == 2 ? 6 : kV == 3 ? 4 : 3;
 }
 
 template <bool kBf16, int kV, int kUpdate, int kMaxS>
@@ -393,8 +395,9 @@ hipError_t launch_s(const AggregateArgs& a, hipStream_t stream) {
 
 template <bool kBf16, int kV, int kUpdate>
 hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
-  return a.S <= kSmallSrc ? launch_s<kBf16, kV, kUpdate, kSmallSrc>(a, stream)
-                          : launch_s<kBf16, kV, kUpdate, kMaxSrc>(a, stream);
+  return a.S <= 2           ? launch_s<kBf16, kV, kUpdate, 2>(a, stream)
+         : a.S <= kSmallSrc ? launch_s<kBf16, kV, kUpdate, kSmallSrc>(a, stream)
+                            : launch_s<kBf16, kV, kUpdate, kMaxSrc>(a, stream);
 }
 
 hipError_t launch_many_v(const AggregateArgs& a, hipStream_t stream) {
