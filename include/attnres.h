@@ -22,8 +22,11 @@
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).  Work
  *     is enqueued asynchronously on it; buffers must stay alive until it ends.
  *   - Return value: ATTNRES_OK or a negative status.  All argument checks run
- *     on the host before anything is enqueued; a failed check enqueues nothing
- *     and makes no HIP call.  Nothing is thrown across the ABI.
+ *     on the host before anything is enqueued; a failed check enqueues nothing.
+ *     The only HIP calls a check may follow are the query of the current device
+ *     and of its compute-unit count (cached per device), made by the entry
+ *     points whose workspace size depends on them.  Nothing is thrown across
+ *     the ABI.
  *   - Once its checks pass, a call reads (and so clears) the calling thread's
  *     HIP last-error state before it launches, so that ATTNRES_ELAUNCH
  *     reports its own launches only: a caller that wants the error of an
