@@ -1,10 +1,11 @@
 """GPU parity at the widest rows the library takes (bf16 d = 16384 and float32
 d = 8192: four 16-byte vectors per lane) and at three vectors per lane (bf16
 d = 10000, float32 d = 5000), for every kernel family: the aggregation in each
-of its source-bound instances, plain and fused with the partial update; the
-two-phase pair; the backward (the general kernel, the last-source kernel and
-the block pass with its dL/dw contraction).  These are the instances the other
-tests, at d <= 8192 bf16, do not reach.  A few tokens keep the oracle fast."""
+of its source-bound instances, plain and fused with the partial update, and
+over more than 9 sources; the two-phase pair; the backward (the general
+kernel, the last-source kernel and the block pass with its dL/dw contraction).
+These are the instances the other tests, at d <= 8192 bf16, do not reach.  A
+few tokens keep the oracle fast."""
 
 import numpy as np
 import pytest
@@ -34,6 +35,21 @@ def test_wide_aggregate(dtype, d, S):
     torch.cuda.synchronize()
     r_ref, a_ref = oracle_aggregate(host(H), host(w))
     compare(host(out), host(a), r_ref, a_ref, dtype == "bf16", f"wide aggregate {dtype} d={d} S={S}")
+
+
+@pytest.mark.parametrize("dtype,d", WIDE)
+@pytest.mark.parametrize("S", [10, 94])
+def test_wide_many_sources(dtype, d, S):
+    """More than 9 sources (Full AttnRes: batches of 9 merged by online softmax)."""
+    T = 3
+    note(f"wide many sources {dtype} d={d} S={S} T={T}")
+    dev = device()
+    H = synth.sources(S, T, d, scale=(0.5, 50.0), seed=S + d, dtype=dtype, device=dev)
+    w = synth.query(d, seed=S, device=dev)
+    out, a = B.aggregate(H, w)
+    torch.cuda.synchronize()
+    r_ref, a_ref = oracle_aggregate(host(H), host(w))
+    compare(host(out), host(a), r_ref, a_ref, dtype == "bf16", f"wide many sources {dtype} d={d} S={S}")
 
 
 @pytest.mark.parametrize("dtype,d", WIDE)
