@@ -132,6 +132,10 @@ def _check(func: str, status: int) -> int:
 
 
 def _stream(device: torch.device, stream) -> int:
+    """The stream handle for a launch on ``device``, which must be a GPU: the C
+    ABI takes plain pointers and cannot tell host memory from device memory."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, not {device}")
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return int(getattr(stream, "cuda_stream", stream))

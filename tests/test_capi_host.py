@@ -337,3 +337,23 @@ def test_binding_limits_match_the_header():
     assert defines["ATTNRES_MAX_INTER_SOURCES"] == B.MAX_INTER_SOURCES
     assert defines["ATTNRES_MAX_BLOCK_QUERIES"] == B.MAX_BLOCK_QUERIES
     assert defines["ATTNRES_MAX_D_BF16"] == B.MAX_D_BF16 and defines["ATTNRES_MAX_D_F32"] == B.MAX_D_F32
+
+
+def test_binding_refuses_host_tensors():
+    """The C ABI cannot tell host pointers from device pointers, so the binding
+    refuses tensors that are not on a GPU before anything reaches the library --
+    also when a stream handle is given explicitly."""
+    import torch
+    S, T, d = 3, 4, 16
+    H = torch.zeros((S, T, d), dtype=torch.bfloat16)
+    w = torch.zeros(d, dtype=torch.float32)
+    for stream in (None, 0):
+        with pytest.raises(ValueError, match="GPU"):
+            B.aggregate(H, w, stream=stream)
+        with pytest.raises(ValueError, match="GPU"):
+            B.add_rows(H[0], H[1], torch.empty((T, d), dtype=torch.bfloat16), stream=stream)
+        with pytest.raises(ValueError, match="GPU"):
+            B.split_queries(torch.zeros((2, d), dtype=torch.float32), stream=stream)
+        with pytest.raises(ValueError, match="GPU"):
+            B.aggregate_backward(H, w, H[0], torch.zeros((S, T, d), dtype=torch.float32),
+                                 workspace=torch.zeros(64, dtype=torch.float32), stream=stream)
