@@ -17,6 +17,7 @@ REPO = os.path.dirname(HERE)
 LIB_NAME = "libattnres.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 PATTERN_BENCH = os.path.join(HERE, "pattern_bench")
+CAPI_CLIENT = os.path.join(HERE, "capi_client")
 SOURCES = ("aggregate.hip", "accumulate.hip", "twophase.hip", "backward.hip", "capi.cpp")
 ARCH = "gfx950"
 
@@ -52,6 +53,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         print(log)
     os.replace(tmp, LIB_PATH)
     _compile([hipcc(), *HIP_FLAGS, *extra_flags, os.path.join(CSRC, "pattern_bench.hip")], PATTERN_BENCH, verbose)
+    # a plain C program that calls the library through the header alone
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    _compile([shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-I", os.path.join(REPO, "include"),
+              "-I", os.path.join(rocm, "include"), os.path.join(CSRC, "capi_client.c"), "-L", HERE, "-lattnres",
+              "-Wl,-rpath,$ORIGIN", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+              "-Wl,-rpath," + os.path.join(rocm, "lib")], CAPI_CLIENT, verbose)
     return LIB_PATH
 
 
@@ -64,7 +71,7 @@ def _compile(cmd, target: str, verbose: bool) -> None:
     noise = "'-packed-fp32-ops' is not a recognized feature"
     log = "\n".join(l for l in proc.stdout.splitlines() if noise not in l)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{log}")
+        raise RuntimeError(f"{os.path.basename(cmd[0])} failed ({proc.returncode}):\n{log}")
     os.replace(tmp, target)
 
 

@@ -357,3 +357,17 @@ def test_binding_refuses_host_tensors():
         with pytest.raises(ValueError, match="GPU"):
             B.aggregate_backward(H, w, H[0], torch.zeros((S, T, d), dtype=torch.float32),
                                  workspace=torch.zeros(64, dtype=torch.float32), stream=stream)
+
+
+def test_c_client_checks_its_input_before_any_gpu_call(tmp_path):
+    """The plain C caller refuses bad usage and a bad header before it makes
+    any HIP call (so this runs without a GPU)."""
+    import struct
+    import subprocess
+    client = os.path.join(os.path.dirname(B.LIB_PATH), "capi_client")
+    r = subprocess.run([client], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    bad = tmp_path / "bad.bin"
+    bad.write_bytes(struct.pack("<4i", 0, 4, 16, 0))
+    r = subprocess.run([client, str(bad), str(tmp_path / "out.bin")], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "bad header" in r.stderr
