@@ -224,21 +224,37 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   }
 }
 
-// ---- more than 9 sources: online softmax over batches of 9 ------------------
+// ---- more than 9 sources: online softmax over batches ----------------------
 //
 // Full AttnRes (kimi.papertok.ai ch. 4 §4.2: every earlier layer output is a
 // source, S up to L + 1) or sublayer granularity needs more rows than fit in
-// registers at once.  The sources are taken in batches of 9; after each batch
+// registers at once.  The sources are taken in batches of kB; after each batch
 // the running maximum m, normaliser l and float32 accumulator are rescaled by
 // exp(m_old - m_new) before the batch's terms are added ([TUT] §4.4: online
 // softmax merges partial results computed separately).  One barrier per batch.
 // The logits are kept in LDS so the weights can be written once m and l are
 // final.
+//
+// The traffic is nearly all reads (S rows in, one out), so what matters is
+// keeping loads in flight: the rows go through two register buffers, and the
+// next batch is loaded as soon as this one's statistics are formed, so that it
+// arrives while this batch's barrier, merge and weighted sum run (the batch
+// loop is unrolled by two so that each buffer keeps its registers).  Two
+// 9-row buffers take ~210 VGPRs at V = 2: one workgroup per CU whose next batch
+// is always in flight beats two that each drain between batches (smaller
+// batches at two workgroups per CU were slower still: more barriers).  Wider
+// rows take smaller batches.
+template <int kV>
+constexpr int many_batch() { return kV <= 2 ? 9 : kV == 3 ? 5 : 3; }
+template <int kV>
+constexpr int waves_per_simd_many() { return kV == 1 ? 3 : 2; }
+
 template <bool kBf16, int kV>
-__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kV>())))
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_many<kV>())))
 aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                       const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
                       float eps, float inv_d) {
+  constexpr int kB = many_batch<kV>();
   __shared__ float red[2][kMaxWaves][2][16];
   __shared__ float zbuf[kMaxSourcesMany];
 
@@ -252,6 +268,7 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
   Query<kBf16, kV> q;
   load_query<kBf16, kV>(q, w, nvec, tid, nthr);
   constexpr int kE = kBf16 ? 8 : 4;  // elements per 16-byte vector
+  const int nbatches = (S + kB - 1) / kB;
 
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
@@ -263,23 +280,28 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
 #pragma unroll
       for (int e = 0; e < kE; ++e) acc[v][e] = 0.f;
 
-    for (int s0 = 0; s0 < S; s0 += kMaxSrc, buf ^= 1) {
-      const int nb = min(kMaxSrc, S - s0);
-      u32x4 x[kMaxSrc][kV];
+    // rows b*kB .. of this token into x (rows past S left zero)
+    auto load_batch = [&](u32x4 (&x)[kB][kV], int b) {
+      const int s0 = b * kB;
 #pragma unroll
-      for (int s = 0; s < kMaxSrc; ++s) {
-        if (s < nb) {
+      for (int s = 0; s < kB; ++s) {
 #pragma unroll
-          for (int v = 0; v < kV; ++v) {
-            const int idx = v * nthr + tid;
-            x[s][v] = u32x4{0, 0, 0, 0};
-            if (idx < nvec) x[s][v] = __builtin_nontemporal_load(tok + (int64_t)(s0 + s) * src_stride_v + idx);
-          }
+        for (int v = 0; v < kV; ++v) {
+          const int idx = v * nthr + tid;
+          x[s][v] = u32x4{0, 0, 0, 0};
+          if (s0 + s < S && idx < nvec)
+            x[s][v] = __builtin_nontemporal_load(tok + (int64_t)(s0 + s) * src_stride_v + idx);
         }
       }
+    };
+
+    // batch b from x; loads batch b + 1 into xn once x's statistics are formed
+    auto batch = [&](u32x4 (&x)[kB][kV], u32x4 (&xn)[kB][kV], int b) {
+      const int s0 = b * kB;
+      const int nb = min(kB, S - s0);
       float gss = 0.f, gdt = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxSrc; ++s) {
+      for (int s = 0; s < kB; ++s) {
         if (s < nb) {
           float ss = 0.f, dt = 0.f;
 #pragma unroll
@@ -304,6 +326,7 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
           gdt = put_lane(wave_sum(dt), s, gdt, s16);
         }
       }
+      if (b + 1 < nbatches) load_batch(xn, b + 1);
       if (lane < 16) {
         red[buf][wave][0][lane] = gss;
         red[buf][wave][1][lane] = gdt;
@@ -319,21 +342,22 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
         z = dt / sqrtf(ss * inv_d + eps);
         if (wave == 0 && lane < 16) zbuf[s0 + s16] = z;
       }
+      buf ^= 1;
       // online merge of this batch into (m, l, acc)
       const float m_new = fmaxf(m, row_max16(z));
       const float c = expf(m - m_new);  // 0 on the first batch (m = -inf)
       const float p = (s16 < nb) ? expf(z - m_new) : 0.f;
       l = l * c + row_sum16(p);
       m = m_new;
-      float ps[kMaxSrc];
+      float ps[kB];
 #pragma unroll
-      for (int s = 0; s < kMaxSrc; ++s) ps[s] = (s < nb) ? lane_bcast(p, s) : 0.f;
+      for (int s = 0; s < kB; ++s) ps[s] = (s < nb) ? lane_bcast(p, s) : 0.f;
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
 #pragma unroll
         for (int e = 0; e < kE; ++e) acc[v][e] *= c;
 #pragma unroll
-        for (int s = 0; s < kMaxSrc; ++s) {
+        for (int s = 0; s < kB; ++s) {
           if (s < nb) {
             if constexpr (kBf16) {
 #pragma unroll
@@ -349,6 +373,14 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
           }
         }
       }
+    };
+
+    u32x4 xa[kB][kV], xb[kB][kV];
+    load_batch(xa, 0);
+    for (int b = 0; b < nbatches; b += 2) {
+      batch(xa, xb, b);
+      if (b + 1 >= nbatches) break;
+      batch(xb, xa, b + 1);
     }
 
     const float inv_l = 1.0f / l;
