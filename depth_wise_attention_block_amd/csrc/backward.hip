@@ -72,6 +72,19 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&e)[Elems<kBf16>::kE]) {
   }
 }
 
+// A float32 gradient row leaves as kGv 16-byte pieces per lane, piece h of
+// vector idx at (idx * kGv + h).  With kGv = 2 one store instruction covers
+// every other 16 bytes of its lines; non-temporal stores of the two halves of a
+// line are not merged in L2 and each half goes to HBM as its own write (about
+// twice the write traffic), while plain stores are merged there first.
+template <int kGv>
+__device__ __forceinline__ void store_grad_piece(f32x4 v, f32x4* p) {
+  if constexpr (kGv == 1)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 // dL/dw: each lane keeps its running sums for its own elements in LDS (one row
 // of f32x4 per vector) and adds one token's share, summed in registers over the
 // sources, per trip.
@@ -271,7 +284,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
             f32x4 o = old[s & 1][v][h];
             o = f32x4{o[0] + r[4 * h], o[1] + r[4 * h + 1], o[2] + r[4 * h + 2], o[3] + r[4 * h + 3]};
             if (idx < nvec && !((defer_mask >> s) & 1u)) {
-              __builtin_nontemporal_store(o, grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+              store_grad_piece<kGv>(o, grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
               old[s & 1][v][h] = o;  // kept for the copy of the last source's gradient
             }
           }
@@ -485,7 +498,7 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
             o[h][c] = oldl[v][h][c] + fmaf(aL, ge[e], fmaf(c1L, wf[e], -c3L * xe[e]));
           }
           if (idx < nvec)
-            __builtin_nontemporal_store(o[h], grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+            store_grad_piece<kGv>(o[h], grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
         }
         if (grad_last != nullptr && idx < nvec) {
           u32x4 ob;
@@ -598,8 +611,8 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
         if (s < n) {
 #pragma unroll
           for (int h = 0; h < kGv; ++h)
-            __builtin_nontemporal_store(f32x4{acc[s][4 * h], acc[s][4 * h + 1], acc[s][4 * h + 2], acc[s][4 * h + 3]},
-                                        grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+            store_grad_piece<kGv>(f32x4{acc[s][4 * h], acc[s][4 * h + 1], acc[s][4 * h + 2], acc[s][4 * h + 3]},
+                                  grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
           if (grad_last != nullptr && s == n - 1) {
             u32x4 o;
             if constexpr (kBf16) {

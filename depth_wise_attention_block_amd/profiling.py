@@ -5,11 +5,19 @@
     python -m depth_wise_attention_block_amd.profiling counters \
         --run LABEL FETCH.csv WRITE.csv "fetch command" "write command" [--run ...] --out X.json
 
+    python -m depth_wise_attention_block_amd.profiling pass \
+        --fetch FETCH.csv --write WRITE.csv --fetch-cmd "..." --write-cmd "..." \
+        --T T --d D --algorithmic BYTES --label NAME --out X.json
+
 ``counters`` calibrates each counter with the plain-copy kernel that
 ``bench.py --with-copy`` launches in every run (it moves a known T*d bf16 in and
 out), and records the HBM bytes per launch of each kernel together with the
 SHA-256 of the sources the aggregation kernel is compiled from;
 ``bench.py`` reports that traffic only while those sources are unchanged.
+``pass`` does the same for a whole multi-launch pass (a schedule forward or
+backward run once after one copy): it sums the calibrated bytes of every
+dispatch after the last copy and sets them against the pass's algorithmic
+bytes, with a per-kernel breakdown.
 """
 
 from __future__ import annotations
@@ -143,6 +151,53 @@ def counters_summary(runs, T: int, d: int, S: int):
     }
 
 
+def _per_dispatch(csv_path: str, counter: str):
+    """[(dispatch id, short kernel name, value)] in dispatch order."""
+    rows = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows[int(r["Dispatch_Id"])] = (_short(r["Kernel_Name"]), float(r["Counter_Value"]))
+    return [(i, n, v) for i, (n, v) in sorted(rows.items())]
+
+
+def pass_summary(fetch_csv: str, write_csv: str, fetch_cmd: str, write_cmd: str, T: int, d: int,
+                 algorithmic: int, label: str):
+    """Counter bytes of every dispatch after the last plain copy (one pass of a
+    multi-launch workload), calibrated by that copy, against ``algorithmic``."""
+    kib = 1024.0
+    copy_bytes = 2 * T * d
+    per_kernel, calib = collections.OrderedDict(), {}
+    total = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = _per_dispatch(path, counter)
+        copies = [k for k, (_, n, _) in enumerate(disp) if n == COPY_KERNEL]
+        if not copies:
+            raise SystemExit(f"{path}: no {COPY_KERNEL} dispatch to calibrate {counter} with")
+        scale = copy_bytes / (disp[copies[-1]][2] * kib)
+        calib[counter] = scale
+        after = disp[copies[-1] + 1:]
+        total[counter] = sum(v for _, _, v in after) * kib * scale
+        for _, name, v in after:
+            e = per_kernel.setdefault(name, {"launches": 0, "FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0})
+            e[counter] += v * kib * scale
+            if counter == "FETCH_SIZE":
+                e["launches"] += 1
+    traffic = total["FETCH_SIZE"] + total["WRITE_SIZE"]
+    return {
+        "workload": label, "T": T, "d": d,
+        "commands": {"FETCH_SIZE": fetch_cmd, "WRITE_SIZE": write_cmd},
+        "copy_calibration": {"kernel": COPY_KERNEL, "bytes_moved_each_way": copy_bytes,
+                             "fetch_scale": calib["FETCH_SIZE"], "write_scale": calib["WRITE_SIZE"]},
+        "pass": {"fetch_bytes": total["FETCH_SIZE"], "write_bytes": total["WRITE_SIZE"], "traffic_bytes": traffic,
+                 "algorithmic_bytes": algorithmic, "traffic_over_algorithmic": traffic / algorithmic,
+                 "launches": sum(e["launches"] for e in per_kernel.values())},
+        "kernels": {n: {"launches": e["launches"], "fetch_bytes": e["FETCH_SIZE"], "write_bytes": e["WRITE_SIZE"]}
+                    for n, e in sorted(per_kernel.items(), key=lambda kv: -(kv[1]["FETCH_SIZE"] +
+                                                                            kv[1]["WRITE_SIZE"]))},
+    }
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="what", required=True)
@@ -160,7 +215,19 @@ def main():
     c.add_argument("--d", type=int, default=7168)
     c.add_argument("--S", type=int, default=9)
     c.add_argument("--out", required=True)
+    q = sub.add_parser("pass")
+    for flag in ("--fetch", "--write", "--fetch-cmd", "--write-cmd", "--label", "--out"):
+        q.add_argument(flag, required=True)
+    q.add_argument("--T", type=int, required=True)
+    q.add_argument("--d", type=int, default=7168)
+    q.add_argument("--algorithmic", type=int, required=True, help="algorithmic bytes of one pass")
     a = p.parse_args()
+    if a.what == "pass":
+        s = pass_summary(a.fetch, a.write, a.fetch_cmd, a.write_cmd, a.T, a.d, a.algorithmic, a.label)
+        with open(a.out, "w") as f:
+            json.dump(s, f, indent=1)
+            f.write("\n")
+        return
     if a.what == "trace":
         stats = kernel_stats_from_db(a.db) if a.db else kernel_stats_from_csv(a.csv)
         disp = dispatch_durations(a.dispatches[0], a.dispatches[1], int(a.dispatches[2])) if a.dispatches else None
