@@ -55,7 +55,7 @@ def parse():
                         "Infinity Cache -- else 1)")
     p.add_argument("--with-copy", action="store_true",
                    help="also run one plain copy of T*d bf16 before each step, outside the timed region "
-                        "(reference kernel for the HBM byte counters; not with full_s94)")
+                        "(reference kernel for the HBM byte counters)")
     return p.parse_args()
 
 
@@ -270,10 +270,10 @@ def main():
                "step": ("one fused launch: partial += layer output, then aggregate over 9 sources" if fused else
                         "attnres_accumulate (partial += layer output), then attnres_aggregate over 9 sources")}
     copy_store = copy_src = None
-    if args.with_copy and args.workload != "full_s94":
+    if args.with_copy:
         copy_store = binding.SourceStore(T, wl.d, s_max=2, dtype=torch.bfloat16, device=dev)
         copy_src = {"schedule_93": lambda: wl.F[0], "schedule_93_backward": lambda: wl.fwd.F[0],
-                    "backward_t32768": lambda: wl.g}.get(args.workload, lambda: wl.F)()
+                    "backward_t32768": lambda: wl.g, "full_s94": lambda: wl.H[0]}.get(args.workload, lambda: wl.F)()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     print(f"# setup {setup_s:.1f} s: workload {cfg['workload']} T={T} fused={fused}", file=sys.stderr, flush=True)
