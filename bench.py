@@ -74,6 +74,21 @@ def counter_traffic(kernel: str, T: int):
     return None if k is None else k.get("traffic_bytes_per_launch")
 
 
+def pass_traffic(label: str, T: int):
+    """HBM bytes of one whole pass from its committed counter summary
+    (``profiles/<label>_counters.json``), if it was taken on the current
+    sources at this T; else None."""
+    from depth_wise_attention_block_amd.profiling import pass_source_digest
+    try:
+        with open(os.path.join(REPO, "profiles", f"{label}_counters.json")) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") is None or c.get("source_sha256") != pass_source_digest(label) or c.get("T") != T:
+        return None
+    return c.get("pass", {}).get("traffic_bytes")
+
+
 def cpu_baseline(wl, budget_s: float, seed: int):
     """The oracle, as it is, on a bounded token sample of the same step."""
     import numpy as np
@@ -342,8 +357,11 @@ def main():
         ms_step = (sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events) if copy_store is not None
                    else wall * 1e3 / args.steps)
         achieved = step_bytes / (ms_step * 1e-3) / 1e9
+        label = {"schedule_93": "schedule_93_t32768_two_phase",
+                 "schedule_93_backward": "schedule_93_t32768_backward"}[args.workload]
+        counted = args.workload == "schedule_93_backward" or sched_mode == "two_phase"
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": pass_traffic(label, T) if counted else None,
                 "kernel": "whole schedule (all launches of one pass)", "bytes_per_launch": step_bytes}
         detail["step_gb"] = step_bytes / 1e9
     elif args.workload in ("full_s94", "backward_t32768"):
@@ -353,7 +371,8 @@ def main():
         kernel = {"full_s94": "aggregate_many_kernel<true, 2>",
                   "backward_t32768": "aggregate_backward_kernel<true, 2> + reduce_rows_kernel"}[args.workload]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": pass_traffic("many_sources_s94_t32768", T) if args.workload == "full_s94" else None,
                 "kernel": kernel, "bytes_per_launch": step_bytes, "avg_launch_ms": round(dom_ms, 4)}
     else:
         dom_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)

@@ -35,12 +35,30 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 AGG_SOURCES = tuple(os.path.join(HERE, "csrc", f) for f in ("aggregate.hip", "device_common.h", "internal.h"))
 
 
-def aggregate_source_digest() -> str:
+# every file the kernels of one whole pass are compiled from
+PASS_SOURCES = {
+    "schedule_93_t32768_two_phase": ("aggregate.hip", "twophase.hip", "device_common.h", "internal.h"),
+    "schedule_93_t32768_backward": ("backward.hip", "device_common.h", "internal.h"),
+    "many_sources_s94_t32768": ("aggregate.hip", "device_common.h", "internal.h"),
+}
+
+
+def source_digest(paths) -> str:
     h = hashlib.sha256()
-    for path in AGG_SOURCES:
+    for path in paths:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def aggregate_source_digest() -> str:
+    return source_digest(AGG_SOURCES)
+
+
+def pass_source_digest(label: str):
+    """SHA-256 of the sources of the pass ``label``, or None for an unknown pass."""
+    files = PASS_SOURCES.get(label)
+    return None if files is None else source_digest(os.path.join(HERE, "csrc", f) for f in files)
 
 COPY_KERNEL = "accumulate_kernel<true, true>"
 
@@ -186,6 +204,8 @@ def pass_summary(fetch_csv: str, write_csv: str, fetch_cmd: str, write_cmd: str,
     traffic = total["FETCH_SIZE"] + total["WRITE_SIZE"]
     return {
         "workload": label, "T": T, "d": d,
+        "sources": [f"depth_wise_attention_block_amd/csrc/{f}" for f in PASS_SOURCES.get(label, ())],
+        "source_sha256": pass_source_digest(label),
         "commands": {"FETCH_SIZE": fetch_cmd, "WRITE_SIZE": write_cmd},
         "copy_calibration": {"kernel": COPY_KERNEL, "bytes_moved_each_way": copy_bytes,
                              "fetch_scale": calib["FETCH_SIZE"], "write_scale": calib["WRITE_SIZE"]},

@@ -49,3 +49,21 @@ def test_pass_summary_needs_a_copy(tmp_path):
     _write(tmp_path / "w.csv", "WRITE_SIZE", [("k_a(x)", 1.0)])
     with pytest.raises(SystemExit):
         P.pass_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "", "", T, D, 1, "x")
+
+
+@pytest.mark.parametrize("label", ["schedule_93_t32768_two_phase", "schedule_93_t32768_backward",
+                                   "many_sources_s94_t32768"])
+def test_bench_reports_pass_traffic_only_on_the_sources_it_was_taken_on(label):
+    """``bench.pass_traffic``: the committed summary's bytes while the sources
+    its kernels are built from are unchanged (their SHA-256 is recorded), else
+    None; never at another T."""
+    import json
+    import os
+
+    import bench
+    with open(os.path.join(os.path.dirname(bench.__file__), "profiles", f"{label}_counters.json")) as f:
+        c = json.load(f)
+    current = c["source_sha256"] == P.pass_source_digest(label)
+    expected = c["pass"]["traffic_bytes"] if current else None
+    assert bench.pass_traffic(label, 32768) == expected
+    assert bench.pass_traffic(label, 4096) is None
