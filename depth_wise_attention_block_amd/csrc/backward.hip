@@ -72,11 +72,21 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&e)[Elems<kBf16>::kE]) {
   }
 }
 
-// A float32 gradient row leaves as kGv 16-byte pieces per lane, piece h of
-// vector idx at (idx * kGv + h).  With kGv = 2 one store instruction covers
-// every other 16 bytes of its lines; non-temporal stores of the two halves of a
-// line are not merged in L2 and each half goes to HBM as its own write (about
-// twice the write traffic), while plain stores are merged there first.
+// A float32 gradient row moves as kGv 16-byte pieces per lane, piece h of
+// vector idx at (idx * kGv + h).  With kGv = 2 one instruction covers every
+// other 16 bytes of its lines; non-temporal stores of the two halves of a line
+// are not merged in L2 and each half goes to HBM as its own write (about twice
+// the write traffic), while plain stores are merged there first.  The old row
+// of a read-modify-write is read with plain loads as well, which measured
+// faster than non-temporal ones.
+template <int kGv>
+__device__ __forceinline__ f32x4 load_grad_piece(const f32x4* p) {
+  if constexpr (kGv == 1)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 template <int kGv>
 __device__ __forceinline__ void store_grad_piece(f32x4 v, f32x4* p) {
   if constexpr (kGv == 1)
@@ -240,7 +250,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
         for (int h = 0; h < kGv; ++h) {
           o[v][h] = f32x4{0.f, 0.f, 0.f, 0.f};
           if (add && idx < nvec)
-            o[v][h] = __builtin_nontemporal_load(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+            o[v][h] = load_grad_piece<kGv>(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
         }
       }
     };
@@ -431,7 +441,7 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
           oldl[v][h] = f32x4{0.f, 0.f, 0.f, 0.f};
           if (add && idx < nvec)
             oldl[v][h] =
-                __builtin_nontemporal_load(grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+                load_grad_piece<kGv>(grad + (S - 1) * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
         }
       }
     }
@@ -574,7 +584,7 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
           for (int h = 0; h < kGv; ++h) {
             f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
             if ((acc_mask >> s) & 1u)
-              o = __builtin_nontemporal_load(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
+              o = load_grad_piece<kGv>(grad + s * grad_stride_v + (t * (int64_t)nvec + idx) * kGv + h);
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[s][4 * h + c] = fmaf(-c3, xe[4 * h + c], o[c]);
           }
