@@ -44,7 +44,7 @@ class attnres_store_t(ctypes.Structure):
 
 class attnres_launch_t(ctypes.Structure):
     _fields_ = [("threads", ctypes.c_int32), ("vecs_per_lane", ctypes.c_int32), ("grid", ctypes.c_int64),
-                ("tokens_per_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("tokens_per_group", ctypes.c_int32), ("xcd_run", ctypes.c_int32)]
 
 
 _SIGNATURES = {
@@ -154,7 +154,7 @@ def aggregate_config(S: int, T: int, d: int, dtype=torch.bfloat16, num_cus: int 
     _check("attnres_aggregate_config",
            lib().attnres_aggregate_config(S, T, d, _DTYPE_CODE[dtype], num_cus, ctypes.byref(cfg)))
     return {"threads": cfg.threads, "vecs_per_lane": cfg.vecs_per_lane, "grid": cfg.grid,
-            "tokens_per_group": cfg.tokens_per_group}
+            "tokens_per_group": cfg.tokens_per_group, "xcd_run": cfg.xcd_run}
 
 
 def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,

@@ -65,7 +65,7 @@ template <bool kBf16, int kV, int kUpdate, int kMaxS>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_s<kV, kMaxS>())))
 aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
-                 float eps, float inv_d, const u32x4* __restrict__ layer_out) {
+                 float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t span, int run_log2) {
   // [buffer][wave][sum of squares | w.x][source]
   __shared__ float red[2][kMaxWaves][2][16];
 
@@ -76,11 +76,16 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   const int nwaves = nthr >> 6;
   const int s16 = lane & 15;  // source handled by this lane in the softmax step
 
+  // a workgroup of a one-trip grid whose token is past the end has nothing to do
+  if (gridDim.x >= span && xcd_token(blockIdx.x, run_log2) >= T) return;
+
   Query<kBf16, kV> q;
   load_query<kBf16, kV>(q, w, nvec, tid, nthr);
 
   int buf = 0;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+  for (int64_t b = blockIdx.x; b < span; b += gridDim.x, buf ^= 1) {
+    const int64_t t = xcd_token(b, run_log2);
+    if (t >= T) continue;
     u32x4* tok = src + t * (int64_t)nvec;
     const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxS;  // the updated slot, if any
 
@@ -418,10 +423,13 @@ template <bool kBf16, int kV, int kUpdate, int kMaxS>
 hipError_t launch_s(const AggregateArgs& a, hipStream_t stream) {
   const int epv = kBf16 ? 8 : 4;
   const int nvec = a.d / epv;
+  const int run_log2 = __builtin_ctz((unsigned)a.xcd_run);
+  const int64_t span = (a.T + 8 * (int64_t)a.xcd_run - 1) / (8 * (int64_t)a.xcd_run) * (8 * (int64_t)a.xcd_run);
+  if ((a.xcd_run & (a.xcd_run - 1)) != 0 || (a.xcd_run > 1 && a.grid % 8 != 0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS>), dim3((unsigned)a.grid), dim3(a.threads), 0,
                      stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
                      a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
-                     static_cast<const u32x4*>(a.layer_out));
+                     static_cast<const u32x4*>(a.layer_out), a.xcd_run > 1 ? span : a.T, run_log2);
   return hipGetLastError();
 }
 

@@ -50,7 +50,17 @@ int check_shape(int64_t T, int32_t d, int32_t dtype) {
 // the smallest value that keeps the workgroup within kMaxWaves waves.  One
 // token per workgroup per trip; the grid covers every token up to a cap, past
 // which workgroups loop over tokens.
-int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus, attnres_launch_t* cfg) {
+//
+// With xcd_runs (the aggregation kernels), workgroups are dispatched to the 8
+// XCDs in turn, and each XCD takes runs of kXcdRun consecutive tokens instead
+// of every 8th token: the HBM traffic of one XCD then moves in runs of
+// kXcdRun rows of each source (measured at T = 262,144: 3% more bandwidth for
+// the aggregation and the fused step, results bit-identical).  Small batches
+// keep one token per XCD in turn, where runs would leave workgroups idle.
+constexpr int kXcdRunLog2 = 5;                  // runs of 32 tokens
+constexpr int64_t kXcdRunMinTokens = 4096;      // from this batch size on
+int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus, attnres_launch_t* cfg,
+                bool xcd_runs = false) {
   const int nvec = d / elems_per_vec(dtype);
   const int max_threads = 64 * attnres::kMaxWaves;
   const int v = (nvec + max_threads - 1) / max_threads;
@@ -58,10 +68,11 @@ int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus,
   const int lanes = (nvec + v - 1) / v;
   cfg->threads = (lanes + 63) / 64 * 64;
   cfg->vecs_per_lane = v;
-  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 4096;
-  cfg->grid = T < cap ? T : cap;
+  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 4096;  // a multiple of 8
+  cfg->xcd_run = (xcd_runs && T >= kXcdRunMinTokens) ? (1 << kXcdRunLog2) : 1;
+  const int64_t span = cfg->xcd_run > 1 ? (T + 8 * cfg->xcd_run - 1) / (8 * cfg->xcd_run) * (8 * cfg->xcd_run) : T;
+  cfg->grid = span < cap ? span : cap;
   cfg->tokens_per_group = 1;
-  cfg->reserved = 0;
   (void)S;
   return ATTNRES_OK;
 }
@@ -125,7 +136,7 @@ ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_
   if (S < 1 || S > ATTNRES_MAX_SOURCES_FULL) return ATTNRES_EINVAL;
   const int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
-  return pick_config(S, T, d, dtype, num_cus, cfg);
+  return pick_config(S, T, d, dtype, num_cus, cfg, S <= ATTNRES_MAX_SOURCES);
 }
 
 ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
@@ -159,7 +170,7 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
   rc = device_cus(&cus);
   if (rc != ATTNRES_OK) return rc;
   attnres_launch_t cfg;
-  rc = pick_config(S, T, d, dtype, cus, &cfg);
+  rc = pick_config(S, T, d, dtype, cus, &cfg, S <= ATTNRES_MAX_SOURCES);
   if (rc != ATTNRES_OK) return rc;
 
   attnres::AggregateArgs a;
@@ -176,6 +187,7 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
   a.threads = cfg.threads;
   a.vecs_per_lane = cfg.vecs_per_lane;
   a.grid = cfg.grid;
+  a.xcd_run = cfg.xcd_run;
   (void)hipGetLastError();  // start from a clean error state
   return attnres::launch_aggregate(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                       : ATTNRES_ELAUNCH;
@@ -486,7 +498,7 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
     rc = device_cus(&cus);
     if (rc != ATTNRES_OK) return rc;
     attnres_launch_t cfg;
-    rc = pick_config(S, T, d, st->dtype, cus, &cfg);
+    rc = pick_config(S, T, d, st->dtype, cus, &cfg, true);
     if (rc != ATTNRES_OK) return rc;
     attnres::AggregateArgs a;
     a.sources = st->base;
@@ -502,6 +514,7 @@ ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* la
     a.threads = cfg.threads;
     a.vecs_per_lane = cfg.vecs_per_lane;
     a.grid = cfg.grid;
+    a.xcd_run = cfg.xcd_run;
     a.update = st->partial_valid ? attnres::AggregateArgs::kAddUpdate : attnres::AggregateArgs::kCopyUpdate;
     a.layer_out = layer_out;
     (void)hipGetLastError();

@@ -34,6 +34,14 @@ __device__ __forceinline__ u32x4 add_rows(u32x4 p, u32x4 f, bool bf16) {
   return r;
 }
 
+// Token of virtual workgroup index b when each of the 8 XCDs (workgroup b runs
+// on XCD b % 8) takes runs of 2^run_log2 consecutive tokens in turn.  A
+// bijection of [0, T rounded up to 8 * 2^run_log2); run_log2 = 0 is b itself.
+__device__ __forceinline__ int64_t xcd_token(int64_t b, int run_log2) {
+  const int64_t x = b & 7, k = b >> 3;
+  return ((((k >> run_log2) << 3) | x) << run_log2) | (k & ((INT64_C(1) << run_log2) - 1));
+}
+
 // ---- DPP helpers (GFX9 data-parallel primitives inside one wave) -----------
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]

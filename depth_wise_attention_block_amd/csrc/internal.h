@@ -32,7 +32,8 @@ struct AggregateArgs {
   bool bf16;
   int threads;          // multiple of 64, <= 64*kMaxWaves
   int vecs_per_lane;    // 1..kMaxVecsPerLane
-  int64_t grid;
+  int64_t grid;         // a multiple of 8 when xcd_run > 1
+  int xcd_run = 1;      // tokens per XCD run, a power of two (see xcd_token)
   // Fused partial-sum update of the last source (index S-1) before use:
   // kCopyUpdate: slot = layer_out; kAddUpdate: slot = slot + layer_out.
   enum Update { kNoUpdate = 0, kCopyUpdate = 1, kAddUpdate = 2 };

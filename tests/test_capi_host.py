@@ -101,12 +101,47 @@ def test_launch_shape_policy(lib, S, T, d, dtype, threads, vpl):
     epv = 8 if dtype == B.BF16 else 4
     assert cfg["threads"] * cfg["vecs_per_lane"] >= d // epv  # every vector has a lane
     assert cfg["threads"] % 64 == 0 and cfg["threads"] <= 512
-    assert cfg["grid"] == min(T, 256 * 4096) and cfg["tokens_per_group"] == 1
+    run = 32 if (T >= 4096 and S <= 9) else 1
+    span = -(-T // (8 * run)) * 8 * run if run > 1 else T
+    assert cfg["grid"] == min(span, 256 * 4096) and cfg["tokens_per_group"] == 1 and cfg["xcd_run"] == run
 
 
 def test_launch_grid_caps_and_loops(lib):
     cfg = B.aggregate_config(2, 5_000_000, 8, B.torch.bfloat16, 256)
-    assert cfg["grid"] == 256 * 4096
+    assert cfg["grid"] == 256 * 4096 and cfg["xcd_run"] == 32
+
+
+@pytest.mark.parametrize("T,run,grid", [
+    (4095, 1, 4095),              # small batches: one token per XCD in turn
+    (4096, 32, 4096),             # runs of 32 tokens per XCD
+    (4097, 32, 4096 + 256),       # the virtual range is T rounded up to 8 runs
+    (262144, 32, 262144),
+    (256 * 4096 + 1, 32, 256 * 4096),  # grid-stride beyond the cap (a multiple of 8)
+])
+def test_launch_xcd_runs(lib, T, run, grid):
+    cfg = B.aggregate_config(9, T, 7168, B.torch.bfloat16, 256)
+    assert cfg["xcd_run"] == run and cfg["grid"] == grid
+    assert run == 1 or cfg["grid"] % 8 == 0
+    # the many-source kernel keeps one token per workgroup in order
+    assert B.aggregate_config(10, T, 7168, B.torch.bfloat16, 256)["xcd_run"] == 1
+
+
+def xcd_token(b: int, run_log2: int) -> int:
+    """The device's token of virtual workgroup index b (restated for the host test)."""
+    x, k = b & 7, b >> 3
+    return ((((k >> run_log2) << 3) | x) << run_log2) | (k & ((1 << run_log2) - 1))
+
+
+@pytest.mark.parametrize("run_log2", [0, 1, 5])
+def test_xcd_token_map_is_a_bijection(run_log2):
+    span = 8 << run_log2
+    for rounds in (1, 3):
+        n = span * rounds
+        got = sorted(xcd_token(b, run_log2) for b in range(n))
+        assert got == list(range(n))
+        # each XCD's tokens come in runs of 2^run_log2 consecutive tokens
+        for b in range(0, n, 8):
+            assert xcd_token(b + 8, run_log2) - xcd_token(b, run_log2) in (1, 8 * (1 << run_log2) - (1 << run_log2) + 1)
 
 
 def _store(T=0, d=8, s_max=9, base=SRC, stride=0, dtype=B.BF16):
