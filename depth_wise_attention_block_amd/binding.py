@@ -141,6 +141,22 @@ def _stream(device: torch.device, stream) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
+def _same_gpu(dev: torch.device, *named) -> None:
+    """Every tensor argument of a launch must sit on the launch's GPU ``dev``:
+    the C ABI takes plain pointers, so a host tensor (or one on another GPU)
+    among device tensors would reach a kernel as a foreign address.  ``named``
+    holds ``(name, tensor-or-None)`` pairs; lists of tensors are checked item
+    by item."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, not {dev}")
+    for name, t in named:
+        items = t if isinstance(t, (list, tuple)) else (t,)
+        for i, x in enumerate(items):
+            if x is not None and x.device != dev:
+                label = f"{name}[{i}]" if isinstance(t, (list, tuple)) else name
+                raise ValueError(f"{label} must be on {dev}, the GPU of this launch, not on {x.device}")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     try:
         return _DTYPE_CODE[t.dtype]
@@ -169,6 +185,7 @@ def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None =
     if T > 0 and (sources.stride(2) != 1 or sources.stride(1) != d):
         raise ValueError("each source must be a contiguous [T, d] block")
     dev = sources.device
+    _same_gpu(dev, ("w", w), ("out", out), ("weights", weights))
     if out is None:
         out = torch.empty((T, d), dtype=sources.dtype, device=dev)
     if weights is None and want_weights:
@@ -210,6 +227,7 @@ def add_rows(a: torch.Tensor | None, b: torch.Tensor, out: torch.Tensor, stream=
     """``attnres_add_rows``: ``out = a + b`` as the partial-sum update forms it
     (``out = b`` when ``a`` is None); rows ``[T, d]``, contiguous."""
     T, d = b.shape
+    _same_gpu(b.device, ("a", a), ("out", out))
     for name, t in (("b", b), ("out", out)) + ((("a", a),) if a is not None else ()):
         if not t.is_contiguous() or t.dtype != b.dtype or tuple(t.shape) != (T, d) or t.device != b.device:
             raise ValueError(f"{name} must be a contiguous [T, d] tensor like b")
@@ -246,6 +264,8 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
                                     or last_source.numel() != T * d):
         raise ValueError("last_source must be a contiguous [T, d] tensor like the sources")
     dev = grad_sources.device
+    _same_gpu(dev, ("sources", sources), ("last_source", last_source), ("w", w), ("grad_out", grad_out),
+              ("coef", coef), ("grad_w", grad_w), ("grad_last", grad_last), ("workspace", workspace))
     if grad_sources.dtype != torch.float32:
         raise ValueError("grad_sources must be float32")
     if grad_w is None:
@@ -287,6 +307,7 @@ def partial_sums(layer_outs, out: torch.Tensor, stream=None) -> torch.Tensor:
     if count == 0 or out.dim() != 3 or out.shape[0] < count:
         raise ValueError("out must be [>= count, T, d]")
     _, T, d = out.shape
+    _same_gpu(out.device, ("layer_outs", list(layer_outs)))
     for F in layer_outs:
         if F.dtype != out.dtype or not F.is_contiguous() or tuple(F.shape) != (T, d):
             raise ValueError("each layer output must be a contiguous [T, d] tensor like out")
@@ -312,6 +333,8 @@ def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor
     if sources.shape != grad_sources.shape or len(queries) != Bl or len(grad_ws) != Bl:
         raise ValueError("sources must match grad_sources; one query and one dL/dw row per upstream gradient")
     dev = grad_sources.device
+    _same_gpu(dev, ("sources", sources), ("grad_outs", list(grad_outs)), ("queries", list(queries)),
+              ("coef", coef), ("grad_ws", list(grad_ws)), ("grad_last", grad_last), ("workspace", workspace))
     for name, t in (("sources", sources), ("grad_sources", grad_sources)):
         if T > 0 and (t.stride(2) != 1 or t.stride(1) != d):
             raise ValueError(f"each row of {name} must be a contiguous [T, d] block")
@@ -354,6 +377,7 @@ def split_queries(w: torch.Tensor, out: torch.Tensor | None = None, stream=None)
     if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w must be a contiguous float32 [n, d] tensor")
     n, d = w.shape
+    _same_gpu(w.device, ("out", out))
     shape = prepared_query_shape(n, d)
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=w.device)
@@ -427,6 +451,7 @@ class SourceStore:
             raise
 
     def accumulate(self, layer_out: torch.Tensor, finalize_block: bool = False, stream=None) -> None:
+        _same_gpu(self.slots.device, ("layer_out", layer_out))
         if layer_out.dtype != self.slots.dtype or layer_out.device != self.slots.device \
                 or not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d:
             raise ValueError("layer_out must be a contiguous [T, d] tensor like the store")
@@ -442,6 +467,7 @@ class SourceStore:
         """``attnres_accumulate_aggregate``: add ``layer_out`` into the current
         block (closing it if asked), then aggregate the live sources with the
         next layer's query ``w`` -- one kernel.  Returns ``(out, weights)``."""
+        _same_gpu(self.slots.device, ("layer_out", layer_out), ("w", w), ("out", out), ("weights", weights))
         if layer_out.dtype != self.slots.dtype or layer_out.device != self.slots.device \
                 or not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d:
             raise ValueError("layer_out must be a contiguous [T, d] tensor like the store")
@@ -476,6 +502,8 @@ class SourceStore:
         ``[B, T, K]`` float32 with ``K = 1 + n_completed`` after the close;
         ``weights0`` optional ``[T, K]``."""
         dev = self.slots.device
+        _same_gpu(dev, ("layer_out", layer_out), ("w_split", w_split), ("inter", inter), ("logits", logits),
+                  ("weights0", weights0))
         B = inter.shape[0] if inter.dim() == 3 else -1
         if w_split.dtype != torch.bfloat16 or tuple(w_split.shape) != prepared_query_shape(B, self.d) \
                 or not w_split.is_contiguous():
@@ -506,6 +534,8 @@ class SourceStore:
         ``[T, K]``) for this layer's query ``w``.  ``out`` may be ``inter``
         itself.  Returns ``(out, weights)``, weights ``[T, K + 1]``."""
         dev = self.slots.device
+        _same_gpu(dev, ("layer_out", layer_out), ("w", w), ("inter", inter), ("logits", logits), ("out", out),
+                  ("weights", weights))
         K = 1 + self.n_completed
         for name, t, dt, n in (("layer_out", layer_out, self.slots.dtype, self.T * self.d),
                                ("w", w, torch.float32, self.d), ("inter", inter, self.slots.dtype, self.T * self.d),

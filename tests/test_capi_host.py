@@ -394,6 +394,106 @@ def test_binding_refuses_host_tensors():
                                  workspace=torch.zeros(64, dtype=torch.float32), stream=stream)
 
 
+class _OnGpu:
+    """A host tensor that reports a GPU device: enough for the binding's
+    argument checks, which must refuse a call before any pointer reaches the
+    library.  Slicing keeps the disguise."""
+
+    def __init__(self, t):
+        self._t = t
+
+    @property
+    def device(self):
+        import torch
+        return torch.device("cuda", 0)
+
+    def __getitem__(self, k):
+        return _OnGpu(self._t[k])
+
+    def __getattr__(self, name):
+        return getattr(self._t, name)
+
+
+class _HostOnlyLib:
+    """The real library for its host-only calls; any launching entry point fails the test."""
+    HOST = {"attnres_store_init", "attnres_store_sources", "attnres_strerror", "attnres_version"}
+
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        if name in self.HOST:
+            return getattr(self._real, name)
+        raise AssertionError(f"{name} was called with a host tensor among its arguments")
+
+
+def _mixed_calls():
+    """(label, argument index, call) for every binding entry point that
+    launches work: call(k) disguises every tensor argument as a GPU tensor
+    except the k-th, which stays on the host."""
+    import torch
+    S, T, d, Bq = 3, 4, 16, 2
+    bf, f32 = torch.bfloat16, torch.float32
+
+    def mk(*shape, dtype=bf):
+        return torch.zeros(shape, dtype=dtype)
+
+    def pick(args, k):
+        return [a if i == k else (_OnGpu(a) if a is not None else None) for i, a in enumerate(args)]
+
+    calls = []
+
+    def add(label, args, fn):
+        for k in range(len(args)):
+            calls.append((label, k, lambda k=k, args=args, fn=fn: fn(*pick(args, k))))
+
+    add("aggregate", [mk(S, T, d), mk(d, dtype=f32), mk(T, d), mk(T, S, dtype=f32)],
+        lambda H, w, o, a: B.aggregate(H, w, o, a))
+    add("add_rows", [mk(T, d), mk(T, d), mk(T, d)], lambda a, b, o: B.add_rows(a, b, o))
+    add("aggregate_backward",
+        [mk(S - 1, T, d), mk(T, d), mk(d, dtype=f32), mk(T, d), mk(S, T, d, dtype=f32), mk(T, 3 * S, dtype=f32),
+         mk(d, dtype=f32), mk(T, d), mk(64, dtype=f32)],
+        lambda H, last, w, g, gs, cf, gw, gl, ws: B.aggregate_backward(
+            H, w, g, gs, last_source=last, defer=1, coef=cf, coef_stride=3 * S, grad_w=gw, grad_last=gl,
+            workspace=ws))
+    add("partial_sums", [mk(T, d), mk(T, d), mk(2, T, d)], lambda a, b, o: B.partial_sums([a, b], o))
+    add("block_backward",
+        [mk(S, T, d), mk(T, d), mk(T, d), mk(d, dtype=f32), mk(d, dtype=f32), mk(T, Bq, S, 3, dtype=f32),
+         mk(S, T, d, dtype=f32), mk(d, dtype=f32), mk(d, dtype=f32), mk(T, d), mk(64, dtype=f32)],
+        lambda H, g0, g1, w0, w1, cf, gs, dw0, dw1, gl, ws: B.block_backward(
+            H, [g0, g1], [w0, w1], cf, gs, [dw0, dw1], grad_last=gl, workspace=ws))
+    add("split_queries", [mk(Bq, d, dtype=f32), mk(*B.prepared_query_shape(Bq, d))],
+        lambda w, o: B.split_queries(w, o))
+
+    def store(slots):
+        st = B.SourceStore(T, d, s_max=4, slots=slots)
+        st.set_state(1, True)
+        return st
+
+    add("SourceStore.accumulate", [mk(4, T, d), mk(T, d)], lambda sl, F: store(sl).accumulate(F))
+    add("SourceStore.accumulate_aggregate", [mk(4, T, d), mk(T, d), mk(d, dtype=f32), mk(T, d), mk(T, 3, dtype=f32)],
+        lambda sl, F, w, o, a: store(sl).accumulate_aggregate(F, False, w, o, a))
+    add("SourceStore.block_prepare",
+        [mk(4, T, d), mk(T, d), mk(*B.prepared_query_shape(Bq, d)), mk(Bq, T, d), mk(Bq, T, 3, dtype=f32),
+         mk(T, 3, dtype=f32)],
+        lambda sl, F, ws, inter, lg, w0: store(sl).block_prepare(F, True, ws, inter, lg, w0))
+    add("SourceStore.block_merge",
+        [mk(4, T, d), mk(T, d), mk(d, dtype=f32), mk(T, d), mk(T, 2, dtype=f32), mk(T, d), mk(T, 3, dtype=f32)],
+        lambda sl, F, w, inter, lg, o, a: store(sl).block_merge(F, w, inter, lg, o, a))
+    return calls
+
+
+@pytest.mark.parametrize("label,k,call", _mixed_calls(), ids=lambda v: str(v) if not callable(v) else "")
+def test_binding_refuses_one_host_tensor_among_gpu_tensors(monkeypatch, label, k, call):
+    """Every launching entry point checks the device of every tensor argument:
+    one host tensor among (disguised) GPU tensors is refused with ValueError
+    before the library sees a pointer."""
+    real = B.lib()
+    monkeypatch.setattr(B, "lib", lambda: _HostOnlyLib(real))
+    with pytest.raises(ValueError, match="GPU|must be on"):
+        call()
+
+
 def test_c_client_checks_its_input_before_any_gpu_call(tmp_path):
     """The plain C caller refuses bad usage and a bad header before it makes
     any HIP call (so this runs without a GPU)."""
