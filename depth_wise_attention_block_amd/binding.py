@@ -15,7 +15,9 @@ import threading
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libattnres.so")
+# ATTNRES_LIBRARY names another build of the same ABI (the CPU tests point it at
+# the sanitized host-only build); by default the HIP library next to this file
+LIB_PATH = os.environ.get("ATTNRES_LIBRARY") or os.path.join(HERE, "libattnres.so")
 
 BF16, F32 = 0, 1
 MAX_SOURCES = 9            # Block AttnRes store slots

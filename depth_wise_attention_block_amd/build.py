@@ -17,6 +17,11 @@ REPO = os.path.dirname(HERE)
 LIB_NAME = "libattnres.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 PATTERN_BENCH = os.path.join(HERE, "pattern_bench")
+# host-only C ABI (argument checks, range arithmetic, store bookkeeping) under
+# AddressSanitizer + UndefinedBehaviorSanitizer, with launchers that launch
+# nothing: the CPU tests run the binding's host checks against it
+HOSTSAN_LIB = os.path.join(HERE, "libattnres_hostsan.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 CAPI_CLIENT = os.path.join(HERE, "capi_client")
 SOURCES = ("aggregate.hip", "accumulate.hip", "twophase.hip", "backward.hip", "capi.cpp")
 ARCH = "gfx950"
@@ -53,13 +58,41 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         print(log)
     os.replace(tmp, LIB_PATH)
     _compile([hipcc(), *HIP_FLAGS, *extra_flags, os.path.join(CSRC, "pattern_bench.hip")], PATTERN_BENCH, verbose)
-    # a plain C program that calls the library through the header alone
     rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    build_host_sanitized(rocm, verbose)
+    # a plain C program that calls the library through the header alone
     _compile([shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-I", os.path.join(REPO, "include"),
               "-I", os.path.join(rocm, "include"), os.path.join(CSRC, "capi_client.c"), "-L", HERE, "-lattnres",
               "-Wl,-rpath,$ORIGIN", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
               "-Wl,-rpath," + os.path.join(rocm, "lib")], CAPI_CLIENT, verbose)
     return LIB_PATH
+
+
+def build_host_sanitized(rocm: str, verbose: bool = False) -> str:
+    """capi.cpp + host_stubs.cpp with g++ (host code only, no .hip file) under
+    ASan/UBSan -> libattnres_hostsan.so.  Load it with the ASan runtime
+    preloaded (``sanitizer_env()``)."""
+    _compile([shutil.which("g++") or "g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", *SAN_FLAGS,
+              "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(REPO, "include"), "-I", CSRC,
+              "-I", os.path.join(rocm, "include"), os.path.join(CSRC, "capi.cpp"), os.path.join(CSRC, "host_stubs.cpp"),
+              "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")],
+             HOSTSAN_LIB, verbose)
+    return HOSTSAN_LIB
+
+
+def sanitizer_env(base=None) -> dict:
+    """Environment for a child process that loads libattnres_hostsan.so: the
+    binding pointed at it, the gcc ASan runtime loaded first (ahead of whatever
+    the environment already preloads), leak checking off (the Python process
+    itself is not instrumented), any report fatal."""
+    env = dict(os.environ if base is None else base)
+    gcc = shutil.which("gcc") or "gcc"
+    asan = subprocess.run([gcc, "-print-file-name=libasan.so"], stdout=subprocess.PIPE, text=True).stdout.strip()
+    env["LD_PRELOAD"] = (asan + " " + env["LD_PRELOAD"]).strip() if env.get("LD_PRELOAD") else asan
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:halt_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["ATTNRES_LIBRARY"] = HOSTSAN_LIB
+    return env
 
 
 def _compile(cmd, target: str, verbose: bool) -> None:
