@@ -1,11 +1,26 @@
-// Attainable-bandwidth probe for the aggregation's HBM access pattern.
+// Attainable-bandwidth probes for the aggregation's HBM access pattern.
 //
 // The aggregation reads S = 9 source rows of a token and writes one output row
-// (bf16, d = 7168): ~90% reads, ~10% writes, as 10 concurrent streams.  This
-// program times the same pattern with trivial arithmetic (xor), plus plain
-// streaming read / write / copy kernels, so the aggregation's achieved
-// bandwidth can be compared with what the memory system delivers for this
-// traffic mix on the same device.  Prints one JSON object.
+// (bf16, d = 7168): ~90% reads, ~10% writes, as 10 concurrent streams; the
+// fused step reads 10 rows and writes 2.  This program moves exactly those
+// bytes with trivial arithmetic (xor), in several structures, so that the
+// kernels' bandwidth can be set against what the memory system delivers for the
+// same traffic on the same device:
+//
+//   token_*   one workgroup (448 lanes x 2 vectors) per token, every load of
+//             the token issued at once -- the kernels' own structure, with
+//             their token order (XCD x = workgroup % 8 takes runs of 32
+//             consecutive tokens);
+//   token_*_rr  the same, one token per XCD in turn (the order before runs);
+//   chunk_*   one wave per 1 KiB chunk of every stream (64 lanes x 16 B), the
+//             chunks in order, so that consecutive KiB go to different XCDs;
+//             8 waves per CU (dynamic LDS caps the residency).  A per-token
+//             kernel cannot take this shape without exchanging partial sums
+//             across XCDs;
+//   chunk_*_g128  the same with each XCD taking runs of 128 chunks;
+//   stream_*  plain streams, one 16-byte vector per lane: read, write, copy.
+//
+// Prints one JSON object of GB/s (bytes moved / mean time over `reps` launches).
 //
 //   pattern_bench [T] [d] [reps]
 #include <hip/hip_runtime.h>
@@ -17,6 +32,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 448;
+constexpr int kRunLog2 = 5;  // the kernels' XCD run: 32 tokens
 
 #define CHECK(x)                                                                         \
   do {                                                                                   \
@@ -27,81 +43,86 @@ constexpr int kThreads = 448;
     }                                                                                    \
   } while (0)
 
-// One workgroup per token: 9 source rows in, one row out (or none).
-template <bool kWrite>
-__global__ void __launch_bounds__(kThreads)
-token_pattern(const u32x4* __restrict__ src, int64_t T, int nvec, u32x4* __restrict__ out, unsigned* sink) {
-  const int64_t t = blockIdx.x;
-  u32x4 x[9][2];
-#pragma unroll
-  for (int s = 0; s < 9; ++s)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int idx = v * kThreads + threadIdx.x;
-      x[s][v] = idx < nvec ? __builtin_nontemporal_load(src + (s * T + t) * nvec + idx) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    u32x4 o = x[0][v];
-#pragma unroll
-    for (int s = 1; s < 9; ++s) o ^= x[s][v];
-    const int idx = v * kThreads + threadIdx.x;
-    if (kWrite) {
-      if (idx < nvec) __builtin_nontemporal_store(o, out + t * nvec + idx);
-    } else if ((o.x ^ o.y ^ o.z ^ o.w) == 0x9e3779b9u) {
-      sink[0] = o.x;
-    }
-  }
+__device__ __forceinline__ u32x4 ld(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st(u32x4 v, u32x4* p) { __builtin_nontemporal_store(v, p); }
+
+// XCD b % 8 takes runs of 2^lg consecutive items (lg = 0: item b).
+__device__ __forceinline__ int64_t xcd_item(int64_t b, int lg) {
+  const int64_t x = b & 7, k = b >> 3;
+  return ((((k >> lg) << 3) | x) << lg) | (k & ((INT64_C(1) << lg) - 1));
 }
 
-// The fused step's pattern: 8 source rows + the partial row + the layer-output
-// row in, the partial row written back in place and one output row out.
+// One workgroup per token.  NR = 9: the 9 source rows; NR = 10: plus the layer
+// output.  NW = 0: nothing written; 1: the output row; 2: also source row 8
+// rewritten in place (the fused step's slot update).
+template <int NR, int NW>
 __global__ void __launch_bounds__(kThreads)
-fused_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ layer_out, int64_t T, int nvec,
-              u32x4* __restrict__ out) {
-  const int64_t t = blockIdx.x;
-  u32x4 x[10][2];
+token_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ lout, int64_t T, int nvec, u32x4* __restrict__ out,
+              unsigned* sink, int lg) {
+  const int64_t t = xcd_item(blockIdx.x, lg);
+  if (t >= T) return;
+  u32x4 x[NR][2];
 #pragma unroll
-  for (int s = 0; s < 10; ++s)
+  for (int s = 0; s < NR; ++s)
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int idx = v * kThreads + threadIdx.x;
-      const u32x4* row = s < 9 ? src + (s * T + t) * nvec : layer_out + t * nvec;
-      x[s][v] = idx < nvec ? __builtin_nontemporal_load(row + idx) : u32x4{0, 0, 0, 0};
+      const u32x4* row = s < 9 ? src + (s * T + t) * nvec : lout + t * nvec;
+      x[s][v] = idx < nvec ? ld(row + idx) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const int idx = v * kThreads + threadIdx.x;
-    const u32x4 p = x[8][v] ^ x[9][v];
+    u32x4 p = x[8][v];
+    if (NR == 10) p ^= x[9][v];
     u32x4 o = p;
 #pragma unroll
     for (int s = 0; s < 8; ++s) o ^= x[s][v];
     if (idx < nvec) {
-      __builtin_nontemporal_store(p, src + (8 * T + t) * nvec + idx);
-      __builtin_nontemporal_store(o, out + t * nvec + idx);
+      if (NW >= 1) st(o, out + t * nvec + idx);
+      if (NW == 2) st(p, src + (8 * T + t) * nvec + idx);
     }
+    if (NW == 0 && (o.x ^ o.y ^ o.z ^ o.w) == 0x9e3779b9u) sink[0] = o.x;
   }
 }
 
-__global__ void __launch_bounds__(256) stream_read(const u32x4* __restrict__ a, int64_t n, unsigned* sink) {
-  unsigned acc = 0;
-  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 1024) {
-    u32x4 v[4];
+// One wave per 1 KiB chunk: chunk c covers vectors [64 c, 64 c + 64) of every
+// stream (the streams are n vectors long).  Same NR / NW meaning as above.
+template <int NR, int NW>
+__global__ void __launch_bounds__(64)
+chunk_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ lout, int64_t n, int64_t nchunks,
+              u32x4* __restrict__ out, unsigned* sink, int lg) {
+  const int64_t c = xcd_item(blockIdx.x, lg);
+  if (c >= nchunks) return;
+  const int64_t i = c * 64 + threadIdx.x;
+  if (i >= n) return;
+  u32x4 x[NR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t j = i + u * 256;
-      v[u] = j < n ? __builtin_nontemporal_load(a + j) : u32x4{0, 0, 0, 0};
-    }
+  for (int s = 0; s < NR; ++s) x[s] = ld((s < 9 ? src + s * n : lout) + i);
+  u32x4 p = x[8];
+  if (NR == 10) p ^= x[9];
+  u32x4 o = p;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  if (acc == 0x9e3779b9u) sink[0] = acc;
+  for (int s = 0; s < 8; ++s) o ^= x[s];
+  if (NW >= 1) st(o, out + i);
+  if (NW == 2) st(p, src + 8 * n + i);
+  if (NW == 0 && (o.x ^ o.y ^ o.z ^ o.w) == 0x9e3779b9u) sink[0] = o.x;
 }
 
-__global__ void __launch_bounds__(256) stream_write(u32x4* __restrict__ b, int64_t n) {
-  const u32x4 v = {1u, 2u, 3u, 4u};
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    __builtin_nontemporal_store(v, b + i);
+// Plain streams, one vector per lane: MODE 0 read, 1 write, 2 copy.
+template <int MODE>
+__global__ void __launch_bounds__(256) stream(const u32x4* __restrict__ a, u32x4* __restrict__ b, int64_t n,
+                                              unsigned* sink) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  if (MODE == 0) {
+    const u32x4 v = ld(a + i);
+    if ((v.x ^ v.y ^ v.z ^ v.w) == 0x9e3779b9u) sink[0] = v.x;
+  } else if (MODE == 1) {
+    st(u32x4{1u, 2u, 3u, (unsigned)i}, b + i);
+  } else {
+    st(ld(a + i), b + i);
+  }
 }
 
 }  // namespace
@@ -115,18 +136,19 @@ int main(int argc, char** argv) {
     return 2;
   }
   const int nvec = (int)(d / 8);
-  const int64_t src_vecs = 9 * T * nvec, out_vecs = T * nvec;
+  const int64_t n = T * nvec;                  // vectors per stream
+  const int64_t nchunks = (n + 63) / 64;
   u32x4 *src = nullptr, *out = nullptr, *lout = nullptr;
   unsigned* sink = nullptr;
-  CHECK(hipMalloc(&src, src_vecs * 16));
-  CHECK(hipMalloc(&out, out_vecs * 16));
-  CHECK(hipMalloc(&lout, out_vecs * 16));
-  CHECK(hipMemset(lout, 2, out_vecs * 16));
+  CHECK(hipMalloc(&src, 9 * n * 16));
+  CHECK(hipMalloc(&out, n * 16));
+  CHECK(hipMalloc(&lout, n * 16));
   CHECK(hipMalloc(&sink, 64));
-  CHECK(hipMemset(src, 1, src_vecs * 16));
-  CHECK(hipMemset(out, 0, out_vecs * 16));
-  int cus = 0;
-  CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0));
+  CHECK(hipMemset(src, 1, 9 * n * 16));
+  CHECK(hipMemset(out, 0, n * 16));
+  CHECK(hipMemset(lout, 2, n * 16));
+  int max_lds = 0;
+  CHECK(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, 0));
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
@@ -142,17 +164,36 @@ int main(int argc, char** argv) {
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     return bytes / (ms / reps * 1e-3) / 1e9;
   };
-  const double row = (double)T * d * 2.0;
-  const int64_t grid = (int64_t)cus * 64;
-  const double mixed = gbps(10 * row, [&] { token_pattern<true><<<T, kThreads>>>(src, T, nvec, out, sink); });
-  const double ronly = gbps(9 * row, [&] { token_pattern<false><<<T, kThreads>>>(src, T, nvec, out, sink); });
-  const double fused = gbps(12 * row, [&] { fused_pattern<<<T, kThreads>>>(src, lout, T, nvec, out); });
-  const double rstream = gbps(9 * row, [&] { stream_read<<<grid, 256>>>(src, src_vecs, sink); });
-  const double wstream = gbps(row, [&] { stream_write<<<grid, 256>>>(out, out_vecs); });
-  std::printf("{\"T\": %lld, \"d\": %lld, \"reps\": %d, \"token_pattern_9r1w_gbps\": %.1f, "
-              "\"token_pattern_9r_gbps\": %.1f, \"fused_pattern_10r2w_gbps\": %.1f, \"stream_read_gbps\": %.1f, "
-              "\"stream_write_gbps\": %.1f}\n",
-              (long long)T, (long long)d, reps, mixed, ronly, fused, rstream, wstream);
+  const double row = (double)n * 16;
+  // token grids: T rounded up to 8 runs (workgroups past T return)
+  const int64_t run = INT64_C(1) << kRunLog2;
+  const unsigned g_tok = (unsigned)((T + 8 * run - 1) / (8 * run) * (8 * run));
+  const unsigned g_rr = (unsigned)T;
+  // chunk grids: the fine order covers nchunks; runs of 128 round up to 8 runs
+  const unsigned g_chunk = (unsigned)nchunks;
+  const unsigned g_chunk128 = (unsigned)((nchunks + 8 * 128 - 1) / (8 * 128) * (8 * 128));
+  const int lds8 = max_lds >= 20480 ? 20480 : 0;  // 160 KiB per CU / 20 KiB: 8 one-wave workgroups per CU
+  const double t9r1w = gbps(10 * row, [&] { token_pattern<9, 1><<<g_tok, kThreads>>>(src, lout, T, nvec, out, sink, kRunLog2); });
+  const double t9r = gbps(9 * row, [&] { token_pattern<9, 0><<<g_tok, kThreads>>>(src, lout, T, nvec, out, sink, kRunLog2); });
+  const double t10r2w = gbps(12 * row, [&] { token_pattern<10, 2><<<g_tok, kThreads>>>(src, lout, T, nvec, out, sink, kRunLog2); });
+  const double r9r1w = gbps(10 * row, [&] { token_pattern<9, 1><<<g_rr, kThreads>>>(src, lout, T, nvec, out, sink, 0); });
+  const double r10r2w = gbps(12 * row, [&] { token_pattern<10, 2><<<g_rr, kThreads>>>(src, lout, T, nvec, out, sink, 0); });
+  const double c9r1w = gbps(10 * row, [&] { chunk_pattern<9, 1><<<g_chunk, 64, lds8>>>(src, lout, n, nchunks, out, sink, 0); });
+  const double c10r2w = gbps(12 * row, [&] { chunk_pattern<10, 2><<<g_chunk, 64, lds8>>>(src, lout, n, nchunks, out, sink, 0); });
+  const double g9r1w = gbps(10 * row, [&] { chunk_pattern<9, 1><<<g_chunk128, 64, lds8>>>(src, lout, n, nchunks, out, sink, 7); });
+  const double g10r2w = gbps(12 * row, [&] { chunk_pattern<10, 2><<<g_chunk128, 64, lds8>>>(src, lout, n, nchunks, out, sink, 7); });
+  const unsigned g_st = (unsigned)((n + 255) / 256);
+  const double sread = gbps(row, [&] { stream<0><<<g_st, 256>>>(src, out, n, sink); });
+  const double swrite = gbps(row, [&] { stream<1><<<g_st, 256>>>(src, out, n, sink); });
+  const double scopy = gbps(2 * row, [&] { stream<2><<<g_st, 256>>>(src, out, n, sink); });
+  std::printf("{\"T\": %lld, \"d\": %lld, \"reps\": %d, "
+              "\"token_pattern_9r1w_gbps\": %.1f, \"token_pattern_9r_gbps\": %.1f, \"fused_pattern_10r2w_gbps\": %.1f, "
+              "\"token_rr_9r1w_gbps\": %.1f, \"token_rr_10r2w_gbps\": %.1f, "
+              "\"chunk_9r1w_gbps\": %.1f, \"chunk_10r2w_gbps\": %.1f, "
+              "\"chunk_g128_9r1w_gbps\": %.1f, \"chunk_g128_10r2w_gbps\": %.1f, "
+              "\"stream_read_gbps\": %.1f, \"stream_write_gbps\": %.1f, \"stream_copy_gbps\": %.1f}\n",
+              (long long)T, (long long)d, reps, t9r1w, t9r, t10r2w, r9r1w, r10r2w, c9r1w, c10r2w, g9r1w, g10r2w, sread,
+              swrite, scopy);
   CHECK(hipFree(lout));
   CHECK(hipFree(src));
   CHECK(hipFree(out));
