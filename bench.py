@@ -41,8 +41,6 @@ def parse():
                    choices=["prefill_t262144", "layer_t4096", "decode", "decode_93", "schedule_93", "full_s94",
                             "backward_t32768", "schedule_93_backward"])
     p.add_argument("--decode-T", type=int, default=64)
-    p.add_argument("--no-split", action="store_true",
-                   help="decode sizes: one workgroup per token instead of the split-row instance")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bounded oracle timing budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -292,7 +290,7 @@ def bench_decode_93(args, dev):
 
     from depth_wise_attention_block_amd import workloads
 
-    wl = workloads.Schedule(args.decode_T, seed=args.seed, device=dev, split=not args.no_split)
+    wl = workloads.Schedule(args.decode_T, seed=args.seed, device=dev)
     T = wl.T
     stream = torch.cuda.current_stream(dev)
 
@@ -318,7 +316,6 @@ def bench_decode_93(args, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode_93", "T": T, "d": wl.d, "layers": wl.layers, "block_size": wl.block_size,
-                   "split_row": wl.exchange is not None,
                    "step": "one decode pass through the 93-layer depth path (94 aggregations), replayed as a "
                            "HIP graph"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -398,11 +395,10 @@ def main():
     else:
         T = {"prefill_t262144": 262144, "layer_t4096": 4096, "decode": args.decode_T}[args.workload]
         rotate = args.rotate or (3 if args.workload == "layer_t4096" else 1)
-        wls = [workloads.LayerStep(T, seed=args.seed + k, device=dev, split=not args.no_split) for k in range(rotate)]
+        wls = [workloads.LayerStep(T, seed=args.seed + k, device=dev) for k in range(rotate)]
         wl = wls[0]
         step_bytes = wl.step_bytes(fused)
         cfg = {"workload": args.workload, "T": T, "d": wl.d, "S": 9, "input_sets": rotate,
-               "split_row": wl.exchange is not None,
                "step": ("one fused launch: partial += layer output, then aggregate over 9 sources" if fused else
                         "attnres_accumulate (partial += layer output), then attnres_aggregate over 9 sources")}
     copy_store = copy_src = None

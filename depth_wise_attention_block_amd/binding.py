@@ -25,7 +25,6 @@ MAX_SOURCES_FULL = 256     # one aggregation (Full AttnRes / sublayer granularit
 MAX_INTER_SOURCES = 8      # two-phase: inter-block sources per pass
 MAX_BLOCK_QUERIES = 16     # two-phase: layer queries per pass
 MAX_D_BF16, MAX_D_F32 = 16384, 8192   # widest rows (ATTNRES_MAX_D_BF16 / _F32)
-SPLIT_MAX_TOKENS = 256     # largest batch of the split-row instance (ATTNRES_SPLIT_MAX_TOKENS)
 OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
 
@@ -56,12 +55,6 @@ _SIGNATURES = {
     "attnres_aggregate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]),
-    "attnres_aggregate_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
-                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
-                                            ctypes.c_void_p]),
-    "attnres_exchange_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                              ctypes.POINTER(ctypes.c_int64)]),
     "attnres_store_init": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "attnres_store_sources": (ctypes.c_int, [ctypes.POINTER(attnres_store_t)]),
@@ -70,10 +63,6 @@ _SIGNATURES = {
     "attnres_accumulate_aggregate": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                                     ctypes.c_void_p]),
-    "attnres_accumulate_aggregate_ex": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p,
-                                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
-                                                       ctypes.c_void_p]),
     "attnres_block_prepare": (ctypes.c_int, [ctypes.POINTER(attnres_store_t), ctypes.c_void_p, ctypes.c_int32,
                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]),
@@ -186,44 +175,19 @@ def aggregate_config(S: int, T: int, d: int, dtype=torch.bfloat16, num_cus: int 
             "tokens_per_group": cfg.tokens_per_group, "xcd_run": cfg.xcd_run}
 
 
-def exchange_bytes(T: int, d: int, dtype=torch.bfloat16) -> int:
-    """``attnres_exchange_bytes``: workspace of the split-row (decode-size)
-    instance for T tokens of width d; 0 when T is outside 1..SPLIT_MAX_TOKENS."""
-    out = ctypes.c_int64()
-    _check("attnres_exchange_bytes", lib().attnres_exchange_bytes(T, d, _DTYPE_CODE[dtype], ctypes.byref(out)))
-    return out.value
-
-
-def new_exchange(T: int, d: int, dtype=torch.bfloat16, device="cuda") -> torch.Tensor | None:
-    """A zeroed exchange workspace for batches of up to T tokens of width d (the
-    split-row instance), or None when T is too large for it.  One per stream."""
-    n = exchange_bytes(T, d, dtype)
-    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
-
-
-def _exchange_args(exchange, dev):
-    if exchange is None:
-        return None, 0
-    if exchange.device != dev or not exchange.is_contiguous():
-        raise ValueError(f"exchange must be a contiguous tensor on {dev}")
-    return exchange.data_ptr(), exchange.numel() * exchange.element_size()
-
-
 def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None,
               weights: torch.Tensor | None = None, *, want_weights: bool = True, eps: float = 1e-5,
-              exchange: torch.Tensor | None = None, stream=None):
+              stream=None):
     """``attnres_aggregate`` on ``sources`` ``[S, T, d]`` (rows contiguous; any
     source stride), query ``w`` ``[d]`` float32.  Returns ``(out, weights)``;
-    ``weights`` is ``None`` when not wanted.  With ``exchange`` (see
-    :func:`new_exchange`) decode-size batches run the split-row instance
-    (``attnres_aggregate_ex``)."""
+    ``weights`` is ``None`` when not wanted."""
     if sources.dim() != 3:
         raise ValueError("sources must be [S, T, d]")
     S, T, d = sources.shape
     if T > 0 and (sources.stride(2) != 1 or sources.stride(1) != d):
         raise ValueError("each source must be a contiguous [T, d] block")
     dev = sources.device
-    _same_gpu(dev, ("w", w), ("out", out), ("weights", weights), ("exchange", exchange))
+    _same_gpu(dev, ("w", w), ("out", out), ("weights", weights))
     if out is None:
         out = torch.empty((T, d), dtype=sources.dtype, device=dev)
     if weights is None and want_weights:
@@ -238,11 +202,10 @@ def aggregate(sources: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None =
     if weights is not None and (weights.dtype != torch.float32 or weights.numel() != T * S):
         raise ValueError("weights must be float32 with T*S elements")
     stride = sources.stride(0) if S > 1 else T * d
-    xp, xn = _exchange_args(exchange, dev)
-    rc = lib().attnres_aggregate_ex(sources.data_ptr(), S, T, d, stride, w.data_ptr(), out.data_ptr(),
-                                    weights.data_ptr() if weights is not None else None, float(eps),
-                                    _dtype_code(sources), xp, xn, _stream(dev, stream))
-    _check("attnres_aggregate_ex", rc)
+    rc = lib().attnres_aggregate(sources.data_ptr(), S, T, d, stride, w.data_ptr(), out.data_ptr(),
+                                 weights.data_ptr() if weights is not None else None, float(eps),
+                                 _dtype_code(sources), _stream(dev, stream))
+    _check("attnres_aggregate", rc)
     return out, weights
 
 
@@ -498,20 +461,15 @@ class SourceStore:
                                       _stream(self.slots.device, stream))
         _check("attnres_accumulate", rc)
 
-    def aggregate(self, w: torch.Tensor, out=None, weights=None, *, want_weights=True, eps=1e-5, exchange=None,
-                  stream=None):
-        return aggregate(self.sources(), w, out, weights, want_weights=want_weights, eps=eps, exchange=exchange,
-                         stream=stream)
+    def aggregate(self, w: torch.Tensor, out=None, weights=None, *, want_weights=True, eps=1e-5, stream=None):
+        return aggregate(self.sources(), w, out, weights, want_weights=want_weights, eps=eps, stream=stream)
 
     def accumulate_aggregate(self, layer_out: torch.Tensor, finalize_block: bool, w: torch.Tensor, out=None,
-                             weights=None, *, want_weights=True, eps=1e-5, exchange=None, stream=None):
+                             weights=None, *, want_weights=True, eps=1e-5, stream=None):
         """``attnres_accumulate_aggregate``: add ``layer_out`` into the current
         block (closing it if asked), then aggregate the live sources with the
-        next layer's query ``w`` -- one kernel.  Returns ``(out, weights)``.
-        With ``exchange`` (:func:`new_exchange`) decode-size batches run the
-        split-row instance (``attnres_accumulate_aggregate_ex``)."""
-        _same_gpu(self.slots.device, ("layer_out", layer_out), ("w", w), ("out", out), ("weights", weights),
-                  ("exchange", exchange))
+        next layer's query ``w`` -- one kernel.  Returns ``(out, weights)``."""
+        _same_gpu(self.slots.device, ("layer_out", layer_out), ("w", w), ("out", out), ("weights", weights))
         if layer_out.dtype != self.slots.dtype or layer_out.device != self.slots.device \
                 or not layer_out.is_contiguous() or layer_out.numel() != self.T * self.d:
             raise ValueError("layer_out must be a contiguous [T, d] tensor like the store")
@@ -528,12 +486,11 @@ class SourceStore:
         if weights is not None and (weights.dtype != torch.float32 or weights.numel() != self.T * S
                                     or not weights.is_contiguous()):
             raise ValueError("weights must be a contiguous float32 tensor with T*S elements")
-        xp, xn = _exchange_args(exchange, dev)
-        rc = lib().attnres_accumulate_aggregate_ex(ctypes.byref(self._st), layer_out.data_ptr(),
-                                                   int(bool(finalize_block)), w.data_ptr(), out.data_ptr(),
-                                                   weights.data_ptr() if weights is not None else None, float(eps),
-                                                   xp, xn, _stream(dev, stream))
-        _check("attnres_accumulate_aggregate_ex", rc)
+        rc = lib().attnres_accumulate_aggregate(ctypes.byref(self._st), layer_out.data_ptr(), int(bool(finalize_block)),
+                                                w.data_ptr(), out.data_ptr(),
+                                                weights.data_ptr() if weights is not None else None, float(eps),
+                                                _stream(dev, stream))
+        _check("attnres_accumulate_aggregate", rc)
         return out, weights
 
     # ---- two-phase schedule -------------------------------------------------

@@ -61,40 +61,11 @@ constexpr int waves_per_simd_s() {
                                                   : kV == 1 ? 7 : kV == 2 ? 6 : kV == 3 ? 4 : 3;
 }
 
-// Split-row instance (kSplit): for decode-size batches, where one token per
-// workgroup leaves most of the device idle and the token's latency is what
-// counts, each token's row is cut into 1 KiB chunks (64 lanes x 16 bytes of
-// every source) and each chunk gets a one-wave workgroup of its own, on its own
-// CU.  A wave forms its chunk's per-source sum of squares and w.x, publishes
-// them to the token's record in the exchange workspace and reads every chunk's
-// record of its token; each lane then sums the chunks in chunk order (bitwise
-// reproducible), and the softmax and the weighted sum of the chunk follow as in
-// the per-token instance.  Workspace (all of it zero before first use, then
-// kept by the kernel itself, so nothing needs clearing between calls and a
-// captured graph replays correctly):
-//   header, 256 bytes: uint32 generation, uint32 finished workgroups of the
-//                      running launch, uint32 timeout flag (sticky);
-//   records:           [T][nchunk][32] uint64 -- lane L < S: sum of squares of
-//                      source L, lane 16 + L: its w.x; float bits in the low
-//                      half, tag = generation + 1 in the high half.
-// Value and tag are one 64-bit atomic object (agent scope, relaxed), so a wave
-// that sees this launch's tag in all of its token's records has their values;
-// the last workgroup to finish advances the generation for the next launch.
-// A wave only waits for the chunks of its own token, whose workgroups have
-// consecutive indices: workgroups are dispatched in index order, so every
-// chunk a wave waits for is already dispatched, and the wait is bounded (the
-// timeout flag records a wait that ran out).
-constexpr int kExchangeHeaderBytes = 256;
-constexpr int kRecordLanes = 32;
-constexpr unsigned kExchangeSpinLimit = 1u << 16;
-
-template <bool kBf16, int kV, int kUpdate, int kMaxS, bool kSplit>
-__global__ void __launch_bounds__(64 * kMaxWaves)
-__attribute__((amdgpu_waves_per_eu(kSplit ? 8 : waves_per_simd_s<kV, kMaxS>())))
+template <bool kBf16, int kV, int kUpdate, int kMaxS>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_s<kV, kMaxS>())))
 aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
-                 float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t span, int run_log2,
-                 void* __restrict__ exchange, int nchunk) {
+                 float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t span, int run_log2) {
   // [buffer][wave][sum of squares | w.x][source]
   __shared__ float red[2][kMaxWaves][2][16];
 
@@ -104,36 +75,18 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   const int wave = tid >> 6;
   const int nwaves = nthr >> 6;
   const int s16 = lane & 15;  // source handled by this lane in the softmax step
-  constexpr int kEpv = kBf16 ? 8 : 4;  // elements per 16-byte vector
 
-  // split: this workgroup is chunk j of token t_split; its vectors start at col0
-  int64_t t_split = 0;
-  int j = 0, col0 = 0;
-  unsigned* hdr = nullptr;
-  uint64_t* rec = nullptr;
-  unsigned gen = 0;
-  if constexpr (kSplit) {
-    t_split = blockIdx.x / nchunk;
-    j = (int)(blockIdx.x - t_split * nchunk);
-    col0 = j * 64;
-    hdr = static_cast<unsigned*>(exchange);
-    rec = reinterpret_cast<uint64_t*>(static_cast<char*>(exchange) + kExchangeHeaderBytes);
-    gen = __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    // a workgroup of a one-trip grid whose token is past the end has nothing to do
-    if (gridDim.x >= span && xcd_token(blockIdx.x, run_log2) >= T) return;
-  }
-  const int nv = nvec - col0;  // vectors of the row from col0 on
+  // a workgroup of a one-trip grid whose token is past the end has nothing to do
+  if (gridDim.x >= span && xcd_token(blockIdx.x, run_log2) >= T) return;
 
   Query<kBf16, kV> q;
-  load_query<kBf16, kV>(q, w + (int64_t)col0 * kEpv, nv, tid, nthr);
+  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
 
   int buf = 0;
-  for (int64_t b = kSplit ? 0 : blockIdx.x; b < (kSplit ? 1 : span); b += kSplit ? 1 : gridDim.x, buf ^= 1) {
-    const int64_t t = kSplit ? t_split : xcd_token(b, run_log2);
-    if (!kSplit && t >= T) continue;
-    u32x4* tok = src + t * (int64_t)nvec + col0;
-    const u32x4* lrow = layer_out + t * (int64_t)nvec + col0;
+  for (int64_t b = blockIdx.x; b < span; b += gridDim.x, buf ^= 1) {
+    const int64_t t = xcd_token(b, run_log2);
+    if (t >= T) continue;
+    u32x4* tok = src + t * (int64_t)nvec;
     const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxS;  // the updated slot, if any
 
     // 1. issue every load of this token: S sources x V vectors per lane (for
@@ -149,15 +102,15 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
           x[s][v] = u32x4{0, 0, 0, 0};
           if (s == s_upd) {
             if constexpr (kUpdate == kUpdateCopy) {
-              if (idx < nv) x[s][v] = __builtin_nontemporal_load(lrow + idx);
+              if (idx < nvec) x[s][v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
             } else {
               f[v] = u32x4{0, 0, 0, 0};
-              if (idx < nv) {
-                f[v] = __builtin_nontemporal_load(lrow + idx);
+              if (idx < nvec) {
+                f[v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
                 x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
               }
             }
-          } else if (idx < nv) {
+          } else if (idx < nvec) {
             x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
           }
         }
@@ -172,7 +125,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
           for (int v = 0; v < kV; ++v) {
             const int idx = v * nthr + tid;
             if constexpr (kUpdate == kUpdateAdd) x[s][v] = add_rows(x[s][v], f[v], kBf16);
-            if (idx < nv) __builtin_nontemporal_store(x[s][v], tok + s * src_stride_v + idx);
+            if (idx < nvec) __builtin_nontemporal_store(x[s][v], tok + s * src_stride_v + idx);
           }
         }
       }
@@ -207,74 +160,35 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
       }
     }
 
-    // 3. combine the parts of the row, then the logits (lanes s16 < S; split:
-    //    row 0 only)
-    float z = -INFINITY;
-    bool scored = s16 < S;
-    if constexpr (kSplit) {
-      // publish this chunk's sums, then gather every chunk's of the token
-      uint64_t* trec = rec + t * (int64_t)nchunk * kRecordLanes;
-      const unsigned tag = gen + 1u;
-      const bool mine = lane < S || (lane >= 16 && lane < 16 + S);
-      if (mine)
-        __hip_atomic_store(trec + j * kRecordLanes + lane,
-                           (uint64_t)__float_as_uint(lane < 16 ? gss : gdt) | ((uint64_t)tag << 32),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      float tot = 0.f;
-      if (mine) {
-        for (unsigned spins = 0;; ++spins) {
-          bool all = true;
-          float sum = 0.f;
-          for (int c = 0; c < nchunk; ++c) {
-            const uint64_t r = __hip_atomic_load(trec + c * kRecordLanes + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            all = all && (unsigned)(r >> 32) == tag;
-            sum += __uint_as_float((unsigned)r);
-          }
-          if (all) {
-            tot = sum;
-            break;
-          }
-          if (spins >= kExchangeSpinLimit) {
-            __hip_atomic_store(hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      const float dt_tot = __shfl_down(tot, 16);  // lane L < 16: source L's w.x
-      scored = lane < 16 && s16 < S;
-      if (scored) z = dt_tot / sqrtf(tot * inv_d + eps);
-    } else {
-      // one LDS exchange across the waves, one barrier
-      if (lane < 16) {
-        red[buf][wave][0][lane] = gss;
-        red[buf][wave][1][lane] = gdt;
-      }
-      __syncthreads();
-      if (s16 < S) {
-        float ss = 0.f, dt = 0.f;
-        for (int k = 0; k < nwaves; ++k) {
-          ss += red[buf][k][0][s16];
-          dt += red[buf][k][1][s16];
-        }
-        z = dt / sqrtf(ss * inv_d + eps);
-      }
+    // 3. combine the waves: one LDS exchange, one barrier
+    if (lane < 16) {
+      red[buf][wave][0][lane] = gss;
+      red[buf][wave][1][lane] = gdt;
     }
+    __syncthreads();
 
-    // 4. softmax over depth
+    // 4. logits and softmax over depth, lanes s16 < S of every row
+    float z = -INFINITY;
+    if (s16 < S) {
+      float ss = 0.f, dt = 0.f;
+      for (int k = 0; k < nwaves; ++k) {
+        ss += red[buf][k][0][s16];
+        dt += red[buf][k][1][s16];
+      }
+      z = dt / sqrtf(ss * inv_d + eps);
+    }
     const float m = row_max16(z);
-    const float p = scored ? expf(z - m) : 0.f;
+    const float p = (s16 < S) ? expf(z - m) : 0.f;
     const float l = row_sum16(p);
     const float a = p / l;
-    if (weights != nullptr && (kSplit ? j == 0 : wave == 0) && lane < S) weights[t * S + lane] = a;
+    if (weights != nullptr && wave == 0 && lane < S) weights[t * S + lane] = a;
 
     // 5. weighted sum of the raw sources in float32, one rounding to the output
     float as[kMaxS];
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) as[s] = (s < S) ? lane_bcast(a, s) : 0.f;
 
-    u32x4* orow = out + t * (int64_t)nvec + col0;
+    u32x4* orow = out + t * (int64_t)nvec;
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       const int idx = v * nthr + tid;
@@ -298,7 +212,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
         u32x4 o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-        if (idx < nv) __builtin_nontemporal_store(o, orow + idx);
+        if (idx < nvec) __builtin_nontemporal_store(o, orow + idx);
       } else {
         f32x4 acc = as[0] * __builtin_bit_cast(f32x4, x[0][v]);
 #pragma unroll
@@ -309,17 +223,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
             for (int k = 0; k < 4; ++k) acc[k] = fmaf(as[s], xf[k], acc[k]);
           }
         }
-        if (idx < nv) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, acc), orow + idx);
-      }
-    }
-  }
-  if constexpr (kSplit) {
-    // the last workgroup of the launch to get here advances the generation
-    if (lane == 0) {
-      const unsigned done = __hip_atomic_fetch_add(hdr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == gridDim.x - 1) {
-        __hip_atomic_store(hdr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(hdr, gen == 0xFFFFFFFEu ? 0u : gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (idx < nvec) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, acc), orow + idx);
       }
     }
   }
@@ -522,34 +426,15 @@ hipError_t launch_s(const AggregateArgs& a, hipStream_t stream) {
   const int run_log2 = __builtin_ctz((unsigned)a.xcd_run);
   const int64_t span = (a.T + 8 * (int64_t)a.xcd_run - 1) / (8 * (int64_t)a.xcd_run) * (8 * (int64_t)a.xcd_run);
   if ((a.xcd_run & (a.xcd_run - 1)) != 0 || (a.xcd_run > 1 && a.grid % 8 != 0)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS, false>), dim3((unsigned)a.grid), dim3(a.threads),
-                     0, stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
+  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS>), dim3((unsigned)a.grid), dim3(a.threads), 0,
+                     stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
                      a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
-                     static_cast<const u32x4*>(a.layer_out), a.xcd_run > 1 ? span : a.T, run_log2, nullptr, 0);
-  return hipGetLastError();
-}
-
-// The split-row instance: one 64-lane workgroup per 1 KiB chunk of each token.
-template <bool kBf16, int kUpdate, int kMaxS>
-hipError_t launch_split(const AggregateArgs& a, hipStream_t stream) {
-  const int epv = kBf16 ? 8 : 4;
-  const int nvec = a.d / epv;
-  const int nchunk = (nvec + 63) / 64;
-  if (a.exchange == nullptr || a.T * nchunk > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((aggregate_kernel<kBf16, 1, kUpdate, kMaxS, true>), dim3((unsigned)(a.T * nchunk)), dim3(64),
-                     0, stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
-                     a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
-                     static_cast<const u32x4*>(a.layer_out), a.T, 0, a.exchange, nchunk);
+                     static_cast<const u32x4*>(a.layer_out), a.xcd_run > 1 ? span : a.T, run_log2);
   return hipGetLastError();
 }
 
 template <bool kBf16, int kV, int kUpdate>
 hipError_t launch(const AggregateArgs& a, hipStream_t stream) {
-  if (a.exchange != nullptr) {
-    return a.S <= 2           ? launch_split<kBf16, kUpdate, 2>(a, stream)
-           : a.S <= kSmallSrc ? launch_split<kBf16, kUpdate, kSmallSrc>(a, stream)
-                              : launch_split<kBf16, kUpdate, kMaxSrc>(a, stream);
-  }
   return a.S <= 2           ? launch_s<kBf16, kV, kUpdate, 2>(a, stream)
          : a.S <= kSmallSrc ? launch_s<kBf16, kV, kUpdate, kSmallSrc>(a, stream)
                             : launch_s<kBf16, kV, kUpdate, kMaxSrc>(a, stream);
@@ -587,7 +472,6 @@ hipError_t launch_v(const AggregateArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream) {
-  if (a.exchange != nullptr && a.S > kMaxSrc) return hipErrorInvalidValue;
   if (a.S > kMaxSrc) {
     if (a.update != AggregateArgs::kNoUpdate || a.S > kMaxSourcesMany) return hipErrorInvalidValue;
     return launch_many_v(a, stream);

@@ -12,7 +12,6 @@
 static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
 static_assert(ATTNRES_MAX_INTER_SOURCES == attnres::kMaxInterSources, "inter-source limits disagree");
 static_assert(ATTNRES_MAX_BLOCK_QUERIES == attnres::kMaxBlockQueries, "query limits disagree");
-static_assert(ATTNRES_SPLIT_MAX_TOKENS == attnres::kSplitMaxTokens, "split-row limits disagree");
 
 namespace {
 
@@ -113,24 +112,6 @@ int check_store(const attnres_store_t* st) {
   return ATTNRES_OK;
 }
 
-// Checks of an exchange workspace: NULL (one workgroup per token), or 256-byte
-// aligned, large enough for T tokens of width d, clear of every other buffer.
-// *use is set when the split-row instance will run.
-int check_exchange(const void* exchange, int64_t exchange_bytes, int32_t S, int64_t T, int32_t d, int32_t dtype,
-                   const Range* others, int nothers, bool* use) {
-  *use = false;
-  if (exchange == nullptr) return exchange_bytes == 0 ? ATTNRES_OK : ATTNRES_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(exchange) & 255u) != 0) return ATTNRES_EUNSUPPORTED;
-  if (exchange_bytes < 0) return ATTNRES_EINVAL;
-  if (T < 1 || T > attnres::kSplitMaxTokens || S > ATTNRES_MAX_SOURCES) return ATTNRES_OK;  // not used
-  if (exchange_bytes < attnres::exchange_bytes(T, d, dtype == ATTNRES_BF16)) return ATTNRES_EINVAL;
-  const Range r_x = range(exchange, exchange_bytes);
-  for (int i = 0; i < nothers; ++i)
-    if (overlap(r_x, others[i])) return ATTNRES_EALIAS;
-  *use = true;
-  return ATTNRES_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -158,23 +139,9 @@ ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_
   return pick_config(S, T, d, dtype, num_cus, cfg, S <= ATTNRES_MAX_SOURCES);
 }
 
-ATTNRES_API int attnres_exchange_bytes(int64_t T, int32_t d, int32_t dtype, int64_t* bytes) {
-  if (bytes == nullptr) return ATTNRES_EINVAL;
-  const int rc = check_shape(T, d, dtype);
-  if (rc != ATTNRES_OK) return rc;
-  *bytes = (T >= 1 && T <= attnres::kSplitMaxTokens) ? attnres::exchange_bytes(T, d, dtype == ATTNRES_BF16) : 0;
-  return ATTNRES_OK;
-}
-
 ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
                                   const float* w, void* out, float* weights, float eps, int32_t dtype,
                                   void* stream) {
-  return attnres_aggregate_ex(sources, S, T, d, src_stride, w, out, weights, eps, dtype, nullptr, 0, stream);
-}
-
-ATTNRES_API int attnres_aggregate_ex(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
-                                     const float* w, void* out, float* weights, float eps, int32_t dtype,
-                                     void* exchange, int64_t exchange_bytes, void* stream) {
   if (S < 1 || S > ATTNRES_MAX_SOURCES_FULL) return ATTNRES_EINVAL;
   int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
@@ -194,12 +161,10 @@ ATTNRES_API int attnres_aggregate_ex(const void* sources, int32_t S, int64_t T, 
   const Range r_w = range(w, (int64_t)d * 4);
   const Range r_out = range(out, row * es);
   if (overlap(r_out, r_src) || overlap(r_out, r_w)) return ATTNRES_EALIAS;
-  const Range r_wt = weights != nullptr ? range(weights, T * (int64_t)S * 4) : Range{0, 0};
-  if (overlap(r_wt, r_src) || overlap(r_wt, r_w) || overlap(r_wt, r_out)) return ATTNRES_EALIAS;
-  const Range others[4] = {r_src, r_w, r_out, r_wt};
-  bool split = false;
-  rc = check_exchange(exchange, exchange_bytes, S, T, d, dtype, others, 4, &split);
-  if (rc != ATTNRES_OK) return rc;
+  if (weights != nullptr) {
+    const Range r_wt = range(weights, T * (int64_t)S * 4);
+    if (overlap(r_wt, r_src) || overlap(r_wt, r_w) || overlap(r_wt, r_out)) return ATTNRES_EALIAS;
+  }
 
   int cus = 0;
   rc = device_cus(&cus);
@@ -223,7 +188,6 @@ ATTNRES_API int attnres_aggregate_ex(const void* sources, int32_t S, int64_t T, 
   a.vecs_per_lane = cfg.vecs_per_lane;
   a.grid = cfg.grid;
   a.xcd_run = cfg.xcd_run;
-  a.exchange = split ? exchange : nullptr;
   (void)hipGetLastError();  // start from a clean error state
   return attnres::launch_aggregate(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                       : ATTNRES_ELAUNCH;
@@ -500,12 +464,6 @@ ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t coun
 
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                              const float* w, void* out, float* weights, float eps, void* stream) {
-  return attnres_accumulate_aggregate_ex(st, layer_out, finalize_block, w, out, weights, eps, nullptr, 0, stream);
-}
-
-ATTNRES_API int attnres_accumulate_aggregate_ex(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
-                                                const float* w, void* out, float* weights, float eps, void* exchange,
-                                                int64_t exchange_bytes, void* stream) {
   int rc = check_store(st);
   if (rc != ATTNRES_OK) return rc;
   if (finalize_block != 0 && finalize_block != 1) return ATTNRES_EINVAL;
@@ -519,7 +477,6 @@ ATTNRES_API int attnres_accumulate_aggregate_ex(attnres_store_t* st, const void*
   const int64_t T = st->T;
   const int d = st->d;
   const int64_t row = T * (int64_t)d;
-  bool split = false;
   if (row > 0) {
     if (layer_out == nullptr || w == nullptr || out == nullptr) return ATTNRES_EINVAL;
     if (!aligned16(layer_out) || !aligned16(w) || !aligned16(out)) return ATTNRES_EUNSUPPORTED;
@@ -532,12 +489,11 @@ ATTNRES_API int attnres_accumulate_aggregate_ex(attnres_store_t* st, const void*
     if (overlap(r_f, r_store) || overlap(r_out, r_store) || overlap(r_out, r_f) || overlap(r_out, r_w) ||
         overlap(r_w, r_store))
       return ATTNRES_EALIAS;
-    const Range r_wt = weights != nullptr ? range(weights, T * (int64_t)S * 4) : Range{0, 0};
-    if (overlap(r_wt, r_store) || overlap(r_wt, r_f) || overlap(r_wt, r_w) || overlap(r_wt, r_out))
-      return ATTNRES_EALIAS;
-    const Range others[5] = {r_store, r_f, r_w, r_out, r_wt};
-    rc = check_exchange(exchange, exchange_bytes, S, T, d, st->dtype, others, 5, &split);
-    if (rc != ATTNRES_OK) return rc;
+    if (weights != nullptr) {
+      const Range r_wt = range(weights, T * (int64_t)S * 4);
+      if (overlap(r_wt, r_store) || overlap(r_wt, r_f) || overlap(r_wt, r_w) || overlap(r_wt, r_out))
+        return ATTNRES_EALIAS;
+    }
     int cus = 0;
     rc = device_cus(&cus);
     if (rc != ATTNRES_OK) return rc;
@@ -561,7 +517,6 @@ ATTNRES_API int attnres_accumulate_aggregate_ex(attnres_store_t* st, const void*
     a.xcd_run = cfg.xcd_run;
     a.update = st->partial_valid ? attnres::AggregateArgs::kAddUpdate : attnres::AggregateArgs::kCopyUpdate;
     a.layer_out = layer_out;
-    a.exchange = split ? exchange : nullptr;
     (void)hipGetLastError();
     if (attnres::launch_aggregate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
   }

@@ -39,17 +39,7 @@ struct AggregateArgs {
   enum Update { kNoUpdate = 0, kCopyUpdate = 1, kAddUpdate = 2 };
   Update update = kNoUpdate;
   const void* layer_out = nullptr;  // [T][d], with update only
-  // Split-row instance (decode sizes): one 64-lane workgroup per 1 KiB chunk of
-  // each token's row, partial sums exchanged through this workspace (see
-  // aggregate_kernel); nullptr = one workgroup per token.
-  void* exchange = nullptr;
 };
-
-// Split-row exchange workspace: header and one record per (token, chunk).
-constexpr int kSplitMaxTokens = 256;        // largest batch the split instance takes (ATTNRES_SPLIT_MAX_TOKENS)
-constexpr int64_t exchange_bytes(int64_t T, int d, bool bf16) {
-  return 256 + T * ((d / (bf16 ? 8 : 4) + 63) / 64) * 32 * 8;
-}
 
 // Enqueue one aggregation; returns the hipError_t of the launch.
 hipError_t launch_aggregate(const AggregateArgs& a, hipStream_t stream);

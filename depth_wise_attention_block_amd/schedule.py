@@ -44,8 +44,7 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                  on_layer: Optional[Callable[[int, torch.Tensor, Optional[torch.Tensor]], None]] = None,
                  fused: bool = True, two_phase_from: Optional[int] = None,
                  inter: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                 queries_split: Optional[Sequence[Optional[torch.Tensor]]] = None, eps: float = 1e-5,
-                 exchange: Optional[torch.Tensor] = None):
+                 queries_split: Optional[Sequence[Optional[torch.Tensor]]] = None, eps: float = 1e-5):
     """Run every layer's aggregation and partial-sum update in stream order.
 
     Per layer one of:
@@ -74,9 +73,8 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     once since the queries are frozen parameters) saves the split per pass;
     ``block_queries_split`` builds that list.
     ``on_layer(l, r_l, a_l)`` runs after layer l's aggregation is enqueued
-    (1-based l).  ``exchange`` (:func:`new_exchange`) lets decode-size batches
-    run every one-launch aggregation in the split-row instance.  Returns the
-    output layer's ``(out, weights)`` when ``final_query`` is given, else None.
+    (1-based l).  Returns the output layer's ``(out, weights)`` when
+    ``final_query`` is given, else None.
     """
     num_layers = len(layer_outputs)
     if len(queries) != num_layers or num_layers == 0:
@@ -100,12 +98,12 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     if not fused:
         for l in range(1, num_layers + 1):
             r, a = rbuf(l), wview(l, store.num_sources())
-            aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps, exchange=exchange)
+            aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
             if on_layer is not None:
                 on_layer(l, r, a)
             store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
         if final_query is not None:
-            return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps, exchange=exchange)
+            return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
         return None
 
     num_blocks = (num_layers + block_size - 1) // block_size
@@ -150,18 +148,17 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
                               out=r, weights=a, want_weights=a is not None, eps=eps)
         elif l == 1:
             r, a = rbuf(l), wview(l, store.num_sources())
-            aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps, exchange=exchange)
+            aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
         else:
             closes = closes_block(l - 1, num_layers, block_size)
             S = 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
             r, a = rbuf(l), wview(l, S)
             store.accumulate_aggregate(layer_outputs[l - 2], closes, queries[l - 1], r, a,
-                                       want_weights=a is not None, eps=eps, exchange=exchange)
+                                       want_weights=a is not None, eps=eps)
         if on_layer is not None:
             on_layer(l, r, a)
     if final_query is not None:
-        return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps,
-                                          exchange=exchange)
+        return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps)
     store.accumulate(layer_outputs[-1], True)
     return None
 

@@ -28,16 +28,14 @@ from __future__ import annotations
 import torch
 
 from . import synth
-from .binding import MAX_SOURCES, SourceStore, new_exchange
+from .binding import MAX_SOURCES, SourceStore
 from .schedule import block_queries_split, closes_block, run_schedule
 
 
 class LayerStep:
     def __init__(self, T: int, d: int = 7168, *, seed: int = 0, device="cuda", scale=(0.5, 50.0),
-                 layer_out_std: float = 1.0, split: bool = True):
+                 layer_out_std: float = 1.0):
         self.T, self.d = T, d
-        # decode-size batches: the split-row instance's exchange workspace (None above its limit)
-        self.exchange = new_exchange(T, d, torch.bfloat16, device) if split else None
         self.store = SourceStore(T, d, s_max=MAX_SOURCES, dtype=torch.bfloat16, device=device)
         synth.sources(MAX_SOURCES, T, d, scale=scale, seed=seed, out=self.store.slots)
         self.store.set_state(MAX_SOURCES - 2, True)   # h0, b1..b7, partial
@@ -50,10 +48,10 @@ class LayerStep:
         self.store.accumulate(self.F, finalize_block=False)
 
     def aggregate(self):
-        self.store.aggregate(self.w, self.out, self.weights, exchange=self.exchange)
+        self.store.aggregate(self.w, self.out, self.weights)
 
     def fused(self):
-        self.store.accumulate_aggregate(self.F, False, self.w, self.out, self.weights, exchange=self.exchange)
+        self.store.accumulate_aggregate(self.F, False, self.w, self.out, self.weights)
 
     def step(self, fused: bool = True):
         if fused:
@@ -86,9 +84,8 @@ class Schedule:
     TWO_PHASE_FROM = 3
 
     def __init__(self, T: int, d: int = 7168, *, layers: int = 93, block_size: int = 12, seed: int = 0,
-                 device="cuda", h0_scale: float = 1.0, layer_out_std: float = 0.1, split: bool = True):
+                 device="cuda", h0_scale: float = 1.0, layer_out_std: float = 0.1):
         self.T, self.d, self.layers, self.block_size = T, d, layers, block_size
-        self.exchange = new_exchange(T, d, torch.bfloat16, device) if split else None
         self.store = SourceStore(T, d, s_max=MAX_SOURCES, dtype=torch.bfloat16, device=device)
         synth.fill_normal_(self.store.h0, h0_scale, seed=seed, tag=1)
         self.F = [synth.layer_output(T, d, std=layer_out_std, seed=seed, tag=l, device=device)
@@ -122,7 +119,7 @@ class Schedule:
             raise ValueError(f"unknown mode {mode!r}")
         run_schedule(self.store, self.F, self.W, self.block_size, out=self.out, weights=self.weights,
                      final_query=self.w_out, final_out=self.final_out, final_weights=self.final_weights,
-                     on_layer=on_layer, fused=mode != "unfused", exchange=self.exchange, **kw)
+                     on_layer=on_layer, fused=mode != "unfused", **kw)
 
     def capture(self, mode: str = "fused") -> "torch.cuda.CUDAGraph":
         """A HIP graph of one pass (``step(mode=mode)``): its launches recorded

@@ -111,48 +111,6 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
                                   float* weights, float eps, int32_t dtype, void* stream);
 
 /*
- * Split-row aggregation for decode-size batches.  With one workgroup per token
- * a batch of a few tokens occupies a few CUs and each token's latency is that
- * of one CU streaming S rows of 2d bytes, reducing them and weighing them.  The
- * _ex entry points below take an exchange workspace; with one, batches of
- * 1..ATTNRES_SPLIT_MAX_TOKENS tokens (S <= ATTNRES_MAX_SOURCES) run one 64-lane
- * workgroup per 1 KiB chunk of each token's row instead: every chunk forms its
- * per-source sum of squares and w.x, the chunks of a token exchange them
- * through the workspace, and each chunk then forms the softmax and its part of
- * the weighted sum (the definition above, unchanged; the sums over d are taken
- * in chunk order, so results are bitwise reproducible, though rounded in a
- * different order than the one-workgroup-per-token kernel's).  Larger batches,
- * or no workspace, run the one-workgroup-per-token kernel.
- *
- * attnres_exchange_bytes -- bytes of exchange workspace for T tokens of width d
- * (0 when T is outside 1..ATTNRES_SPLIT_MAX_TOKENS: no workspace needed).  Host
- * only.  A workspace sized for T serves every smaller batch.
- *
- * The workspace is device memory owned by the caller: 256-byte aligned, all
- * zero before its first use (e.g. hipMemset once after allocating), then kept
- * consistent by the kernels themselves -- no clearing between calls, so a
- * captured graph may replay it.  Calls sharing one workspace must not overlap
- * in time (one workspace per stream); a launch that never completes leaves it
- * to be zeroed again.  Byte 8 holds a sticky flag (uint32) that a kernel sets
- * if a chunk's wait for its token's other chunks ran out (never expected).
- */
-#define ATTNRES_SPLIT_MAX_TOKENS 256
-ATTNRES_API int attnres_exchange_bytes(int64_t T, int32_t d, int32_t dtype, int64_t* bytes);
-
-/*
- * attnres_aggregate_ex -- attnres_aggregate with an exchange workspace
- * (exchange, exchange_bytes), or NULL and 0 for none (then identical to
- * attnres_aggregate).  ATTNRES_EUNSUPPORTED if exchange is not 256-byte
- * aligned; ATTNRES_EINVAL if the split instance applies and exchange_bytes is
- * below attnres_exchange_bytes(T, d); ATTNRES_EALIAS if the workspace overlaps
- * sources, w, out or weights.
- */
-ATTNRES_API int attnres_aggregate_ex(const void* sources, int32_t S, int64_t T, int32_t d,
-                                     int64_t src_stride, const float* w, void* out, float* weights,
-                                     float eps, int32_t dtype, void* exchange, int64_t exchange_bytes,
-                                     void* stream);
-
-/*
  * Source store: host-side bookkeeping for device slots [s_max][T][d].
  * Slot 0 holds the embedding h_0 (written by the caller); slot n holds block
  * representation b_n once block n is complete; slot 1 + n_completed holds the
@@ -231,18 +189,6 @@ ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out,
  */
 ATTNRES_API int attnres_accumulate_aggregate(attnres_store_t* st, const void* layer_out, int32_t finalize_block,
                                              const float* w, void* out, float* weights, float eps, void* stream);
-
-/*
- * attnres_accumulate_aggregate_ex -- attnres_accumulate_aggregate with an
- * exchange workspace for decode-size batches (see attnres_exchange_bytes; the
- * same checks as attnres_aggregate_ex, the workspace also clear of the store
- * and layer_out).  The slot update is bit-identical to attnres_accumulate in
- * either instance.
- */
-ATTNRES_API int attnres_accumulate_aggregate_ex(attnres_store_t* st, const void* layer_out,
-                                                int32_t finalize_block, const float* w, void* out,
-                                                float* weights, float eps, void* exchange,
-                                                int64_t exchange_bytes, void* stream);
 
 /*
  * Two-phase schedule (kimi.papertok.ai ch. 4 §4.4, third benefit, and §4.6,

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -70,68 +70,6 @@ def agg(S=9, T=4, d=7168, stride=0, src=SRC, w=W, out=OUT, wts=WTS, eps=1e-5, dt
 ])
 def test_aggregate_rejects_before_any_launch(lib, kwargs, status):
     assert agg(**kwargs) == status
-
-
-XCH = 0x50000000  # fake exchange workspace, 256-byte aligned
-
-
-def agg_ex(xch=XCH, nbytes=None, T=4, d=7168, S=9, **kw):
-    if nbytes is None:
-        nbytes = B.exchange_bytes(max(T, 1), d) if xch else 0
-    return B.lib().attnres_aggregate_ex(kw.get("src", SRC), S, T, d, 0, W, OUT, WTS, 1e-5, B.BF16, xch, nbytes, None)
-
-
-def test_exchange_bytes(lib):
-    # 256-byte header + T * ceil(d/8/64) chunks * 32 records of 8 bytes (bf16)
-    assert B.exchange_bytes(1, 7168) == 256 + 14 * 256
-    assert B.exchange_bytes(64, 7168) == 256 + 64 * 14 * 256
-    assert B.exchange_bytes(3, 7176) == 256 + 3 * 15 * 256          # a ragged last chunk
-    assert B.exchange_bytes(5, 7168, B.torch.float32) == 256 + 5 * 28 * 256
-    assert B.exchange_bytes(B.SPLIT_MAX_TOKENS, 8) == 256 + B.SPLIT_MAX_TOKENS * 256
-    assert B.exchange_bytes(0, 7168) == 0 and B.exchange_bytes(B.SPLIT_MAX_TOKENS + 1, 7168) == 0
-    with pytest.raises(B.AttnResError):
-        B.exchange_bytes(4, 7164)
-
-
-@pytest.mark.parametrize("kwargs,status", [
-    (dict(xch=XCH + 16), B.EUNSUPPORTED),            # not 256-byte aligned
-    (dict(nbytes=256 + 4 * 14 * 256 - 8), B.EINVAL),  # too small for T = 4
-    (dict(nbytes=-1), B.EINVAL),
-    (dict(xch=None, nbytes=64), B.EINVAL),           # bytes without a workspace
-    (dict(xch=SRC + 256), B.EALIAS),                 # inside the sources
-    (dict(xch=OUT - 256), B.EALIAS),                 # runs into out
-    (dict(xch=WTS), B.EALIAS),
-])
-def test_aggregate_ex_checks_the_workspace(lib, kwargs, status):
-    assert agg_ex(**kwargs) == status
-
-
-def test_aggregate_ex_checks_apply_only_where_the_split_instance_runs(lib):
-    # above the split limit the workspace is not used: a small one is not an error (the
-    # call then reaches the device query, which fails on a host without a GPU)
-    assert agg_ex(T=B.SPLIT_MAX_TOKENS + 1, nbytes=512) == B.ELAUNCH
-    assert agg_ex(S=10, nbytes=512) == B.ELAUNCH          # many-source kernel: not split
-    assert agg_ex(T=0, xch=XCH + 16) == B.OK              # nothing to do
-
-
-def test_accumulate_aggregate_ex_checks_the_workspace(lib):
-    st = B.attnres_store_t()
-    assert B.lib().attnres_store_init(ctypes.byref(st), SRC, 9, 4, 7168, 0, B.BF16) == B.OK
-    st.n_completed, st.partial_valid = 3, 1
-    F = 0x60000000
-
-    def acc_ex(xch=XCH, nbytes=B.exchange_bytes(4, 7168), layer=F):
-        before = (st.n_completed, st.partial_valid)
-        rc = B.lib().attnres_accumulate_aggregate_ex(ctypes.byref(st), layer, 0, W, OUT, WTS, 1e-5, xch, nbytes,
-                                                     None)
-        assert (st.n_completed, st.partial_valid) == before   # no change on failure
-        return rc
-
-    assert acc_ex(xch=XCH + 8) == B.EUNSUPPORTED
-    assert acc_ex(nbytes=100) == B.EINVAL
-    assert acc_ex(xch=SRC + 512) == B.EALIAS                  # inside the store
-    assert acc_ex(xch=F) == B.EALIAS                          # the layer output
-    assert acc_ex(xch=None, nbytes=8) == B.EINVAL
 
 
 def test_aggregate_empty_batch_is_ok_without_pointers(lib):

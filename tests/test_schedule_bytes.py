@@ -38,7 +38,7 @@ class CountingStore:
         self._add_layer(finalize_block)
 
     def accumulate_aggregate(self, layer_out, finalize_block, w, out=None, weights=None, *, want_weights=True,
-                             eps=1e-5, exchange=None, stream=None):
+                             eps=1e-5, stream=None):
         had_partial = self.partial_valid
         self._add_layer(finalize_block)
         S, T, d = self.num_sources(), self.T, self.d
@@ -76,8 +76,7 @@ class CountingStore:
 def _run(mode, T=3, d=16, layers=93, block_size=12, two_phase_from=3):
     store = CountingStore(T, d)
 
-    def counting_aggregate(sources, w, out=None, weights=None, *, want_weights=True, eps=1e-5, exchange=None,
-                           stream=None):
+    def counting_aggregate(sources, w, out=None, weights=None, *, want_weights=True, eps=1e-5, stream=None):
         S = sources.shape[0]
         store.bytes += S * store.row + store.row + (4 * T * S if weights is not None else 0) + 4 * d
         return out, weights
