@@ -25,6 +25,7 @@ MAX_SOURCES_FULL = 256     # one aggregation (Full AttnRes / sublayer granularit
 MAX_INTER_SOURCES = 8      # two-phase: inter-block sources per pass
 MAX_BLOCK_QUERIES = 16     # two-phase: layer queries per pass
 MAX_D_BF16, MAX_D_F32 = 16384, 8192   # widest rows (ATTNRES_MAX_D_BF16 / _F32)
+STATIC_SCRATCH_BYTES = 16 << 20       # ATTNRES_STATIC_SCRATCH_BYTES
 OK, EINVAL, EUNSUPPORTED, EALIAS, ELAUNCH, ESTATE = 0, -1, -2, -3, -4, -5
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float32: F32}
 
@@ -80,6 +81,13 @@ _SIGNATURES = {
                                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
                                                   ctypes.c_void_p]),
+    "attnres_aggregate_backward_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                         ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint32,
+                                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                         ctypes.c_void_p, ctypes.c_float, ctypes.c_int32,
+                                                         ctypes.c_void_p]),
     "attnres_partial_sums": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_void_p]),

@@ -37,6 +37,8 @@
 //   (+ 2 d for the optional copy of the last source's gradient).
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -892,6 +894,38 @@ static_assert(kDwWaves * kDwCols == kBlockDwCols, "columns per dL/dw workgroup")
 
 hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream) {
   return a.bf16 ? launch_bwd<true>(a, stream) : launch_bwd<false>(a, stream);
+}
+
+// ---- static scratch for callers that cannot allocate -----------------------
+//
+// attnres_aggregate_backward_static keeps its per-workgroup dL/dw rows here
+// instead of in a caller's workspace: 16 MiB, held on every GPU the library
+// runs on until the process ends.  Every workgroup writes its whole row before
+// the fixed-order sum reads it, so nothing needs clearing between calls; calls
+// that overlap in time on one GPU race for it.  Host code never passes the
+// array's name to a kernel -- in host code it is a stand-in, not a device
+// address -- only the address resolved below.
+namespace {
+__device__ __align__(256) static float scratch[kStaticScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> hold(g_scratch_lock);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current: this GPU's copy
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream) {

@@ -12,6 +12,7 @@
 static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
 static_assert(ATTNRES_MAX_INTER_SOURCES == attnres::kMaxInterSources, "inter-source limits disagree");
 static_assert(ATTNRES_MAX_BLOCK_QUERIES == attnres::kMaxBlockQueries, "query limits disagree");
+static_assert(ATTNRES_STATIC_SCRATCH_BYTES == attnres::kStaticScratchBytes, "static scratch sizes disagree");
 
 namespace {
 
@@ -223,13 +224,18 @@ ATTNRES_API int attnres_aggregate_backward_workspace(int64_t T, int32_t d, int32
   return ATTNRES_OK;
 }
 
-ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
-                                           const void* last_source, const float* w, const void* grad_out,
-                                           float* grad_sources,
-                                           int64_t grad_stride, uint32_t accumulate_mask, uint32_t defer_mask,
-                                           float* coef, int64_t coef_stride, void* grad_last,
-                                           float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
-                                           int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// attnres_aggregate_backward, with its dL/dw rows either in the caller's
+// workspace or (use_static) in the library's static device array, whose grid
+// is then capped at the rows that fit.
+int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
+                            const void* last_source, const float* w, const void* grad_out, float* grad_sources,
+                            int64_t grad_stride, uint32_t accumulate_mask, uint32_t defer_mask, float* coef,
+                            int64_t coef_stride, void* grad_last, float* grad_w, void* workspace,
+                            int64_t workspace_bytes, bool use_static, float eps, int32_t dtype, void* stream) {
   if (S < 1 || S > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
   int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
@@ -253,7 +259,7 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   const Range r_gw = range(grad_w, (int64_t)d * 4);
   if (T > 0) {
     if ((sources == nullptr && !(S == 1 && last_source != nullptr)) || w == nullptr || grad_out == nullptr ||
-        grad_sources == nullptr || workspace == nullptr || workspace_bytes <= 0)
+        grad_sources == nullptr || (!use_static && (workspace == nullptr || workspace_bytes <= 0)))
       return ATTNRES_EINVAL;
     if (!aligned16(sources) || !aligned16(w) || !aligned16(grad_out) || !aligned16(grad_sources) ||
         !aligned16(workspace) || (grad_last != nullptr && !aligned16(grad_last)) ||
@@ -280,6 +286,8 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
         if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
     }
   }
+  const int64_t row_bytes = (int64_t)d * 4;
+  if (use_static && row_bytes > attnres::kStaticScratchBytes) return ATTNRES_EINVAL;  // beyond the static array
   int cus = 0;
   rc = device_cus(&cus);
   if (rc != ATTNRES_OK) return rc;
@@ -288,8 +296,15 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   if (rc != ATTNRES_OK) return rc;
   const unsigned all = S >= 32 ? 0xFFFFFFFFu : ((1u << S) - 1u);
   const bool last_only = ((~defer_mask & all) & ~(1u << (S - 1))) == 0;
-  const int64_t grid = backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, last_only));
-  if (T > 0 && workspace_bytes < grid * (int64_t)d * 4) return ATTNRES_EINVAL;
+  int64_t grid = backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, last_only));
+  if (use_static) {
+    // the static array, resolved once per device, and no more rows than it holds
+    if (attnres::static_scratch(&workspace) != hipSuccess) return ATTNRES_ELAUNCH;
+    workspace_bytes = attnres::kStaticScratchBytes;
+    const int64_t rows = workspace_bytes / row_bytes;
+    if (grid > rows) grid = rows;
+  }
+  if (T > 0 && workspace_bytes < grid * row_bytes) return ATTNRES_EINVAL;
   attnres::BackwardArgs a;
   a.sources = sources;
   a.S = S;
@@ -317,6 +332,33 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
   (void)hipGetLastError();
   return attnres::launch_aggregate_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                                : ATTNRES_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
+                                           const void* last_source, const float* w, const void* grad_out,
+                                           float* grad_sources,
+                                           int64_t grad_stride, uint32_t accumulate_mask, uint32_t defer_mask,
+                                           float* coef, int64_t coef_stride, void* grad_last,
+                                           float* grad_w, void* workspace, int64_t workspace_bytes, float eps,
+                                           int32_t dtype, void* stream) {
+  return aggregate_backward_impl(sources, S, T, d, src_stride, last_source, w, grad_out, grad_sources, grad_stride,
+                                 accumulate_mask, defer_mask, coef, coef_stride, grad_last, grad_w, workspace,
+                                 workspace_bytes, false, eps, dtype, stream);
+}
+
+ATTNRES_API int attnres_aggregate_backward_static(const void* sources, int32_t S, int64_t T, int32_t d,
+                                                  int64_t src_stride, const void* last_source, const float* w,
+                                                  const void* grad_out, float* grad_sources, int64_t grad_stride,
+                                                  uint32_t accumulate_mask, uint32_t defer_mask, float* coef,
+                                                  int64_t coef_stride, void* grad_last, float* grad_w, float eps,
+                                                  int32_t dtype, void* stream) {
+  return aggregate_backward_impl(sources, S, T, d, src_stride, last_source, w, grad_out, grad_sources, grad_stride,
+                                 accumulate_mask, defer_mask, coef, coef_stride, grad_last, grad_w, nullptr, 0, true,
+                                 eps, dtype, stream);
 }
 
 // Token groups of the block pass's dL/dw contraction: about four workgroups per

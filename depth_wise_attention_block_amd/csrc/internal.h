@@ -134,6 +134,13 @@ struct BackwardArgs {
 
 hipError_t launch_aggregate_backward(const BackwardArgs& a, hipStream_t stream);
 
+// The dL/dw rows of attnres_aggregate_backward_static: a file-scope device array
+// of this many bytes (ATTNRES_STATIC_SCRATCH_BYTES) in backward.hip.
+constexpr int64_t kStaticScratchBytes = INT64_C(16) << 20;
+// Its address on the current device: looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept.
+hipError_t static_scratch(void** ptr);
+
 // The deferred inter-block gradients of one block (see block_backward_kernel).
 constexpr int kMaxBlockLayers = 16;
 struct BlockRows {

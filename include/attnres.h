@@ -337,6 +337,30 @@ ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64
                                            int32_t dtype, void* stream);
 
 /*
+ * attnres_aggregate_backward_static -- attnres_aggregate_backward without a
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, training or serving loops, harnesses that forbid hipMalloc.
+ * Allocates nothing.  The per-workgroup dL/dw rows go to a static device array
+ * of ATTNRES_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; the grid is capped at the rows it holds
+ * (ATTNRES_STATIC_SCRATCH_BYTES / (4 d): 585 at d = 7168, 256 at d = 16384),
+ * so with the same grid the results are bitwise those of
+ * attnres_aggregate_backward.  Arguments, checks and outputs as there, minus
+ * workspace; ATTNRES_EINVAL if one row of d floats exceeds the array (no d the
+ * library supports does).  Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (on different streams) race.  The first
+ * call on a device resolves the array's address on it; make one call before
+ * capturing a graph.
+ */
+#define ATTNRES_STATIC_SCRATCH_BYTES (16 << 20)
+ATTNRES_API int attnres_aggregate_backward_static(const void* sources, int32_t S, int64_t T, int32_t d,
+                                                  int64_t src_stride, const void* last_source, const float* w,
+                                                  const void* grad_out, float* grad_sources, int64_t grad_stride,
+                                                  uint32_t accumulate_mask, uint32_t defer_mask, float* coef,
+                                                  int64_t coef_stride, void* grad_last, float* grad_w, float eps,
+                                                  int32_t dtype, void* stream);
+
+/*
  * attnres_block_backward -- the deferred gradients of a block's inter-block
  * sources.  In Block AttnRes the n sources h_0, b_1 .. b_{n-1} are shared by
  * every layer of block n (kimi.papertok.ai §4.3); when the B layers' backwards

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -349,6 +349,25 @@ def test_backward_host_checks(lib):
     assert wsb(4, 12, 3, B.BF16, ctypes.byref(out)) == B.EUNSUPPORTED and wsb(4, 8, 3, B.BF16, None) == B.EINVAL
 
 
+def test_backward_static_checks_like_the_workspace_entry_point(lib):
+    """attnres_aggregate_backward_static takes the same arguments minus the
+    workspace and rejects the same mistakes before any HIP call; a valid call
+    gets as far as the device query (which fails on a host without a GPU)."""
+    GS, GW, GL, G, CF = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+    def bs(src=SRC, S=3, T=4, d=7168, w=W, g=G, gs=GS, gw=GW, gl=GL, acc=0, defer=0, cf=None, cs=0, eps=1e-5,
+           dtype=B.BF16):
+        return B.lib().attnres_aggregate_backward_static(src, S, T, d, 0, None, w, g, gs, 0, acc, defer, cf, cs,
+                                                         gl, gw, eps, dtype, None)
+
+    assert bs(S=0) == B.EINVAL and bs(S=10) == B.EINVAL and bs(d=7164) == B.EUNSUPPORTED
+    assert bs(eps=float("nan")) == B.EINVAL and bs(gw=None) == B.EINVAL and bs(g=None) == B.EINVAL
+    assert bs(src=SRC + 8) == B.EUNSUPPORTED and bs(gw=GW + 2) == B.EUNSUPPORTED
+    assert bs(gs=SRC + 32) == B.EALIAS and bs(gl=G) == B.EALIAS and bs(gw=W) == B.EALIAS
+    assert bs(defer=1) == B.EINVAL                                 # deferred sources need coef
+    assert bs() == B.ELAUNCH                                       # checks passed: the device query fails here
+
+
 def test_partial_sums_host_checks(lib):
     Arr = ctypes.c_void_p * 3
     F3 = Arr(SRC, SRC + 4096, SRC + 8192)
@@ -372,6 +391,7 @@ def test_binding_limits_match_the_header():
     assert defines["ATTNRES_MAX_INTER_SOURCES"] == B.MAX_INTER_SOURCES
     assert defines["ATTNRES_MAX_BLOCK_QUERIES"] == B.MAX_BLOCK_QUERIES
     assert defines["ATTNRES_MAX_D_BF16"] == B.MAX_D_BF16 and defines["ATTNRES_MAX_D_F32"] == B.MAX_D_F32
+    assert re.search(r"#define ATTNRES_STATIC_SCRATCH_BYTES \(16 << 20\)", text) and B.STATIC_SCRATCH_BYTES == 16 << 20
 
 
 def test_binding_refuses_host_tensors():

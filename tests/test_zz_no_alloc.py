@@ -1,0 +1,79 @@
+"""attnres_aggregate_backward_static -- the entry point that allocates nothing
+(its dL/dw rows in the library's static device array) -- against
+attnres_aggregate_backward with a caller workspace, through the C ABI: two
+calls in a row, the second on a smaller batch (the array still holds the first
+call's rows), for the general kernel and the last-source streaming kernel."""
+
+import numpy as np
+import pytest
+import torch
+
+from depth_wise_attention_block_amd import binding as B
+from depth_wise_attention_block_amd import synth
+from tests.gpu_util import device, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _call(static, H, w, g, grads, gw, gl, defer, coef, ws=None):
+    S, T, d = grads.shape
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (H.data_ptr(), S, T, d, H.stride(0), None, w.data_ptr(), g.data_ptr(), grads.data_ptr(),
+            grads.stride(0), 0, defer, coef.data_ptr() if defer else None, coef.shape[1] if defer else 0,
+            gl.data_ptr() if gl is not None else None, gw.data_ptr())
+    if static:
+        rc = B.lib().attnres_aggregate_backward_static(*args, 1e-5, B.BF16, stream)
+    else:
+        rc = B.lib().attnres_aggregate_backward(*args, ws.data_ptr(), ws.numel() * ws.element_size(), 1e-5, B.BF16,
+                                                stream)
+    assert rc == B.OK, B.strerror(rc)
+
+
+def _case(T, S, d, defer, seed):
+    dev = device()
+    H = synth.sources(S, T, d, scale=(0.5, 50.0), seed=seed, device=dev)
+    w = synth.query(d, seed=seed + 1, device=dev)
+    g = synth.layer_output(T, d, std=1.0, seed=seed, tag=3, device=dev)
+    outs = []
+    for static in (False, True):
+        grads = torch.full((S, T, d), 7.0, dtype=torch.float32, device=dev)
+        gw = torch.full((d,), 7.0, dtype=torch.float32, device=dev)
+        last_deferred = (defer >> (S - 1)) & 1
+        gl = None if last_deferred else torch.zeros((T, d), dtype=torch.bfloat16, device=dev)
+        coef = torch.zeros((T, 3 * S), dtype=torch.float32, device=dev)
+        ws = None
+        if not static:
+            ws = torch.empty(max(B.backward_workspace_bytes(T, d) // 4, 4), dtype=torch.float32, device=dev)
+        _call(static, H, w, g, grads, gw, gl, defer, coef, ws)
+        torch.cuda.synchronize()
+        outs.append((grads, gw, gl, coef))
+    return outs
+
+
+def _same(x, y):
+    return x is None and y is None or torch.equal(x.view(torch.int32 if x.dtype == torch.float32 else torch.int16),
+                                                  y.view(torch.int32 if y.dtype == torch.float32 else torch.int16))
+
+
+@pytest.mark.parametrize("defer", [0, 0xFF], ids=["general", "last_source"])
+def test_static_backward_matches_the_workspace_entry_point(defer):
+    """Two calls in a row, the second smaller; outputs bitwise equal to the
+    workspace entry point's (same grid: the static array holds 585 rows at
+    d = 7168, more than one row per resident workgroup on this device)."""
+    S, d = 9, 7168
+    rows_static = B.STATIC_SCRATCH_BYTES // (4 * d)
+    for T, seed in ((4096, 1), (300, 2)):
+        note(f"no-alloc backward defer={defer:#x} T={T}")
+        (g0, w0, l0, c0), (g1, w1, l1, c1) = _case(T, S, d, defer, seed)
+        grid = B.backward_workspace_bytes(T, d) // (4 * d)
+        for k in range(S):
+            if not (defer >> k) & 1:
+                assert _same(g0[k], g1[k]), f"T={T} grad row {k}"
+        assert _same(l0, l1), f"T={T} handed-out gradient"
+        if defer:
+            assert _same(c0, c1), f"T={T} coefficients"
+        if grid <= rows_static:
+            assert _same(w0, w1), f"T={T} dL/dw"
+        else:   # a device with more workgroups than static rows: dL/dw summed over a capped grid
+            scale = float(w0.abs().max())
+            assert float((w0 - w1).abs().max()) <= 1e-5 * scale, f"T={T} dL/dw"
