@@ -8,6 +8,7 @@
 
 #include "attnres.h"
 #include "internal.h"
+#include "launch_policy.h"
 
 static_assert(ATTNRES_MAX_SOURCES_FULL == attnres::kMaxSourcesMany, "source limits disagree");
 static_assert(ATTNRES_MAX_INTER_SOURCES == attnres::kMaxInterSources, "inter-source limits disagree");
@@ -44,37 +45,6 @@ int check_shape(int64_t T, int32_t d, int32_t dtype) {
   if (d > (dtype == ATTNRES_BF16 ? ATTNRES_MAX_D_BF16 : ATTNRES_MAX_D_F32)) return ATTNRES_EUNSUPPORTED;
   // keep every element offset far inside int64
   if (T > (INT64_C(1) << 40) / d) return ATTNRES_EINVAL;
-  return ATTNRES_OK;
-}
-
-// Launch shape: each lane holds V 16-byte vectors of every source row; V is
-// the smallest value that keeps the workgroup within kMaxWaves waves.  One
-// token per workgroup per trip; the grid covers every token up to a cap, past
-// which workgroups loop over tokens.
-//
-// With xcd_runs (the aggregation kernels), workgroups are dispatched to the 8
-// XCDs in turn, and each XCD takes runs of kXcdRun consecutive tokens instead
-// of every 8th token: the HBM traffic of one XCD then moves in runs of
-// kXcdRun rows of each source (measured at T = 262,144: 3% more bandwidth for
-// the aggregation and the fused step, results bit-identical).  Small batches
-// keep one token per XCD in turn, where runs would leave workgroups idle.
-constexpr int kXcdRunLog2 = 5;                  // runs of 32 tokens
-constexpr int64_t kXcdRunMinTokens = 4096;      // from this batch size on
-int pick_config(int32_t S, int64_t T, int32_t d, int32_t dtype, int32_t num_cus, attnres_launch_t* cfg,
-                bool xcd_runs = false) {
-  const int nvec = d / elems_per_vec(dtype);
-  const int max_threads = 64 * attnres::kMaxWaves;
-  const int v = (nvec + max_threads - 1) / max_threads;
-  if (v < 1 || v > attnres::kMaxVecsPerLane) return ATTNRES_EUNSUPPORTED;
-  const int lanes = (nvec + v - 1) / v;
-  cfg->threads = (lanes + 63) / 64 * 64;
-  cfg->vecs_per_lane = v;
-  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 4096;  // a multiple of 8
-  cfg->xcd_run = (xcd_runs && T >= kXcdRunMinTokens) ? (1 << kXcdRunLog2) : 1;
-  const int64_t span = cfg->xcd_run > 1 ? (T + 8 * cfg->xcd_run - 1) / (8 * cfg->xcd_run) * (8 * cfg->xcd_run) : T;
-  cfg->grid = span < cap ? span : cap;
-  cfg->tokens_per_group = 1;
-  (void)S;
   return ATTNRES_OK;
 }
 

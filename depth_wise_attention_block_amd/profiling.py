@@ -31,18 +31,21 @@ import os
 import sqlite3
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# every file the aggregation kernels are compiled from, and capi.cpp, which
-# picks their launch shape (threads, grid, token order): a change to any of
-# them makes committed counter bytes stale
+# every file the aggregation kernels are compiled from, and launch_policy.h,
+# which picks their launch shape (threads, grid, token order): a change to any
+# of them makes committed counter bytes stale
 AGG_SOURCES = tuple(os.path.join(HERE, "csrc", f)
-                    for f in ("aggregate.hip", "device_common.h", "internal.h", "capi.cpp"))
+                    for f in ("aggregate.hip", "device_common.h", "internal.h", "launch_policy.h"))
 
 
-# every file the kernels of one whole pass are compiled from, plus the launch policy
+# every file the kernels of one whole pass are compiled from, plus the launch
+# policy (capi.cpp sizes the backward's grids and workspaces itself)
 PASS_SOURCES = {
-    "schedule_93_t32768_two_phase": ("aggregate.hip", "twophase.hip", "device_common.h", "internal.h", "capi.cpp"),
-    "schedule_93_t32768_backward": ("backward.hip", "device_common.h", "internal.h", "capi.cpp"),
-    "many_sources_s94_t32768": ("aggregate.hip", "device_common.h", "internal.h", "capi.cpp"),
+    "schedule_93_t32768_two_phase": ("aggregate.hip", "twophase.hip", "device_common.h", "internal.h",
+                                     "launch_policy.h"),
+    "schedule_93_t32768_backward": ("backward.hip", "device_common.h", "internal.h", "launch_policy.h",
+                                    "capi.cpp"),
+    "many_sources_s94_t32768": ("aggregate.hip", "device_common.h", "internal.h", "launch_policy.h"),
 }
 
 
