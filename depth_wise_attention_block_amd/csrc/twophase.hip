@@ -4,7 +4,8 @@
 // once for all the block's layer queries; each layer then folds its growing
 // partial sum in with an online-softmax merge.
 //
-// Phase 1, interblock_kernel (one launch per block).  Per token: load the K
+// Phase 1, interblock_kernel (one launch per block, one workgroup per token;
+// batches past the grid cap take several launches).  Per token: load the K
 // inter-block rows once (optionally closing the previous block first: its last
 // layer output is added into the partial slot, which becomes b_{n-1}); for
 // each of the B queries compute the K logits; softmax per query; and write
@@ -46,10 +47,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 template <int kV>
 constexpr int waves_per_simd2() { return kV == 1 ? 5 : kV == 2 ? 4 : 2; }
 // The inter-block pass holds kK rows of kV vectors per lane.  At kV = 2 both
-// instances run at 4 waves per SIMD (two 7-wave workgroups per CU): 4 rows fit
-// in 128 VGPRs; the 8-row instance spills ~20 loop-invariant values, which
-// measured faster than 3 waves per SIMD without spills.  Wider rows (kV >= 3)
-// get 2 waves per SIMD.
+// instances run at 4 waves per SIMD (two 7-wave workgroups per CU) and fit in
+// 128 VGPRs without spilling (the 8-row one only as a straight-line one-token
+// body, see interblock_kernel).  Wider rows (kV >= 3) get 2 waves per SIMD.
 template <int kV, int kK>
 constexpr int waves_per_simd_prepare() {
   return kV <= 2 ? 4 : 2;
@@ -78,6 +78,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // loads are unconditional: a load behind a branch would make the compiler wait
 // for every outstanding load at the join, which defeats the prefetch ring.
 constexpr int kBufferConfig = 0x00020000;  // buffer resource word 3 on gfx9
+constexpr int kNonTemporal = 2;            // buffer cache policy: non-temporal
 
 struct QueryRows {
   __amdgpu_buffer_rsrc_t rsrc;
@@ -116,7 +117,7 @@ __device__ __forceinline__ void load_query_chunk(u32x4& hi, u32x4& lo, const Que
 // rows leave as whole 64-byte segments.
 template <int kV, int kClose, int kK>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_prepare<kV, kK>())))
-interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, int64_t src_stride_v,
+interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int64_t t0, int nvec, int64_t src_stride_v,
                   const u32x4* __restrict__ w_split, u32x4* __restrict__ inter, int64_t inter_stride_v,
                   float* __restrict__ logits, float* __restrict__ weights0, float eps, float inv_d,
                   const u32x4* __restrict__ layer_out) {
@@ -127,8 +128,8 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
   static_assert(kC % kRing == 0, "ring slots must divide the chunks");
   constexpr int kParts = 4 * kMaxWaves;
   // partial sums: one per 16-lane row of every wave, summed in a fixed order
-  __shared__ float red_ss[2][kMaxInter][kParts];
-  __shared__ float red_dt[2][kMaxQueries][kMaxInter][kParts];
+  __shared__ float red_ss[kMaxInter][kParts];
+  __shared__ float red_dt[kMaxQueries][kMaxInter][kParts];
   __shared__ u32x4 stage[kMaxWaves][16][4][4];  // per wave: [quad][to lane][from lane]
   // per wave: every query's weights as bf16 pairs (sources 2p, 2p+1), hi and lo
   __shared__ unsigned a_pairs[kMaxWaves][2][kMaxQueries][kPairs];
@@ -144,8 +145,9 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
   const bool writer = (lane & 12) == 0;      // one lane per (row, n) after the row sums
   const int part = 4 * wave + (lane >> 4);
 
-  int buf = 0;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
+  // One token per workgroup, t0 + blockIdx.x; the host splits larger batches
+  // over several launches.
+  auto token = [&](const int64_t t) {
     u32x4* tok = src + t * (int64_t)nvec;
     const u32x4* lo_tok = layer_out + t * (int64_t)nvec;
 
@@ -212,7 +214,7 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
         for (int k = 0; k < 4; ++k) ss = dot2(x[g][i][k], x[g][i][k], ss);
       ss += dpp<kDppRor4>(ss, ss);
       ss += dpp<kDppRor8>(ss, ss);
-      if (writer) red_ss[buf][4 * g + n][part] = ss;
+      if (writer) red_ss[4 * g + n][part] = ss;
     }
 
     // 3. w_b . x_s on the matrix cores, four queries at a time; each query
@@ -257,7 +259,7 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
           float v = acc[g][m];
           v += dpp<kDppRor4>(v, v);
           v += dpp<kDppRor8>(v, v);
-          if (writer) red_dt[buf][4 * qg + m][4 * g + n][part] = v;
+          if (writer) red_dt[4 * qg + m][4 * g + n][part] = v;
         }
     }
     __syncthreads();
@@ -272,8 +274,8 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
       if (valid) {
         float ss = 0.f, dt = 0.f;
         for (int p = 0; p < 4 * nwaves; p += 4) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4*>(&red_ss[buf][s][p]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&red_dt[buf][bq][s][p]);
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(&red_ss[s][p]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&red_dt[bq][s][p]);
           ss += (a4[0] + a4[1]) + (a4[2] + a4[3]);
           dt += (d4[0] + d4[1]) + (d4[2] + d4[3]);
         }
@@ -373,15 +375,33 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int nvec, in
             const u32x2 o = {pack_bf16(acc[0][m], acc[1][m]), pack_bf16(acc[2][m], acc[3][m])};
             if (h == 0) {
               first[m] = o;
-            } else if (q0 + m < B && c < nvec) {
+            } else {
+              // through a buffer resource over query row q0 + m of this token
+              // (empty past B; stores past the row end are dropped): the
+              // address is a wave-uniform base and the lane's 32-bit offset,
+              // so no 64-bit per-lane pointer is carried from token to token
               const u32x4 rowv = {first[m][0], first[m][1], o[0], o[1]};
-              __builtin_nontemporal_store(rowv, inter + (int64_t)(q0 + m) * inter_stride_v + t * (int64_t)nvec + c);
+              const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                  inter + (int64_t)(q0 + m) * inter_stride_v + t * (int64_t)nvec, (short)0,
+                  q0 + m < B ? nvec * 16 : 0, kBufferConfig);
+              __builtin_amdgcn_raw_buffer_store_b128(rowv, r, c * 16, 0, kNonTemporal);
             }
           }
         }
         __builtin_amdgcn_sched_barrier(0);  // one chunk's accumulators live at a time
       }
     }
+  };
+  if constexpr (kK > 4) {
+    // straight-line: nothing is kept live from token to token, and the 8-row
+    // instance fits in its registers without spilling
+    const int64_t t = t0 + blockIdx.x;
+    if (t < T) token(t);
+  } else {
+    // the same single trip as a loop the compiler cannot see through: it
+    // schedules the 4-row body with more registers, measured 6% faster
+    const int64_t t_end = t0 + (int64_t)gridDim.x < T ? t0 + (int64_t)gridDim.x : T;
+    for (int64_t t = t0 + blockIdx.x; t < t_end; t += gridDim.x) token(t);
   }
 }
 
@@ -504,12 +524,18 @@ __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restr
 template <int kV, int kClose, int kK>
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
   const int nvec = a.d / 8;
-  hipLaunchKernelGGL((interblock_kernel<kV, kClose, kK>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
-                     static_cast<u32x4*>(a.store), a.K, a.B, a.T, nvec, a.slot_stride / 8,
-                     static_cast<const u32x4*>(a.w_split),
-                     static_cast<u32x4*>(a.inter), a.inter_stride / 8, a.logits, a.weights0, a.eps,
-                     1.0f / (float)a.d, static_cast<const u32x4*>(a.layer_out));
-  return hipGetLastError();
+  // one workgroup per token, at most a.grid tokens per launch
+  for (int64_t t0 = 0; t0 < a.T; t0 += a.grid) {
+    const int64_t n = a.T - t0 < a.grid ? a.T - t0 : a.grid;
+    hipLaunchKernelGGL((interblock_kernel<kV, kClose, kK>), dim3((unsigned)n), dim3(a.threads), 0, stream,
+                       static_cast<u32x4*>(a.store), a.K, a.B, a.T, t0, nvec, a.slot_stride / 8,
+                       static_cast<const u32x4*>(a.w_split),
+                       static_cast<u32x4*>(a.inter), a.inter_stride / 8, a.logits, a.weights0, a.eps,
+                       1.0f / (float)a.d, static_cast<const u32x4*>(a.layer_out));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int kV, bool kAdd>

@@ -70,6 +70,38 @@ def test_prepare_matches_oracle(T, d, n_completed, partial_valid, close, Bq):
             assert np.max(np.abs(host(w0) - a_ref)) <= 1e-3
 
 
+def test_prepare_split_over_launches_beyond_the_grid_cap():
+    """More tokens than one launch's grid (CUs x 4096): the host splits the
+    inter-block pass over several launches of one workgroup per token.  Tokens
+    on both sides of the launch boundary, the ends and a random sample match the
+    oracle, and the closed block is written at every one of them."""
+    dev = device()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    cap = cus * 4096
+    T, d, n_completed, Bq = cap + 4099, 8, 2, 5
+    note(f"prepare over launches T={T} cap={cap}")
+    st = _store(T, d, 21, n_completed, True, dev)
+    F = synth.layer_output(T, d, std=1.0, seed=21, tag=5, device=dev)
+    K = n_completed + 2
+    idx = torch.unique(torch.cat([synth.token_sample(T, 256, 4, seed=21), torch.arange(cap - 3, cap + 3)]))
+    idx_dev = idx.to(dev)
+    before = host(st.slots[:K].index_select(1, idx_dev))
+    W = torch.stack([synth.query(d, seed=b, device=dev, tag=b) for b in range(Bq)])
+    inter = torch.empty((Bq, T, d), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((Bq, T, K), dtype=torch.float32, device=dev)
+    st.block_prepare(F, True, B.split_queries(W), inter, logits)
+    torch.cuda.synchronize()
+    H = before.copy()
+    H[K - 1] = orc.accumulate(before[K - 1], host(F.index_select(0, idx_dev)), "bf16")
+    assert same_bits(st.slots[K - 1].index_select(0, idx_dev), H[K - 1]), "closed block representation"
+    for b in range(Bq):
+        r_ref, a_ref = oracle_aggregate(H, host(W[b]))
+        a_gpu = torch.softmax(logits[b].index_select(0, idx_dev).double(), dim=1).cpu().numpy()
+        compare(host(inter[b].index_select(0, idx_dev)), a_gpu, r_ref, a_ref, True, f"prepare over launches, query {b}")
+    del st, inter, logits
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T,d", [(64, 7168), (9, 520)])
 def test_merge_matches_oracle_through_a_block(T, d):
     """One block of 12 layers at K = 6 inter-block sources: prepare, then 11
