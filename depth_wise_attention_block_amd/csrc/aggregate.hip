@@ -8,7 +8,8 @@
 // about 2.7 flop per byte moved, far below the fp32 ridge point, so the kernel
 // is bound by HBM bandwidth and MFMA has nothing to do here.
 //
-// Design (one workgroup = one token at a time, grid-stride over tokens):
+// Design (one workgroup = one token; batches past the grid cap take several
+// launches):
 //   * the workgroup's lanes split the d-vector into 16-byte pieces; each lane
 //     loads its V pieces of ALL S sources at once (S*V outstanding 16-byte
 //     loads per lane), so every source row is read from HBM exactly once and
@@ -17,8 +18,11 @@
 //     memory: sum of squares as dot2(x, x), and w.x as dot2(x, w_hi) +
 //     dot2(x, w_lo) with the float32 query split into two bf16 halves once per
 //     workgroup -- no unpacking before the reductions;
+//   * the query's float32 loads are issued with the rows' and converted to
+//     bf16 hi + lo only after all of them are in flight, so that a token costs
+//     one memory round trip (at decode sizes that round trip is the kernel);
 //   * 2*S wave sums by DPP (row butterfly, then row_bcast15/31), one LDS
-//     exchange across waves and ONE barrier per token (double-buffered LDS);
+//     exchange across waves and ONE barrier per token;
 //   * logits, max, exponentials and the normaliser are computed by lanes
 //     0..S-1 of each 16-lane row and broadcast with readlane; the softmax is
 //     exact here because all S scores are known before the weighted sum.  (The
@@ -65,9 +69,9 @@ template <bool kBf16, int kV, int kUpdate, int kMaxS>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_s<kV, kMaxS>())))
 aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
-                 float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t span, int run_log2) {
-  // [buffer][wave][sum of squares | w.x][source]
-  __shared__ float red[2][kMaxWaves][2][16];
+                 float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t b0, int run_log2) {
+  // [wave][sum of squares | w.x][source]
+  __shared__ float red[kMaxWaves][2][16];
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -76,62 +80,60 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
   const int nwaves = nthr >> 6;
   const int s16 = lane & 15;  // source handled by this lane in the softmax step
 
-  // a workgroup of a one-trip grid whose token is past the end has nothing to do
-  if (gridDim.x >= span && xcd_token(blockIdx.x, run_log2) >= T) return;
-
-  Query<kBf16, kV> q;
-  load_query<kBf16, kV>(q, w, nvec, tid, nthr);
-
-  int buf = 0;
-  for (int64_t b = blockIdx.x; b < span; b += gridDim.x, buf ^= 1) {
-    const int64_t t = xcd_token(b, run_log2);
-    if (t >= T) continue;
+  // virtual index b0 + blockIdx.x; past the end (T rounded up to whole XCD
+  // runs) there is nothing to do
+  const int64_t t = xcd_token(b0 + blockIdx.x, run_log2);
+  if (t >= T) return;
+  {
+    QueryLoads<kBf16, kV> ql;
+    issue_query<kBf16, kV>(ql, w, nvec, tid, nthr);
     u32x4* tok = src + t * (int64_t)nvec;
     const int s_upd = kUpdate != kUpdateNone ? S - 1 : kMaxS;  // the updated slot, if any
 
     // 1. issue every load of this token: S sources x V vectors per lane (for
-    //    the updated slot: the layer output, and the old slot row when adding)
+    //    the updated slot: the layer output, and the old slot row when adding).
+    //    Each row is read through a buffer resource of its own (the row's
+    //    bytes; none for sources past S), so lanes past the row and sources
+    //    past S read zeros without a branch: a load behind a branch makes the
+    //    compiler wait for every load before it at the join.
+    const int off = tid * kVecBytes;           // vector v at off + v * nthr * 16
+    const int row_bytes = nvec * kVecBytes;
+    const u32x4* lrow = layer_out + t * (int64_t)nvec;
     u32x4 x[kMaxS][kV];
     u32x4 f[kV];
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) {
-      if (s < S) {
+      const u32x4* row = (kUpdate == kUpdateCopy && s == s_upd) ? lrow : tok + s * src_stride_v;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(row), (short)0,
+                                                                         s < S ? row_bytes : 0, kBufferConfig);
 #pragma unroll
-        for (int v = 0; v < kV; ++v) {
-          const int idx = v * nthr + tid;
-          x[s][v] = u32x4{0, 0, 0, 0};
-          if (s == s_upd) {
-            if constexpr (kUpdate == kUpdateCopy) {
-              if (idx < nvec) x[s][v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
-            } else {
-              f[v] = u32x4{0, 0, 0, 0};
-              if (idx < nvec) {
-                f[v] = __builtin_nontemporal_load(layer_out + t * (int64_t)nvec + idx);
-                x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
-              }
-            }
-          } else if (idx < nvec) {
-            x[s][v] = __builtin_nontemporal_load(tok + s * src_stride_v + idx);
-          }
-        }
-      }
+      for (int v = 0; v < kV; ++v) x[s][v] = load_nt(r, off + v * nthr * kVecBytes);
+    }
+    if constexpr (kUpdate == kUpdateAdd) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(lrow), (short)0, row_bytes, kBufferConfig);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) f[v] = load_nt(r, off + v * nthr * kVecBytes);
     }
     if constexpr (kUpdate != kUpdateNone) {
       // new slot row = old + layer output (or the layer output), written back
 #pragma unroll
       for (int s = 0; s < kMaxS; ++s) {
         if (s == s_upd) {
+          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(tok + s * src_stride_v, (short)0,
+                                                                             row_bytes, kBufferConfig);
 #pragma unroll
           for (int v = 0; v < kV; ++v) {
-            const int idx = v * nthr + tid;
             if constexpr (kUpdate == kUpdateAdd) x[s][v] = add_rows(x[s][v], f[v], kBf16);
-            if (idx < nvec) __builtin_nontemporal_store(x[s][v], tok + s * src_stride_v + idx);
+            store_nt(x[s][v], r, off + v * nthr * kVecBytes);
           }
         }
       }
     }
 
     // 2. per-lane partial statistics, then wave sums
+    Query<kBf16, kV> q;
+    finish_query<kBf16, kV>(q, ql);
     float gss = 0.f, gdt = 0.f;  // lane s of the row: source s's wave sums
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) {
@@ -162,8 +164,8 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
 
     // 3. combine the waves: one LDS exchange, one barrier
     if (lane < 16) {
-      red[buf][wave][0][lane] = gss;
-      red[buf][wave][1][lane] = gdt;
+      red[wave][0][lane] = gss;
+      red[wave][1][lane] = gdt;
     }
     __syncthreads();
 
@@ -172,8 +174,8 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
     if (s16 < S) {
       float ss = 0.f, dt = 0.f;
       for (int k = 0; k < nwaves; ++k) {
-        ss += red[buf][k][0][s16];
-        dt += red[buf][k][1][s16];
+        ss += red[k][0][s16];
+        dt += red[k][1][s16];
       }
       z = dt / sqrtf(ss * inv_d + eps);
     }
@@ -188,10 +190,10 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) as[s] = (s < S) ? lane_bcast(a, s) : 0.f;
 
-    u32x4* orow = out + t * (int64_t)nvec;
+    const __amdgpu_buffer_rsrc_t orow =
+        __builtin_amdgcn_make_buffer_rsrc(out + t * (int64_t)nvec, (short)0, row_bytes, kBufferConfig);
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
-      const int idx = v * nthr + tid;
       if constexpr (kBf16) {
         float acc[8];
 #pragma unroll
@@ -212,7 +214,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
         u32x4 o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = pack_bf16(acc[2 * k], acc[2 * k + 1]);
-        if (idx < nvec) __builtin_nontemporal_store(o, orow + idx);
+        store_nt(o, orow, off + v * nthr * kVecBytes);
       } else {
         f32x4 acc = as[0] * __builtin_bit_cast(f32x4, x[0][v]);
 #pragma unroll
@@ -223,7 +225,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
             for (int k = 0; k < 4; ++k) acc[k] = fmaf(as[s], xf[k], acc[k]);
           }
         }
-        if (idx < nvec) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, acc), orow + idx);
+        store_nt(__builtin_bit_cast(u32x4, acc), orow, off + v * nthr * kVecBytes);
       }
     }
   }
@@ -424,13 +426,23 @@ hipError_t launch_s(const AggregateArgs& a, hipStream_t stream) {
   const int epv = kBf16 ? 8 : 4;
   const int nvec = a.d / epv;
   const int run_log2 = __builtin_ctz((unsigned)a.xcd_run);
-  const int64_t span = (a.T + 8 * (int64_t)a.xcd_run - 1) / (8 * (int64_t)a.xcd_run) * (8 * (int64_t)a.xcd_run);
-  if ((a.xcd_run & (a.xcd_run - 1)) != 0 || (a.xcd_run > 1 && a.grid % 8 != 0)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS>), dim3((unsigned)a.grid), dim3(a.threads), 0,
-                     stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
-                     a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
-                     static_cast<const u32x4*>(a.layer_out), a.xcd_run > 1 ? span : a.T, run_log2);
-  return hipGetLastError();
+  // virtual indices [0, span): T, rounded up to whole runs on all 8 XCDs
+  const int64_t span =
+      a.xcd_run > 1 ? (a.T + 8 * (int64_t)a.xcd_run - 1) / (8 * (int64_t)a.xcd_run) * (8 * (int64_t)a.xcd_run) : a.T;
+  if ((a.xcd_run & (a.xcd_run - 1)) != 0 || a.grid <= 0 || (a.xcd_run > 1 && a.grid % 8 != 0))
+    return hipErrorInvalidValue;
+  // one workgroup per token; at most a.grid per launch (a multiple of 8 with
+  // XCD runs, so that every launch starts on XCD 0)
+  for (int64_t b0 = 0; b0 < span; b0 += a.grid) {
+    const int64_t n = span - b0 < a.grid ? span - b0 : a.grid;
+    hipLaunchKernelGGL((aggregate_kernel<kBf16, kV, kUpdate, kMaxS>), dim3((unsigned)n), dim3(a.threads), 0,
+                       stream, static_cast<u32x4*>(const_cast<void*>(a.sources)), a.S, a.T, nvec,
+                       a.src_stride / epv, a.w, static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d,
+                       static_cast<const u32x4*>(a.layer_out), b0, run_log2);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool kBf16, int kV, int kUpdate>

@@ -42,6 +42,19 @@ __device__ __forceinline__ int64_t xcd_token(int64_t b, int run_log2) {
   return ((((k >> run_log2) << 3) | x) << run_log2) | (k & ((INT64_C(1) << run_log2) - 1));
 }
 
+// Word 3 of a raw buffer resource on gfx9 (data format 32 bits; offsets at or
+// past the resource's size read zeros and drop stores).
+constexpr int kBufferConfig = 0x00020000;
+constexpr int kCachePolicyNt = 2;  // buffer load / store cache policy: non-temporal
+
+// 16-byte non-temporal load / store at byte offset off of a buffer resource.
+__device__ __forceinline__ u32x4 load_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNt));
+}
+__device__ __forceinline__ void store_nt(u32x4 v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicyNt);
+}
+
 // ---- DPP helpers (GFX9 data-parallel primitives inside one wave) -----------
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
@@ -149,6 +162,50 @@ __device__ __forceinline__ void load_query(Query<kBf16, kV>& q, const float* __r
     } else {
       q.f[v] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (idx < nvec) q.f[v] = reinterpret_cast<const f32x4*>(w)[idx];
+    }
+  }
+}
+
+// The same query in two steps, so that its loads can be in flight together
+// with a token's row loads: issue_query starts the float32 loads (through a
+// buffer resource over w, so that lanes past the row read zeros without a
+// branch -- a load behind a branch makes the compiler wait for it at the
+// join), and finish_query converts once they are needed.
+template <bool kBf16, int kV>
+struct QueryLoads {
+  f32x4 raw[kV][kBf16 ? 2 : 1];
+};
+
+template <bool kBf16, int kV>
+__device__ __forceinline__ void issue_query(QueryLoads<kBf16, kV>& ql, const float* __restrict__ w, int nvec,
+                                            int tid, int nthr) {
+  constexpr int kParts = kBf16 ? 2 : 1;  // 16-byte float32 loads per vector
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(w), (short)0, nvec * 16 * kParts, kBufferConfig);
+#pragma unroll
+  for (int v = 0; v < kV; ++v)
+#pragma unroll
+    for (int p = 0; p < kParts; ++p)
+      ql.raw[v][p] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((v * nthr + tid) * kParts + p) * 16, 0, 0));
+}
+
+template <bool kBf16, int kV>
+__device__ __forceinline__ void finish_query(Query<kBf16, kV>& q, const QueryLoads<kBf16, kV>& ql) {
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    if constexpr (kBf16) {
+      const f32x4 a = ql.raw[v][0], b = ql.raw[v][1];
+      const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const __bf16 h0 = (__bf16)e[2 * k], h1 = (__bf16)e[2 * k + 1];
+        const __bf16 l0 = (__bf16)(e[2 * k] - (float)h0), l1 = (__bf16)(e[2 * k + 1] - (float)h1);
+        q.hi[v][k] = __builtin_bit_cast(unsigned, bf16x2{h0, h1});
+        q.lo[v][k] = __builtin_bit_cast(unsigned, bf16x2{l0, l1});
+      }
+    } else {
+      q.f[v] = ql.raw[v][0];
     }
   }
 }

@@ -14,8 +14,10 @@ namespace {
 
 // Launch shape: each lane holds V 16-byte vectors of every source row; V is
 // the smallest value that keeps the workgroup within kMaxWaves waves.  One
-// token per workgroup per trip; the grid covers every token up to a cap, past
-// which workgroups loop over tokens.
+// token per workgroup at a time; the grid covers every token up to a cap.  Past
+// the cap the aggregation and the inter-block pass take several launches of at
+// most `grid` workgroups (each workgroup handles exactly one token); the other
+// kernels loop over tokens.
 //
 // With xcd_runs (the aggregation kernels), workgroups are dispatched to the 8
 // XCDs in turn, and each XCD takes runs of kXcdRun consecutive tokens instead

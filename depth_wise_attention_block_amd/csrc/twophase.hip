@@ -77,8 +77,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 // chunk past d reads some other chunk that only meets zero source chunks.  The
 // loads are unconditional: a load behind a branch would make the compiler wait
 // for every outstanding load at the join, which defeats the prefetch ring.
-constexpr int kBufferConfig = 0x00020000;  // buffer resource word 3 on gfx9
-constexpr int kNonTemporal = 2;            // buffer cache policy: non-temporal
 
 struct QueryRows {
   __amdgpu_buffer_rsrc_t rsrc;
@@ -384,7 +382,7 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int64_t t0, 
               const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                   inter + (int64_t)(q0 + m) * inter_stride_v + t * (int64_t)nvec, (short)0,
                   q0 + m < B ? nvec * 16 : 0, kBufferConfig);
-              __builtin_amdgcn_raw_buffer_store_b128(rowv, r, c * 16, 0, kNonTemporal);
+              store_nt(rowv, r, c * 16);
             }
           }
         }

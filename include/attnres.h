@@ -407,10 +407,12 @@ typedef struct attnres_launch {
   int32_t threads;          /* threads per workgroup (multiple of 64)         */
   int32_t vecs_per_lane;    /* 16-byte vectors of one source row per lane     */
   int64_t grid;             /* workgroups                                     */
-  int32_t tokens_per_group; /* tokens a workgroup handles per loop trip       */
+  int32_t tokens_per_group; /* tokens a workgroup handles (1)                 */
   int32_t xcd_run;          /* consecutive tokens each XCD takes in turn: the
-                               workgroup of virtual index b (b = blockIdx, then
-                               + grid per trip) runs on XCD b % 8 and handles
+                               workgroup of virtual index b (b = blockIdx, plus
+                               grid per earlier launch when the batch needs
+                               several launches of at most grid workgroups)
+                               runs on XCD b % 8 and handles
                                token ((b / 8 / r) * 8 + b % 8) * r + (b / 8) % r
                                for r = xcd_run (1: token b); the virtual
                                indices cover T rounded up to 8 r             */

@@ -136,9 +136,9 @@ def test_source_stride_larger_than_a_source():
     compare(host(out), host(a), r_ref, a_ref, True, "strided sources")
 
 
-def test_grid_stride_loop_beyond_the_grid_cap():
-    """More tokens than the grid holds: workgroups loop over tokens, the LDS
-    double buffer alternates."""
+def test_batch_beyond_the_grid_cap():
+    """More tokens than one launch's grid holds (CUs x 4096): the host splits the
+    batch over several launches of one workgroup per token, in XCD runs."""
     dev = device()
     S, T, d = 3, 256 * 4096 + 4099, 8
     cfg = B.aggregate_config(S, T, d, torch.bfloat16, torch.cuda.get_device_properties(dev).multi_processor_count)
