@@ -23,10 +23,20 @@
 // Prints one JSON object of GB/s (bytes moved / mean time over `reps` launches).
 //
 //   pattern_bench [T] [d] [reps]
+//
+// With a fourth argument `interblock`, it times instead the traffic of the
+// two-phase schedule's inter-block pass when it closes a block by addition, for
+// K = 3 .. 8 inter-block rows and B result rows: per token K rows and the layer
+// output in; the closed row, B result rows and B x K float32 logits out -- one
+// workgroup per token, every load issued at once, as the kernel does -- and
+// prints the mean time per launch in microseconds for each K.
+//
+//   pattern_bench T d reps interblock [B]
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 
 namespace {
 
@@ -109,6 +119,48 @@ chunk_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ lout, int64_t n
   if (NW == 0 && (o.x ^ o.y ^ o.z ^ o.w) == 0x9e3779b9u) sink[0] = o.x;
 }
 
+// Inter-block pass traffic at K rows, closing by addition: rows 0 .. K-1 of
+// the token (row K-1 the open partial) and the layer output in; the partial
+// written back with the layer output folded in, B result rows and the B x K
+// logits out.
+template <int K>
+__global__ void __launch_bounds__(kThreads)
+interblock_pattern(u32x4* __restrict__ src, const u32x4* __restrict__ lout, int64_t T, int nvec,
+                   u32x4* __restrict__ inter, float* __restrict__ logits, int B) {
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  u32x4 x[K + 1][2];
+#pragma unroll
+  for (int s = 0; s <= K; ++s)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int idx = v * kThreads + threadIdx.x;
+      const u32x4* row = s < K ? src + (s * T + t) * nvec : lout + t * nvec;
+      x[s][v] = idx < nvec ? ld(row + idx) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int idx = v * kThreads + threadIdx.x;
+    x[K - 1][v] ^= x[K][v];
+    if (idx < nvec) st(x[K - 1][v], src + ((K - 1) * T + t) * nvec + idx);
+  }
+  u32x4 r[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    r[v] = x[0][v];
+#pragma unroll
+    for (int s = 1; s < K; ++s) r[v] ^= x[s][v];
+  }
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int idx = v * kThreads + threadIdx.x;
+      if (idx < nvec) st(r[v] ^ u32x4{(unsigned)b, 0, 0, 0}, inter + ((int64_t)b * T + t) * nvec + idx);
+    }
+  if (threadIdx.x < B * K)
+    logits[((int64_t)(threadIdx.x / K) * T + t) * K + threadIdx.x % K] = __uint_as_float(r[0].x);
+}
+
 // Plain streams, one vector per lane: MODE 0 read, 1 write, 2 copy.
 template <int MODE>
 __global__ void __launch_bounds__(256) stream(const u32x4* __restrict__ a, u32x4* __restrict__ b, int64_t n,
@@ -127,6 +179,8 @@ __global__ void __launch_bounds__(256) stream(const u32x4* __restrict__ a, u32x4
 
 }  // namespace
 
+int interblock_main(int64_t T, int64_t d, int reps, int B);
+
 int main(int argc, char** argv) {
   const int64_t T = argc > 1 ? std::atoll(argv[1]) : 262144;
   const int64_t d = argc > 2 ? std::atoll(argv[2]) : 7168;
@@ -134,6 +188,14 @@ int main(int argc, char** argv) {
   if (T <= 0 || T > 0x7fffffff || d <= 0 || d % 8 != 0 || d / 8 > 2 * kThreads || reps <= 0) {
     std::fprintf(stderr, "need T > 0, d a multiple of 8 up to %d, reps > 0\n", 16 * kThreads);
     return 2;
+  }
+  if (argc > 4 && std::string(argv[4]) == "interblock") {
+    const int B = argc > 5 ? std::atoi(argv[5]) : 12;
+    if (B < 1 || B * 8 > kThreads) {
+      std::fprintf(stderr, "need 1 <= B <= %d\n", kThreads / 8);
+      return 2;
+    }
+    return interblock_main(T, d, reps, B);
   }
   const int nvec = (int)(d / 8);
   const int64_t n = T * nvec;                  // vectors per stream
@@ -198,5 +260,51 @@ int main(int argc, char** argv) {
   CHECK(hipFree(src));
   CHECK(hipFree(out));
   CHECK(hipFree(sink));
+  return 0;
+}
+
+int interblock_main(int64_t T, int64_t d, int reps, int B) {
+  constexpr int kMaxK = 8;
+  const int nvec = (int)(d / 8);
+  const int64_t n = T * nvec;  // vectors per row slab
+  u32x4 *src = nullptr, *lout = nullptr, *inter = nullptr;
+  float* logits = nullptr;
+  CHECK(hipMalloc(&src, kMaxK * n * 16));
+  CHECK(hipMalloc(&lout, n * 16));
+  CHECK(hipMalloc(&inter, B * n * 16));
+  CHECK(hipMalloc(&logits, (size_t)B * T * kMaxK * 4));
+  CHECK(hipMemset(src, 1, kMaxK * n * 16));
+  CHECK(hipMemset(lout, 2, n * 16));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  auto us = [&](auto launch) {
+    launch();
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0, 0));
+    for (int i = 0; i < reps; ++i) launch();
+    CHECK(hipEventRecord(e1, 0));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    return ms / reps * 1e3;
+  };
+  const unsigned g = (unsigned)T;
+  double t[kMaxK + 1] = {0};
+  t[3] = us([&] { interblock_pattern<3><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  t[4] = us([&] { interblock_pattern<4><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  t[5] = us([&] { interblock_pattern<5><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  t[6] = us([&] { interblock_pattern<6><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  t[7] = us([&] { interblock_pattern<7><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  t[8] = us([&] { interblock_pattern<8><<<g, kThreads>>>(src, lout, T, nvec, inter, logits, B); });
+  std::printf("{\"T\": %lld, \"d\": %lld, \"reps\": %d, \"B\": %d, \"interblock_pattern_us\": {", (long long)T,
+              (long long)d, reps, B);
+  for (int k = 3; k <= kMaxK; ++k) std::printf("%s\"%d\": %.1f", k > 3 ? ", " : "", k, t[k]);
+  std::printf("}}\n");
+  CHECK(hipFree(logits));
+  CHECK(hipFree(inter));
+  CHECK(hipFree(lout));
+  CHECK(hipFree(src));
   return 0;
 }

@@ -121,8 +121,8 @@ interblock_kernel(u32x4* __restrict__ src, int K, int B, int64_t T, int64_t t0, 
                   const u32x4* __restrict__ layer_out) {
   constexpr int kG = kK / 4;          // source groups held per lane
   constexpr int kC = 4 * kV;          // chunks per quad
-  // query-chunk ring: 4 slots when 4 rows leave room for them, else 2
-  constexpr int kRing = kG == 1 ? 4 : 2;
+  // query-chunk ring: 4 slots (3 chunks ahead of use)
+  constexpr int kRing = 4;
   static_assert(kC % kRing == 0, "ring slots must divide the chunks");
   constexpr int kParts = 4 * kMaxWaves;
   // partial sums: one per 16-lane row of every wave, summed in a fixed order
