@@ -677,6 +677,7 @@ ATTNRES_API int attnres_block_merge(attnres_store_t* st, const void* layer_out, 
     a.threads = cfg.threads;
     a.vecs_per_lane = cfg.vecs_per_lane;
     a.grid = cfg.grid;
+    a.per_token = merge_per_token(T);
     (void)hipGetLastError();
     if (attnres::launch_block_merge(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
   }

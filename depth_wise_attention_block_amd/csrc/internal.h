@@ -99,6 +99,7 @@ struct MergeArgs {
   float eps;
   int threads, vecs_per_lane;
   int64_t grid;
+  bool per_token = false;  // one workgroup per token, every load issued up front
 };
 
 hipError_t launch_block_merge(const MergeArgs& a, hipStream_t stream);

@@ -491,6 +491,105 @@ merge_kernel(u32x4* __restrict__ slot, const u32x4* __restrict__ layer_out, cons
   }
 }
 
+// The merge for small batches: one memory round trip per token (see
+// merge_per_token in the launch policy for when each form is used).
+template <int kV, bool kAdd>
+__global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd2<kV>())))
+merge_token_kernel(u32x4* __restrict__ slot, const u32x4* __restrict__ layer_out, const u32x4* inter,
+             const float* __restrict__ logits, int K, int64_t T, int64_t t0, int nvec, const float* __restrict__ w,
+             u32x4* out, float* __restrict__ weights, float eps, float inv_d) {
+  __shared__ float red[kMaxWaves][2];
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int s16 = lane & 15;
+
+  // one token per workgroup, t0 + blockIdx.x (the host splits larger batches
+  // over several launches); every load of the token -- the query, the three
+  // rows and the logits -- is issued before anything waits, each row through
+  // a buffer resource of its own so that no load sits behind a branch.  The
+  // arithmetic is merge_kernel's, in the same order: results are bit-identical.
+  const int64_t t = t0 + blockIdx.x;
+  if (t >= T) return;
+  QueryLoads<true, kV> ql;
+  issue_query<true, kV>(ql, w, nvec, tid, nthr);
+  const int64_t rowoff = t * (int64_t)nvec;
+  const int off = tid * kVecBytes;  // vector v at off + v * nthr * 16
+  const int row_bytes = nvec * kVecBytes;
+  auto rsrc = [&](const u32x4* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(p + rowoff), (short)0, row_bytes, kBufferConfig);
+  };
+  const __amdgpu_buffer_rsrc_t r_inter = rsrc(inter), r_lo = rsrc(layer_out), r_slot = rsrc(slot);
+  u32x4 R[kV], f[kV], xp[kV];
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    R[v] = load_nt(r_inter, off + v * nthr * kVecBytes);
+    f[v] = load_nt(r_lo, off + v * nthr * kVecBytes);
+    if constexpr (kAdd) xp[v] = load_nt(r_slot, off + v * nthr * kVecBytes);
+  }
+  const __amdgpu_buffer_rsrc_t r_logits =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(logits + t * K), (short)0, K * 4, kBufferConfig);
+  const float zl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_logits, s16 * 4, 0, 0));
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    xp[v] = kAdd ? add_rows(xp[v], f[v], true) : f[v];
+    store_nt(xp[v], r_slot, off + v * nthr * kVecBytes);
+  }
+  const float zi = (s16 < K) ? zl : -INFINITY;
+
+  Query<true, kV> q;
+  finish_query<true, kV>(q, ql);
+  float ss = 0.f, dt = 0.f;
+#pragma unroll
+  for (int v = 0; v < kV; ++v)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ss = dot2(xp[v][k], xp[v][k], ss);
+      dt = dot2(xp[v][k], q.hi[v][k], dt);
+      dt = dot2(xp[v][k], q.lo[v][k], dt);
+    }
+  ss = wave_sum(ss);
+  dt = wave_sum(dt);
+  if (lane == 0) {
+    red[wave][0] = ss;
+    red[wave][1] = dt;
+  }
+  __syncthreads();
+  float ssp = 0.f, dtp = 0.f;
+  for (int k = 0; k < nwaves; ++k) {
+    ssp += red[k][0];
+    dtp += red[k][1];
+  }
+  const float zp = dtp / sqrtf(ssp * inv_d + eps);
+
+  // inter-block statistics from the stored logits, then the online merge
+  const float mi = row_max16(zi);
+  const float li = row_sum16((s16 < K) ? expf(zi - mi) : 0.f);
+  const float M = fmaxf(mi, zp);
+  const float A = li * expf(mi - M);
+  const float P = expf(zp - M);
+  const float inv = 1.0f / (A + P);
+  const float ca = A * inv, cp = P * inv;
+  if (weights != nullptr && wave == 0) {
+    if (lane < K) weights[t * (K + 1) + lane] = expf(zi - M) * inv;
+    if (lane == K) weights[t * (K + 1) + K] = cp;
+  }
+  const __amdgpu_buffer_rsrc_t r_out = rsrc(out);
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[k] = pack_bf16(fmaf(cp, bf16_lo(xp[v][k]), ca * bf16_lo(R[v][k])),
+                       fmaf(cp, bf16_hi(xp[v][k]), ca * bf16_hi(R[v][k])));
+    }
+    store_nt(o, r_out, off + v * nthr * kVecBytes);
+  }
+}
+
 // Prepared queries: groups of 4 queries, [G][plane: hi, lo][chunk][4][8] bf16,
 // G = ceil(n / 4), queries past n zero.  One thread per (query, chunk).
 __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restrict__ w, int n, int nvec,
@@ -539,6 +638,19 @@ hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
 template <int kV, bool kAdd>
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int nvec = a.d / 8;
+  if (a.per_token) {
+    // one workgroup per token, at most a.grid tokens per launch
+    for (int64_t t0 = 0; t0 < a.T; t0 += a.grid) {
+      const int64_t n = a.T - t0 < a.grid ? a.T - t0 : a.grid;
+      hipLaunchKernelGGL((merge_token_kernel<kV, kAdd>), dim3((unsigned)n), dim3(a.threads), 0, stream,
+                         static_cast<u32x4*>(a.slot), static_cast<const u32x4*>(a.layer_out),
+                         static_cast<const u32x4*>(a.inter), a.logits, a.K, a.T, t0, nvec, a.w,
+                         static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   hipLaunchKernelGGL((merge_kernel<kV, kAdd>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
                      static_cast<u32x4*>(a.slot), static_cast<const u32x4*>(a.layer_out),
                      static_cast<const u32x4*>(a.inter), a.logits, a.K, a.T, nvec, a.w,

@@ -128,6 +128,33 @@ def test_merge_matches_oracle_through_a_block(T, d):
                 extra_rounding=weighted_abs(Hi, a_ref, K))
 
 
+@pytest.mark.parametrize("add", [False, True])
+def test_merge_forms_bit_identical(add):
+    """Small batches take the per-token merge (every load of a token issued up
+    front), larger ones the looping form; the arithmetic is the same, so the
+    first 500 tokens of a 600-token merge (looping form) equal a 500-token
+    merge of the same rows (per-token form) bit for bit, in the partial slot,
+    the residual and the weights."""
+    dev = device()
+    d, K = 7168, 5
+    big, small = 600, 500
+    st = _store(big, d, 31, K - 1, add, dev)   # K inter-block sources; the partial is slot K
+    W = synth.query(d, seed=3, device=dev, tag=70)
+    F = synth.layer_output(big, d, std=0.3, seed=3, tag=71, device=dev)
+    inter = synth.layer_output(big, d, std=1.0, seed=3, tag=72, device=dev)
+    logits = torch.randn((big, K), generator=torch.Generator(device=dev).manual_seed(5), device=dev)
+    st_s = B.SourceStore(small, d, dtype=torch.bfloat16, device=dev,
+                         slots=st.slots[:, :small].contiguous())
+    st_s.set_state(st.n_completed, st.partial_valid)
+    note(f"merge forms add={add}: T={big} (looping) and T={small} (per token)")
+    out_b, w_b = st.block_merge(F, W, inter, logits)
+    out_s, w_s = st_s.block_merge(F[:small].contiguous(), W, inter[:small].contiguous(), logits[:small].contiguous())
+    torch.cuda.synchronize()
+    assert same_bits(st.slots[K, :small], host(st_s.slots[K])), "partial slot"
+    assert same_bits(out_b[:small], host(out_s)), "residual"
+    assert same_bits(w_b[:small], host(w_s)), "weights"
+
+
 def test_merge_in_place_over_the_inter_row():
     dev = device()
     T, d, K = 33, 7168, 4
