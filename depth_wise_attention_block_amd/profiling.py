@@ -8,6 +8,7 @@
     python -m depth_wise_attention_block_amd.profiling pass \
         --fetch FETCH.csv --write WRITE.csv --fetch-cmd "..." --write-cmd "..." \
         --T T --d D --algorithmic BYTES --label NAME --out X.json
+    python -m depth_wise_attention_block_amd.profiling markers --csv MARKER_API_TRACE.csv --cmd "..." --out X.txt
 
 ``counters`` calibrates each counter with the plain-copy kernel that
 ``bench.py --with-copy`` launches in every run (it moves a known T*d bf16 in and
@@ -224,6 +225,30 @@ def pass_summary(fetch_csv: str, write_csv: str, fetch_cmd: str, write_cmd: str,
     }
 
 
+def marker_summary(csv_path: str, cmd: str, out_path: str) -> None:
+    """Tally the roctx ranges of a ``rocprofv3 --marker-trace`` run by kind (the
+    range name without its trailing number): count and host time."""
+    import re
+    kinds = {}
+    order = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            kind = re.sub(r" \d+$", "", r["Function"])
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if kind not in kinds:
+                kinds[kind] = [0, 0.0]
+                order.append(kind)
+            kinds[kind][0] += 1
+            kinds[kind][1] += us
+    lines = ["# roctx ranges (host enqueue time of each schedule step), by kind", f"# command: {cmd}", "#",
+             f"# {'range':<40} {'count':>6} {'total_us':>12} {'avg_us':>10}"]
+    for k in order:
+        n, tot = kinds[k]
+        lines.append(f"  {k[:40]:<40} {n:>6} {tot:>12.1f} {tot / n:>10.1f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = p.add_subparsers(dest="what", required=True)
@@ -247,7 +272,14 @@ def main():
     q.add_argument("--T", type=int, required=True)
     q.add_argument("--d", type=int, default=7168)
     q.add_argument("--algorithmic", type=int, required=True, help="algorithmic bytes of one pass")
+    mk = sub.add_parser("markers")
+    mk.add_argument("--csv", required=True)
+    mk.add_argument("--cmd", required=True)
+    mk.add_argument("--out", required=True)
     a = p.parse_args()
+    if a.what == "markers":
+        marker_summary(a.csv, a.cmd, a.out)
+        return
     if a.what == "pass":
         s = pass_summary(a.fetch, a.write, a.fetch_cmd, a.write_cmd, a.T, a.d, a.algorithmic, a.label)
         with open(a.out, "w") as f:

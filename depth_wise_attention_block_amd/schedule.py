@@ -22,6 +22,7 @@ from typing import Callable, Optional, Sequence
 
 import torch
 
+from . import markers
 from .binding import MAX_BLOCK_QUERIES, MAX_INTER_SOURCES, SourceStore, aggregate, split_queries
 
 
@@ -97,13 +98,16 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
 
     if not fused:
         for l in range(1, num_layers + 1):
-            r, a = rbuf(l), wview(l, store.num_sources())
-            aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
+            with markers.span("layer", l):
+                r, a = rbuf(l), wview(l, store.num_sources())
+                aggregate(store.sources(), queries[l - 1], r, a, want_weights=a is not None, eps=eps)
             if on_layer is not None:
                 on_layer(l, r, a)
-            store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
+            with markers.span("update", l):
+                store.accumulate(layer_outputs[l - 1], closes_block(l, num_layers, block_size))
         if final_query is not None:
-            return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
+            with markers.span("output layer"):
+                return aggregate(store.sources(), final_query, final_out, final_weights, eps=eps)
         return None
 
     num_blocks = (num_layers + block_size - 1) // block_size
@@ -119,47 +123,50 @@ def run_schedule(store: SourceStore, layer_outputs: Sequence[torch.Tensor], quer
     for l in range(1, num_layers + 1):
         n, i = (l - 1) // block_size + 1, (l - 1) % block_size + 1
         last = min(n * block_size, num_layers)
-        if n in two_phase and i == 1:
-            B = last - l + 1
-            K = n  # h_0 and b_1..b_{n-1} once the previous block is closed
-            if queries_split is not None and queries_split[n - 1] is not None:
-                W = queries_split[n - 1]
+        with markers.span("layer", l):
+            if n in two_phase and i == 1:
+                B = last - l + 1
+                K = n  # h_0 and b_1..b_{n-1} once the previous block is closed
+                if queries_split is not None and queries_split[n - 1] is not None:
+                    W = queries_split[n - 1]
+                else:
+                    W = split_queries(torch.stack([queries[j] for j in range(l - 1, last)]))
+                block_rows = out[l - 1:last] if out.dim() == 3 else inter[:B]
+                lg_buf = logits if out.dim() != 3 else None
+                if lg_buf is None:
+                    lg_buf = torch.empty(B * T * K, dtype=torch.float32, device=dev)
+                block_logits = lg_buf[: B * T * K].view(B, T, K)
+                a = wview(l, K)
+                # one pass per MAX_BLOCK_QUERIES queries (groups of four in W); only
+                # the first closes the previous block
+                for q0 in range(0, B, MAX_BLOCK_QUERIES):
+                    q1 = min(q0 + MAX_BLOCK_QUERIES, B)
+                    first = q0 == 0
+                    with markers.span("inter-block pass of block", n):
+                        store.block_prepare(layer_outputs[l - 2] if first and l > 1 else None, first and l > 1,
+                                            W[q0 // 4:(q1 + 3) // 4], block_rows[q0:q1], block_logits[q0:q1],
+                                            a if first else None, eps=eps)
+                r = block_rows[0]
+            elif n in two_phase:
+                a = wview(l, n + 1)
+                r = rbuf(l)
+                store.block_merge(layer_outputs[l - 2], queries[l - 1], block_rows[i - 1], block_logits[i - 1],
+                                  out=r, weights=a, want_weights=a is not None, eps=eps)
+            elif l == 1:
+                r, a = rbuf(l), wview(l, store.num_sources())
+                aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
             else:
-                W = split_queries(torch.stack([queries[j] for j in range(l - 1, last)]))
-            block_rows = out[l - 1:last] if out.dim() == 3 else inter[:B]
-            lg_buf = logits if out.dim() != 3 else None
-            if lg_buf is None:
-                lg_buf = torch.empty(B * T * K, dtype=torch.float32, device=dev)
-            block_logits = lg_buf[: B * T * K].view(B, T, K)
-            a = wview(l, K)
-            # one pass per MAX_BLOCK_QUERIES queries (groups of four in W); only
-            # the first closes the previous block
-            for q0 in range(0, B, MAX_BLOCK_QUERIES):
-                q1 = min(q0 + MAX_BLOCK_QUERIES, B)
-                first = q0 == 0
-                store.block_prepare(layer_outputs[l - 2] if first and l > 1 else None, first and l > 1,
-                                    W[q0 // 4:(q1 + 3) // 4], block_rows[q0:q1], block_logits[q0:q1],
-                                    a if first else None, eps=eps)
-            r = block_rows[0]
-        elif n in two_phase:
-            a = wview(l, n + 1)
-            r = rbuf(l)
-            store.block_merge(layer_outputs[l - 2], queries[l - 1], block_rows[i - 1], block_logits[i - 1],
-                              out=r, weights=a, want_weights=a is not None, eps=eps)
-        elif l == 1:
-            r, a = rbuf(l), wview(l, store.num_sources())
-            aggregate(store.sources(), queries[0], r, a, want_weights=a is not None, eps=eps)
-        else:
-            closes = closes_block(l - 1, num_layers, block_size)
-            S = 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
-            r, a = rbuf(l), wview(l, S)
-            store.accumulate_aggregate(layer_outputs[l - 2], closes, queries[l - 1], r, a,
-                                       want_weights=a is not None, eps=eps)
+                closes = closes_block(l - 1, num_layers, block_size)
+                S = 1 + store.n_completed + (1 if closes else 0) + (0 if closes else 1)
+                r, a = rbuf(l), wview(l, S)
+                store.accumulate_aggregate(layer_outputs[l - 2], closes, queries[l - 1], r, a,
+                                           want_weights=a is not None, eps=eps)
         if on_layer is not None:
             on_layer(l, r, a)
-    if final_query is not None:
-        return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps)
-    store.accumulate(layer_outputs[-1], True)
+    with markers.span("output layer"):
+        if final_query is not None:
+            return store.accumulate_aggregate(layer_outputs[-1], True, final_query, final_out, final_weights, eps=eps)
+        store.accumulate(layer_outputs[-1], True)
     return None
 
 
@@ -262,22 +269,23 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         Bc = block_layers(n)
         return coef_all[:T * Bc * n * 3].view(T, Bc, n, 3)
 
-    if final_query is not None:
-        S = 1 + nblocks
-        if final_in_block:
-            # h_0 .. b_{N-1} deferred to the last block's pass (its last layer
-            # slot); only b_N's gradient row is written here
-            N, Bc = nblocks, block_layers(nblocks)
-            aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=0,
-                               defer=(1 << N) - 1, coef=block_coef(N).view(-1)[3 * N * (Bc - 1):],
-                               coef_stride=3 * N * Bc, grad_w=grad_w_final, grad_last=dF, eps=eps)
-            holds[N] = True
+    with markers.span("output layer backward"):
+        if final_query is not None:
+            S = 1 + nblocks
+            if final_in_block:
+                # h_0 .. b_{N-1} deferred to the last block's pass (its last layer
+                # slot); only b_N's gradient row is written here
+                N, Bc = nblocks, block_layers(nblocks)
+                aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=0,
+                                   defer=(1 << N) - 1, coef=block_coef(N).view(-1)[3 * N * (Bc - 1):],
+                                   coef_stride=3 * N * Bc, grad_w=grad_w_final, grad_last=dF, eps=eps)
+                holds[N] = True
+            else:
+                aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
+                                   grad_w=grad_w_final, grad_last=dF, eps=eps)
+                holds[:S] = [True] * S
         else:
-            aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
-                               grad_w=grad_w_final, grad_last=dF, eps=eps)
-            holds[:S] = [True] * S
-    else:
-        dF.zero_()
+            dF.zero_()
     if on_grad is not None:
         on_grad(L, dF)
     for n in range(nblocks, 0, -1):
@@ -286,7 +294,8 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         B = last - first + 1
         # the block's partial sums, formed exactly as the forward formed them
         if B >= 2:
-            partial_sums([layer_outputs[j - 1] for j in range(first, last)], partials)
+            with markers.span("partial sums of block", n):
+                partial_sums([layer_outputs[j - 1] for j in range(first, last)], partials)
         coef = block_coef(n) if defer else None
         Bc = coef.shape[1] if defer else B
         block_g = [None] * B
@@ -295,16 +304,17 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
             g = dr(l)
             block_g[i - 1] = g
             cf = dict(defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * (i - 1):], coef_stride=3 * n * Bc) if defer else {}
-            if i >= 2:
-                rows = list(range(n + 1))
-                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n + 1], last_source=partials[i - 2],
-                                   accumulate=acc_mask(rows), grad_w=grad_w[l - 1], grad_last=dF, eps=eps, **cf)
-                touched = rows if not defer else [n]
-            else:
-                rows = list(range(n))
-                aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n], accumulate=acc_mask(rows),
-                                   grad_w=grad_w[l - 1], grad_last=None if defer else dF, eps=eps, **cf)
-                touched = [] if defer else rows
+            with markers.span("layer backward", l):
+                if i >= 2:
+                    rows = list(range(n + 1))
+                    aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n + 1], last_source=partials[i - 2],
+                                       accumulate=acc_mask(rows), grad_w=grad_w[l - 1], grad_last=dF, eps=eps, **cf)
+                    touched = rows if not defer else [n]
+                else:
+                    rows = list(range(n))
+                    aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n], accumulate=acc_mask(rows),
+                                       grad_w=grad_w[l - 1], grad_last=None if defer else dF, eps=eps, **cf)
+                    touched = [] if defer else rows
             for r in touched:
                 holds[r] = True
             if on_grad is not None and (i >= 2 or not defer):
@@ -314,8 +324,9 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
             dws = [grad_w[j - 1] for j in range(first, last + 1)]
             if Bc > B:   # the final aggregation, in the last slot
                 block_g, qs, dws = block_g + [grad_final], qs + [final_query], dws + [grad_w_final]
-            block_backward(slots[:n], block_g, qs, coef, grad_store[:n], dws, accumulate=acc_mask(range(n)),
-                           grad_last=dF)
+            with markers.span("gradient rows of block", n):
+                block_backward(slots[:n], block_g, qs, coef, grad_store[:n], dws, accumulate=acc_mask(range(n)),
+                               grad_last=dF)
             holds[:n] = [True] * n
             if on_grad is not None:
                 on_grad(first - 1, dF)
