@@ -8,7 +8,10 @@
 // of a block (2 streams).  Closing a block moves no data: the slot simply
 // becomes the block representation (kimi.papertok.ai §4.6: produced once at
 // the boundary, then resident).  Element-wise and HBM-bound: 16-byte vectors,
-// several independent vectors per lane per trip to keep loads in flight.
+// several independent vectors per lane to keep loads in flight, and one trip
+// per workgroup: a grid that loops workgroups over the row keeps each trip's
+// loads queued behind the previous trip's stores (16 workgroups per CU measured
+// 6% slower at 3.76 GB per stream: 2.029 against 1.912 ms).
 #include "device_common.h"
 #include "internal.h"
 
@@ -51,8 +54,10 @@ accumulate_kernel(const u32x4* partial, const u32x4* __restrict__ layer_out, u32
 hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream) {
   const int64_t nvec = a.elems / (a.bf16 ? 8 : 4);
   const int64_t chunk = (int64_t)kThreads * kUnroll;
+  // one trip per workgroup up to the largest grid a launch takes (beyond it,
+  // ~2^41 vectors, the workgroups loop)
   int64_t grid = (nvec + chunk - 1) / chunk;
-  const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 16;
+  const int64_t cap = INT64_C(0x7fffffff);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   const u32x4* p = static_cast<const u32x4*>(a.partial);

@@ -936,8 +936,12 @@ hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream)
 hipError_t launch_partial_sums(const PartialSumsArgs& a, hipStream_t stream) {
   const int64_t nvec = a.elems / (a.bf16 ? 8 : 4);
   if (nvec == 0) return hipSuccess;
+  // one trip per workgroup up to the largest grid a launch takes: a grid that
+  // loops its workgroups over the rows queues each trip's loads behind the
+  // previous trip's stores (8 workgroups per CU measured 14% slower for 11
+  // rows of T = 32,768, d = 7168: 2.148 against 1.838 ms)
   int64_t grid = (nvec + 255) / 256;
-  const int64_t cap = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * 8;
+  const int64_t cap = INT64_C(0x7fffffff);
   if (grid > cap) grid = cap;
   if (a.bf16)
     hipLaunchKernelGGL((partial_sums_kernel<true>), dim3((unsigned)grid), dim3(256), 0, stream, a.rows, a.count,

@@ -460,15 +460,11 @@ ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t coun
     if (overlap(r_out, range(layer_outs[k], row * es))) return ATTNRES_EALIAS;
     a.rows.g[k] = layer_outs[k];
   }
-  int cus = 0;
-  rc = device_cus(&cus);
-  if (rc != ATTNRES_OK) return rc;
   a.count = count;
   a.elems = row;
   a.out = out;
   a.out_stride = out_stride;
   a.bf16 = dtype == ATTNRES_BF16;
-  a.num_cus = cus;
   (void)hipGetLastError();
   return attnres::launch_partial_sums(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                          : ATTNRES_ELAUNCH;
@@ -723,9 +719,6 @@ ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_
   // out may be a itself (in place), not b, and no partial overlap with either
   if (overlap(r_out, range(b, row * es))) return ATTNRES_EALIAS;
   if (a != nullptr && a != out && overlap(r_out, range(a, row * es))) return ATTNRES_EALIAS;
-  int cus = 0;
-  rc = device_cus(&cus);
-  if (rc != ATTNRES_OK) return rc;
   attnres::AccumulateArgs args;
   args.partial = const_cast<void*>(a);
   args.layer_out = b;
@@ -733,7 +726,6 @@ ATTNRES_API int attnres_add_rows(const void* a, const void* b, void* out, int64_
   args.elems = row;
   args.bf16 = dtype == ATTNRES_BF16;
   args.copy = a == nullptr;
-  args.num_cus = cus;
   (void)hipGetLastError();
   return attnres::launch_accumulate(args, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                           : ATTNRES_ELAUNCH;
@@ -753,9 +745,6 @@ ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out, i
     if (!aligned16(layer_out)) return ATTNRES_EUNSUPPORTED;
     const Range r_store = range(st->base, ((int64_t)(st->s_max - 1) * st->slot_stride + row) * es);
     if (overlap(range(layer_out, row * es), r_store)) return ATTNRES_EALIAS;
-    int cus = 0;
-    rc = device_cus(&cus);
-    if (rc != ATTNRES_OK) return rc;
     attnres::AccumulateArgs a;
     a.partial = static_cast<char*>(st->base) + (int64_t)slot * st->slot_stride * es;
     a.layer_out = layer_out;
@@ -763,7 +752,6 @@ ATTNRES_API int attnres_accumulate(attnres_store_t* st, const void* layer_out, i
     a.elems = row;
     a.bf16 = st->dtype == ATTNRES_BF16;
     a.copy = st->partial_valid == 0;
-    a.num_cus = cus;
     (void)hipGetLastError();
     if (attnres::launch_accumulate(a, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTNRES_ELAUNCH;
   }

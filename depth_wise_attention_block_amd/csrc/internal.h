@@ -51,7 +51,6 @@ struct AccumulateArgs {
   int64_t elems;        // T*d
   bool bf16;
   bool copy;            // true: partial = layer_out (first layer of a block)
-  int num_cus;
 };
 
 hipError_t launch_accumulate(const AccumulateArgs& a, hipStream_t stream);
@@ -190,7 +189,6 @@ struct PartialSumsArgs {
   void* out;            // count rows at out_stride elements
   int64_t out_stride;
   bool bf16;
-  int num_cus;
 };
 
 hipError_t launch_partial_sums(const PartialSumsArgs& a, hipStream_t stream);
