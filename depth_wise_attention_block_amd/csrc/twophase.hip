@@ -621,6 +621,7 @@ __global__ void __launch_bounds__(256) split_queries_kernel(const float* __restr
 template <int kV, int kClose, int kK>
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
   const int nvec = a.d / 8;
+  if (a.grid <= 0) return hipErrorInvalidValue;
   // one workgroup per token, at most a.grid tokens per launch
   for (int64_t t0 = 0; t0 < a.T; t0 += a.grid) {
     const int64_t n = a.T - t0 < a.grid ? a.T - t0 : a.grid;
@@ -638,6 +639,7 @@ hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
 template <int kV, bool kAdd>
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int nvec = a.d / 8;
+  if (a.grid <= 0) return hipErrorInvalidValue;
   if (a.per_token) {
     // one workgroup per token, at most a.grid tokens per launch
     for (int64_t t0 = 0; t0 < a.T; t0 += a.grid) {
