@@ -21,8 +21,10 @@
 //   * the query's float32 loads are issued with the rows' and converted to
 //     bf16 hi + lo only after all of them are in flight, so that a token costs
 //     one memory round trip (at decode sizes that round trip is the kernel);
-//   * 2*S wave sums by DPP (row butterfly, then row_bcast15/31), one LDS
-//     exchange across waves and ONE barrier per token;
+//   * the 2*S per-lane sums reduced over each 16-lane row together by DPP
+//     exchanges that halve the values a lane holds (a ninth source by two
+//     plain row sums), one LDS exchange of every row's partials and ONE
+//     barrier per token;
 //   * logits, max, exponentials and the normaliser are computed by lanes
 //     0..S-1 of each 16-lane row and broadcast with readlane; the softmax is
 //     exact here because all S scores are known before the weighted sum.  (The
@@ -70,8 +72,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_pe
 aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                  const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
                  float eps, float inv_d, const u32x4* __restrict__ layer_out, int64_t b0, int run_log2) {
-  // [wave][sum of squares | w.x][source]
-  __shared__ float red[kMaxWaves][2][16];
+  // [statistic][part]: per 16-lane row of every wave (part 4 * wave + row),
+  // the row's sum of each source's sum of squares (statistic s, or 2 kP for a
+  // ninth source) and w.x (kP + s, or 2 kP + 1)
+  constexpr int kP = kMaxS > 8 ? 8 : kMaxS > 2 ? 4 : 2;  // sources reduced together
+  static_assert(kMaxS <= kP + 1, "at most one source beyond the reduced ones");
+  constexpr int kParts = 4 * kMaxWaves;
+  __shared__ __align__(16) float red[2 * kP + 2][kParts];
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -131,14 +138,18 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
       }
     }
 
-    // 2. per-lane partial statistics, then wave sums
+    // 2. per-lane partial statistics, then row sums
     Query<kBf16, kV> q;
     finish_query<kBf16, kV>(q, ql);
-    float gss = 0.f, gdt = 0.f;  // lane s of the row: source s's wave sums
+    // the first kP sources' two sums per lane, reduced over each 16-lane row
+    // together (lane i of a row ends with value i: source i's sum of squares,
+    // then w.x of source i - kP); a ninth source takes two plain row sums
+    float st[2 * kP];
+    float ss9 = 0.f, dt9 = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxS; ++s) {
+      float ss = 0.f, dt = 0.f;
       if (s < S) {
-        float ss = 0.f, dt = 0.f;
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
           if constexpr (kBf16) {
@@ -157,25 +168,42 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
             }
           }
         }
-        gss = put_lane(wave_sum(ss), s, gss, s16);
-        gdt = put_lane(wave_sum(dt), s, gdt, s16);
+      }
+      if (s < kP) {
+        st[s] = ss;
+        st[kP + s] = dt;
+      } else {
+        ss9 = ss;
+        dt9 = dt;
       }
     }
+    const float rs = row_sums<2 * kP>(st, lane);
 
-    // 3. combine the waves: one LDS exchange, one barrier
-    if (lane < 16) {
-      red[wave][0][lane] = gss;
-      red[wave][1][lane] = gdt;
+    // 3. combine the rows of all waves: one LDS exchange, one barrier
+    const int part = 4 * wave + (lane >> 4);
+    if (s16 < 2 * kP) red[s16][part] = rs;
+    if constexpr (kMaxS > kP) {
+      if (S > kP) {
+        ss9 = row_sum16(ss9);
+        dt9 = row_sum16(dt9);
+        if (s16 == 0) {
+          red[2 * kP][part] = ss9;
+          red[2 * kP + 1][part] = dt9;
+        }
+      }
     }
     __syncthreads();
 
     // 4. logits and softmax over depth, lanes s16 < S of every row
     float z = -INFINITY;
     if (s16 < S) {
+      const int is = s16 < kP ? s16 : 2 * kP, id = s16 < kP ? kP + s16 : 2 * kP + 1;
       float ss = 0.f, dt = 0.f;
-      for (int k = 0; k < nwaves; ++k) {
-        ss += red[k][0][s16];
-        dt += red[k][1][s16];
+      for (int p = 0; p < 4 * nwaves; p += 4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&red[is][p]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&red[id][p]);
+        ss += (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        dt += (d4[0] + d4[1]) + (d4[2] + d4[3]);
       }
       z = dt / sqrtf(ss * inv_d + eps);
     }

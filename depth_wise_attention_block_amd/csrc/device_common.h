@@ -114,6 +114,50 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// One step of wave_sums: lane pairs (partner by kCtrl, differing in lane bit
+// `bit`) halve the values each holds: a lane keeps the entries whose index has
+// its own bit and adds the partner's copies of them.
+template <int kCtrl, int M>
+__device__ __forceinline__ void halve_values(const float (&cur)[2 * M], float (&nxt)[M], bool bit) {
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const float keep = bit ? cur[2 * j + 1] : cur[2 * j];
+    const float send = bit ? cur[2 * j] : cur[2 * j + 1];
+    nxt[j] = keep + dpp<kCtrl>(send, send);
+  }
+}
+
+// Sums over each 16-lane row of N = 4, 8 or 16 values at once: lane L ends
+// with its row's sum of v[L % N].  Exchanges across lane bits 0, 1 (quad
+// permutes) and 2, 3 (rotations of the row) halve the values a lane holds, and
+// plain sums cover the row's remaining bits: about 1.5 N operations where N
+// separate row sums take 4 N.  The four rows of a wave are left apart (a
+// caller combines them through LDS).  Fixed order, so deterministic.
+template <int N>
+__device__ __forceinline__ float row_sums(const float (&v)[N], int lane) {
+  static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 values");
+  if constexpr (N == 16) {
+    float a[8], b[4], c[2], e[1];
+    halve_values<kDppXor1, 8>(v, a, lane & 1);
+    halve_values<kDppXor2, 4>(a, b, lane & 2);
+    halve_values<kDppRor4, 2>(b, c, lane & 4);
+    halve_values<kDppRor8, 1>(c, e, lane & 8);
+    return e[0];
+  } else if constexpr (N == 8) {
+    float a[4], b[2], c[1];
+    halve_values<kDppXor1, 4>(v, a, lane & 1);
+    halve_values<kDppXor2, 2>(a, b, lane & 2);
+    halve_values<kDppRor4, 1>(b, c, lane & 4);
+    return c[0] + dpp<kDppRor8>(c[0], c[0]);
+  } else {
+    float a[2], b[1];
+    halve_values<kDppXor1, 2>(v, a, lane & 1);
+    halve_values<kDppXor2, 1>(a, b, lane & 2);
+    const float x = b[0] + dpp<kDppRor4>(b[0], b[0]);
+    return x + dpp<kDppRor8>(x, x);
+  }
+}
+
 __device__ __forceinline__ float lane_bcast(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
