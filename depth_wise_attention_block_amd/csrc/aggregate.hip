@@ -290,7 +290,11 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
                       const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
                       float eps, float inv_d) {
   constexpr int kB = many_batch<kV>();
-  __shared__ float red[2][kMaxWaves][2][16];
+  // a batch's statistics reduced per 16-lane row as in aggregate_kernel: the
+  // first kP sources together, one more by plain row sums; [buffer][statistic][part]
+  constexpr int kP = kB > 8 ? 8 : kB > 4 ? 4 : 2;
+  static_assert(kB == kP + 1, "one source beyond the reduced ones");
+  __shared__ __align__(16) float red[2][2 * kP + 2][4 * kMaxWaves];
   __shared__ float zbuf[kMaxSourcesMany];
 
   const int tid = threadIdx.x;
@@ -334,11 +338,12 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
     auto batch = [&](u32x4 (&x)[kB][kV], u32x4 (&xn)[kB][kV], int b) {
       const int s0 = b * kB;
       const int nb = min(kB, S - s0);
-      float gss = 0.f, gdt = 0.f;
+      float st[2 * kP];
+      float ssx = 0.f, dtx = 0.f;
 #pragma unroll
       for (int s = 0; s < kB; ++s) {
+        float ss = 0.f, dt = 0.f;
         if (s < nb) {
-          float ss = 0.f, dt = 0.f;
 #pragma unroll
           for (int v = 0; v < kV; ++v) {
             if constexpr (kBf16) {
@@ -357,22 +362,38 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
               }
             }
           }
-          gss = put_lane(wave_sum(ss), s, gss, s16);
-          gdt = put_lane(wave_sum(dt), s, gdt, s16);
+        }
+        if (s < kP) {
+          st[s] = ss;
+          st[kP + s] = dt;
+        } else {
+          ssx = ss;
+          dtx = dt;
         }
       }
+      const float rs = row_sums<2 * kP>(st, lane);
+      const bool extra = nb > kP;
+      if (extra) {
+        ssx = row_sum16(ssx);
+        dtx = row_sum16(dtx);
+      }
       if (b + 1 < nbatches) load_batch(xn, b + 1);
-      if (lane < 16) {
-        red[buf][wave][0][lane] = gss;
-        red[buf][wave][1][lane] = gdt;
+      const int part = 4 * wave + (lane >> 4);
+      if (s16 < 2 * kP) red[buf][s16][part] = rs;
+      if (extra && s16 == 0) {
+        red[buf][2 * kP][part] = ssx;
+        red[buf][2 * kP + 1][part] = dtx;
       }
       __syncthreads();
       float z = -INFINITY;
       if (s16 < nb) {
+        const int is = s16 < kP ? s16 : 2 * kP, id = s16 < kP ? kP + s16 : 2 * kP + 1;
         float ss = 0.f, dt = 0.f;
-        for (int k = 0; k < nwaves; ++k) {
-          ss += red[buf][k][0][s16];
-          dt += red[buf][k][1][s16];
+        for (int p = 0; p < 4 * nwaves; p += 4) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(&red[buf][is][p]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&red[buf][id][p]);
+          ss += (a4[0] + a4[1]) + (a4[2] + a4[3]);
+          dt += (d4[0] + d4[1]) + (d4[2] + d4[3]);
         }
         z = dt / sqrtf(ss * inv_d + eps);
         if (wave == 0 && lane < 16) zbuf[s0 + s16] = z;
