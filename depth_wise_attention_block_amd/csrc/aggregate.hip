@@ -288,7 +288,7 @@ template <bool kBf16, int kV>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(waves_per_simd_many<kV>())))
 aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                       const float* __restrict__ w, u32x4* __restrict__ out, float* __restrict__ weights,
-                      float eps, float inv_d) {
+                      float eps, float inv_d, int64_t span, int run_log2) {
   constexpr int kB = many_batch<kV>();
   // a batch's statistics reduced per 16-lane row as in aggregate_kernel: the
   // first kP sources together, one more by plain row sums; [buffer][statistic][part]
@@ -310,7 +310,12 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
   const int nbatches = (S + kB - 1) / kB;
 
   int buf = 0;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  // virtual indices blockIdx.x, + gridDim.x, ... below span (T rounded up to
+  // whole XCD runs; the grid is a multiple of 8 with runs, so a workgroup
+  // stays on its XCD's runs)
+  for (int64_t vb = blockIdx.x; vb < span; vb += gridDim.x) {
+    const int64_t t = xcd_token(vb, run_log2);
+    if (t >= T) continue;
     const u32x4* tok = src + t * (int64_t)nvec;
     float m = -INFINITY, l = 0.f;
     float acc[kV][kE];
@@ -462,11 +467,17 @@ aggregate_many_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec,
 
 template <bool kBf16, int kV>
 hipError_t launch_many(const AggregateArgs& a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
   const int epv = kBf16 ? 8 : 4;
   const int nvec = a.d / epv;
+  const int run_log2 = __builtin_ctz((unsigned)a.xcd_run);
+  const int64_t run8 = 8 * (int64_t)a.xcd_run;
+  const int64_t span = a.xcd_run > 1 ? (a.T + run8 - 1) / run8 * run8 : a.T;
+  if ((a.xcd_run & (a.xcd_run - 1)) != 0 || a.grid <= 0 || (a.xcd_run > 1 && a.grid % 8 != 0))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((aggregate_many_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
                      static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / epv, a.w,
-                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d);
+                     static_cast<u32x4*>(a.out), a.weights, a.eps, 1.0f / (float)a.d, span, run_log2);
   return hipGetLastError();
 }
 

@@ -107,7 +107,7 @@ ATTNRES_API int attnres_aggregate_config(int32_t S, int64_t T, int32_t d, int32_
   if (S < 1 || S > ATTNRES_MAX_SOURCES_FULL) return ATTNRES_EINVAL;
   const int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
-  return pick_config(S, T, d, dtype, num_cus, cfg, S <= ATTNRES_MAX_SOURCES);
+  return pick_config(S, T, d, dtype, num_cus, cfg, true);
 }
 
 ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
@@ -141,7 +141,7 @@ ATTNRES_API int attnres_aggregate(const void* sources, int32_t S, int64_t T, int
   rc = device_cus(&cus);
   if (rc != ATTNRES_OK) return rc;
   attnres_launch_t cfg;
-  rc = pick_config(S, T, d, dtype, cus, &cfg, S <= ATTNRES_MAX_SOURCES);
+  rc = pick_config(S, T, d, dtype, cus, &cfg, true);
   if (rc != ATTNRES_OK) return rc;
 
   attnres::AggregateArgs a;

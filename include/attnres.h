@@ -411,8 +411,9 @@ typedef struct attnres_launch {
   int32_t xcd_run;          /* consecutive tokens each XCD takes in turn: the
                                workgroup of virtual index b (b = blockIdx, plus
                                grid per earlier launch when the batch needs
-                               several launches of at most grid workgroups)
-                               runs on XCD b % 8 and handles
+                               several launches of at most grid workgroups, or
+                               per earlier trip of the workgroup for more than
+                               9 sources) runs on XCD b % 8 and handles
                                token ((b / 8 / r) * 8 + b % 8) * r + (b / 8) % r
                                for r = xcd_run (1: token b); the virtual
                                indices cover T rounded up to 8 r             */

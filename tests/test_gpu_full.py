@@ -62,6 +62,23 @@ def test_many_sources_grid_stride_and_determinism():
     compare(host(o1.index_select(0, idx)), host(a1.index_select(0, idx)), r_ref, a_ref, True, "12 sources, T>grid")
 
 
+def test_many_sources_xcd_runs_with_a_ragged_tail():
+    """From 4,096 tokens on each XCD takes runs of 32 consecutive tokens; a
+    batch that is no multiple of 8 runs leaves the last run partly empty."""
+    dev = device()
+    S, T, d = 20, 4096 + 37, 7168
+    cfg = B.aggregate_config(S, T, d, torch.bfloat16, torch.cuda.get_device_properties(dev).multi_processor_count)
+    assert cfg["xcd_run"] == 32
+    note(f"many sources, XCD runs, S={S} T={T} d={d}")
+    H = synth.sources(S, T, d, seed=6, device=dev)
+    w = synth.query(d, seed=6, device=dev)
+    out, a = B.aggregate(H, w)
+    torch.cuda.synchronize()
+    idx = synth.token_sample(T, 512, 64, seed=6).to(dev)
+    r_ref, a_ref = oracle_aggregate(host(H.index_select(1, idx)), host(w))
+    compare(host(out.index_select(0, idx)), host(a.index_select(0, idx)), r_ref, a_ref, True, "20 sources, runs")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_full_attnres_schedule_matches_oracle(dtype):
     """93 layers, each aggregating h_0 and all earlier outputs (S = 1..93), plus
