@@ -102,12 +102,16 @@ MAX_ORACLE_WORKERS = 16
 ORACLE_CHUNK = 128          # tokens per oracle call, as in the one-thread timing
 
 
-def oracle_workers() -> int:
+def usable_cpus() -> int:
+    """Host CPUs this process may run on (its affinity set, where the OS has one)."""
     try:
-        avail = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        avail = os.cpu_count() or 1
-    return max(1, min(MAX_ORACLE_WORKERS, avail))
+        return os.cpu_count() or 1
+
+
+def oracle_workers() -> int:
+    return max(1, min(MAX_ORACLE_WORKERS, usable_cpus()))
 
 
 def _single_thread_env():
@@ -229,7 +233,7 @@ def cpu_baseline(wl, budget_s: float, seed: int, pool=None, nworkers: int = 1):
         "sample": f"{total} token-steps over a {n_tok}-token sample of the same step (accumulate + 9-source "
                   f"aggregate), float64 NumPy, {nworkers} single-threaded worker processes, {wall:.1f} s wall",
         "single_thread_tokens_per_s": round(one, 1),
-        "host_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+        "host_cpus": os.cpu_count(), "usable_cpus": usable_cpus(),
     })
     return result
 
