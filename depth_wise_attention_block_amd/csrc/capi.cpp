@@ -72,7 +72,7 @@ int check_store(const attnres_store_t* st) {
   if (st == nullptr) return ATTNRES_EINVAL;
   int rc = check_shape(st->T, st->d, st->dtype);
   if (rc != ATTNRES_OK) return rc;
-  if (st->base == nullptr) return ATTNRES_EINVAL;
+  if (st->base == nullptr && st->T > 0) return ATTNRES_EINVAL;  // an empty store holds no rows
   if (!aligned16(st->base)) return ATTNRES_EUNSUPPORTED;
   if (st->s_max < 2 || st->s_max > ATTNRES_MAX_SOURCES) return ATTNRES_EINVAL;
   if (st->slot_stride < st->T * st->d) return ATTNRES_EINVAL;

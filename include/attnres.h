@@ -135,7 +135,8 @@ typedef struct attnres_store {
  * attnres_store_init -- fill *st for caller-owned slots (host only, no HIP
  * call).  slot_stride 0 means T*d.  Counters start at zero: only h_0 is live.
  * Same size/alignment rules as attnres_aggregate; ATTNRES_EINVAL for s_max
- * outside 2..ATTNRES_MAX_SOURCES.
+ * outside 2..ATTNRES_MAX_SOURCES.  base may be NULL only when T = 0: an empty
+ * store, whose calls update the counters and launch nothing.
  */
 ATTNRES_API int attnres_store_init(attnres_store_t* st, void* base, int32_t s_max, int64_t T,
                                    int32_t d, int64_t slot_stride, int32_t dtype);

@@ -152,12 +152,24 @@ def _store(T=0, d=8, s_max=9, base=SRC, stride=0, dtype=B.BF16):
 
 
 @pytest.mark.parametrize("kwargs,status", [
-    (dict(s_max=1), B.EINVAL), (dict(s_max=10), B.EINVAL), (dict(base=None), B.EINVAL),
+    (dict(s_max=1), B.EINVAL), (dict(s_max=10), B.EINVAL), (dict(T=4, base=None), B.EINVAL),
+    (dict(T=0, base=None), B.OK),
     (dict(base=SRC + 2), B.EUNSUPPORTED), (dict(d=12), B.EUNSUPPORTED), (dict(dtype=7), B.EUNSUPPORTED),
     (dict(T=4, d=8, stride=24), B.EINVAL), (dict(T=4, d=8, stride=36), B.EUNSUPPORTED),
 ])
 def test_store_init_checks(lib, kwargs, status):
     assert _store(**kwargs)[0] == status
+
+
+def test_empty_store_without_memory(lib):
+    """T = 0 with no memory behind the slots (an empty tensor's null pointer):
+    the store's calls only update the counters."""
+    rc, st = _store(T=0, base=None)
+    assert rc == B.OK
+    assert B.lib().attnres_accumulate(ctypes.byref(st), None, 0, None) == B.OK
+    assert B.lib().attnres_accumulate_aggregate(ctypes.byref(st), None, 1, None, None, None, 1e-5, None) == B.OK
+    assert (st.n_completed, st.partial_valid) == (1, 0)
+    assert B.lib().attnres_store_sources(ctypes.byref(st)) == 2
 
 
 def test_store_state_machine_follows_the_block_rule(lib):

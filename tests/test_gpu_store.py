@@ -58,6 +58,23 @@ def test_accumulate_rounding_ties_and_wide_range():
     assert same_bits(store.slots[1], orc.accumulate(p.reshape(T, d), f.reshape(T, d), "bf16"))
 
 
+def test_empty_store_through_the_binding():
+    """A store for T = 0 (its slots an empty tensor, whose pointer is null):
+    updates and aggregations only advance the counters and return empty rows."""
+    dev = device()
+    d = 7168
+    st = B.SourceStore(0, d, dtype=torch.bfloat16, device=dev)
+    F = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    w = synth.query(d, seed=1, device=dev)
+    st.accumulate(F)
+    out, a = st.accumulate_aggregate(F, True, w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, d) and a.shape[0] == 0
+    assert (st.n_completed, st.partial_valid) == (1, 0)
+    out, a = st.aggregate(w)
+    assert out.shape == (0, d) and a.shape == (0, 2)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d", [(5, 7168), (129, 264), (1000, 7176), (3, 8)])
 @pytest.mark.parametrize("state,finalize", [((0, 0), 0), ((0, 1), 0), ((2, 1), 1), ((3, 0), 1), ((7, 1), 0)])
