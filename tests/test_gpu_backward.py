@@ -277,22 +277,18 @@ def test_backward_full_size_sampled():
     assert err <= 1e-5 * np.max(np.abs(tot)), f"dw over the batch vs the two halves: {err:.3e}"
 
 
-@pytest.mark.parametrize("defer", [True, False], ids=["deferred", "per_layer"])
-@pytest.mark.parametrize("final", [True, False])
-def test_schedule_backward_matches_oracle(final, defer):
-    """10 layers in blocks of 4, every gradient compared with the oracle's
-    run_schedule_backward (dF and dh_0 rounded to bf16 when handed out); the
-    inter-block gradients deferred to one pass per block, or updated per layer."""
+def _check_schedule_backward(L, bs, T, d, final, defer, seed):
+    """Every gradient of the backward schedule compared with the oracle's
+    run_schedule_backward (dF and dh_0 rounded to bf16 when handed out)."""
     dev = device()
-    L, bs, T, d = 10, 4, 48, 264
-    note(f"schedule backward final={final} defer={defer}")
+    note(f"schedule backward L={L} block={bs} T={T} d={d} final={final} defer={defer}")
     store = B.SourceStore(T, d, dtype=torch.bfloat16, device=dev)
-    synth.fill_normal_(store.h0, 1.0, seed=2, tag=1)
-    Fs = [synth.layer_output(T, d, std=0.3, seed=2, tag=l, device=dev) for l in range(L)]
-    Ws = [synth.query(d, seed=2, device=dev, tag=l) for l in range(L)]
-    wf = synth.query(d, seed=2, device=dev, tag=500)
-    gr = [synth.layer_output(T, d, std=1.0, seed=2, tag=100 + l, device=dev) for l in range(L)]
-    gf = synth.layer_output(T, d, std=1.0, seed=2, tag=999, device=dev)
+    synth.fill_normal_(store.h0, 1.0, seed=seed, tag=1)
+    Fs = [synth.layer_output(T, d, std=0.3, seed=seed, tag=l, device=dev) for l in range(L)]
+    Ws = [synth.query(d, seed=seed, device=dev, tag=l) for l in range(L)]
+    wf = synth.query(d, seed=seed, device=dev, tag=500)
+    gr = [synth.layer_output(T, d, std=1.0, seed=seed, tag=100 + l, device=dev) for l in range(L)]
+    gf = synth.layer_output(T, d, std=1.0, seed=seed, tag=999, device=dev)
     schedule.run_schedule(store, Fs, Ws, bs, final_query=wf if final else None)
     handed = {}
     gs, gw, gwf = schedule.run_schedule_backward(
@@ -319,6 +315,34 @@ def test_schedule_backward_matches_oracle(final, defer):
     if final:
         e = np.max(np.abs(host(gwf) - ref["dw_final"]))
         assert e <= 1e-3 * np.max(np.abs(ref["dw_final"])), f"dw final: {e:.3e}"
+
+
+@pytest.mark.parametrize("defer", [True, False], ids=["deferred", "per_layer"])
+@pytest.mark.parametrize("final", [True, False])
+def test_schedule_backward_matches_oracle(final, defer):
+    """10 layers in blocks of 4; the inter-block gradients deferred to one pass
+    per block, or updated per layer."""
+    _check_schedule_backward(10, 4, 48, 264, final, defer, 2)
+
+
+def _random_backward_schedules(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        bs = int(rng.integers(1, 13))
+        nblocks = int(rng.integers(1, 9))
+        L = int(rng.integers((nblocks - 1) * bs + 1, nblocks * bs + 1))
+        out.append((L, bs, int(rng.integers(1, 60)), int(8 * rng.integers(1, 80)), bool(rng.random() < 0.6),
+                    bool(rng.random() < 0.7), 40 + k))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_backward_schedules(5, 4321),
+                         ids=lambda c: f"L{c[0]}-b{c[1]}-T{c[2]}-d{c[3]}-final{int(c[4])}-defer{int(c[5])}")
+def test_random_backward_schedules_match_oracle(case):
+    """Seeded random layer counts, block sizes, T and d, with and without the
+    output layer and deferral."""
+    _check_schedule_backward(*case)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

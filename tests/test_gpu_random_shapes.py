@@ -44,7 +44,7 @@ def _sources(S, T, d, pad, dtype, seed, dev):
     return H
 
 
-@pytest.mark.parametrize("case", _cases(24, 2024), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}-pad{c[5]}")
+@pytest.mark.parametrize("case", _cases(48, 2024), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}-pad{c[5]}")
 def test_random_aggregate(case):
     k, dtype, S, T, d, pad, seed = case
     note(f"random aggregate #{k}: {dtype} S={S} T={T} d={d} pad={pad}")
@@ -59,7 +59,7 @@ def test_random_aggregate(case):
     compare(host(out), host(a), r_ref, a_ref, dtype == "bf16", f"random #{k}")
 
 
-@pytest.mark.parametrize("case", _cases(16, 77), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
+@pytest.mark.parametrize("case", _cases(32, 77), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
 def test_random_fused_update(case):
     k, dtype, S, T, d, _, seed = case
     dev = device()
@@ -90,7 +90,7 @@ def test_random_fused_update(case):
         compare(host(out_f), host(a_f), r_ref, a_ref, dtype == "bf16", f"random fused #{k}")
 
 
-@pytest.mark.parametrize("case", _cases(16, 99), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
+@pytest.mark.parametrize("case", _cases(24, 99), ids=lambda c: f"{c[1]}-S{c[2]}-T{c[3]}-d{c[4]}")
 def test_random_backward(case):
     k, dtype, S, T, d, pad, seed = case
     rng = np.random.default_rng(seed)

@@ -217,6 +217,27 @@ def _check_schedule(L, Bsz, T, d, two_phase_from, out3d, tag):
     compare(host(final_r), host(final_a), ref["final_r"], ref["final_a"], True, "output layer")
 
 
+def _random_schedules(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bsz = int(rng.integers(1, 21))
+        nblocks = int(rng.integers(1, 9))
+        L = int(rng.integers((nblocks - 1) * bsz + 1, nblocks * bsz + 1))
+        tpf = None if rng.random() < 0.3 else int(rng.integers(1, nblocks + 1))
+        out.append((L, bsz, int(rng.integers(1, 100)), int(8 * rng.integers(1, 257)), tpf, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_schedules(6, 31), ids=lambda c: f"L{c[0]}-b{c[1]}-T{c[2]}-d{c[3]}-from{c[4]}")
+def test_random_schedules_match_oracle(case):
+    """Seeded random layer counts, block sizes (1-20: more than 16 layers per
+    block takes two inter-block passes), up to 8 blocks, ragged T and d, and
+    the two-phase schedule from a random block (or not at all)."""
+    L, bsz, T, d, tpf, out3d = case
+    _check_schedule(L, bsz, T, d, tpf, out3d, "random schedule")
+
+
 @pytest.mark.parametrize("two_phase_from", [1, 2, 4])
 @pytest.mark.parametrize("out3d", [True, False])
 def test_small_schedule_two_phase_matches_oracle(two_phase_from, out3d):
