@@ -275,7 +275,7 @@ aggregate_kernel(u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t sr
 // next batch is loaded as soon as this one's statistics are formed, so that it
 // arrives while this batch's barrier, merge and weighted sum run (the batch
 // loop is unrolled by two so that each buffer keeps its registers).  Two
-// 9-row buffers take ~210 VGPRs at V = 2: one workgroup per CU whose next batch
+// 9-row buffers take ~230 VGPRs at V = 2: one workgroup per CU whose next batch
 // is always in flight beats two that each drain between batches (smaller
 // batches at two workgroups per CU were slower still: more barriers).  Wider
 // rows take smaller batches.
