@@ -93,10 +93,16 @@ _SIGNATURES = {
                                             ctypes.c_void_p]),
     "attnres_block_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                               ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
-                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
+                                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
                                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int32, ctypes.c_void_p]),
+    "attnres_partial_dw": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_void_p]),
+    "attnres_partial_dw_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "attnres_block_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                         ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "attnres_aggregate_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -250,7 +256,7 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
                        *, last_source: torch.Tensor | None = None, accumulate=0, defer=0,
                        coef: torch.Tensor | None = None, coef_stride: int = 0, grad_w: torch.Tensor | None = None,
                        grad_last: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                       eps: float = 1e-5, stream=None) -> torch.Tensor:
+                       form_dw: bool = True, eps: float = 1e-5, stream=None) -> torch.Tensor | None:
     """``attnres_aggregate_backward``: writes (or, for the sources whose bit is
     set in the ``accumulate`` mask, adds) dL/dH into ``grad_sources``
     ``[S, T, d]`` float32 (rows contiguous, any row stride) and returns dL/dw
@@ -261,7 +267,10 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
     Sources in the ``defer`` mask keep their gradient rows untouched and write
     their coefficients to ``coef`` (float32, ``coef_stride`` floats per token,
     may be a view starting mid-row) for :func:`block_backward`, which also adds
-    their share of dL/dw: the returned ``grad_w`` sums the other sources only."""
+    their share of dL/dw: the returned ``grad_w`` sums the other sources only.
+    With ``form_dw=False`` no dL/dw is formed (``grad_w`` must be None; the C
+    call gets NULL): every source's coefficients go to ``coef``, for
+    :func:`block_backward` and :func:`partial_dw`, and None is returned."""
     if grad_sources.dim() != 3 or sources.dim() != 3:
         raise ValueError("sources and grad_sources must be 3-D")
     S, T, d = grad_sources.shape
@@ -278,33 +287,37 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
               ("coef", coef), ("grad_w", grad_w), ("grad_last", grad_last), ("workspace", workspace))
     if grad_sources.dtype != torch.float32:
         raise ValueError("grad_sources must be float32")
-    if grad_w is None:
+    if not form_dw and grad_w is not None:
+        raise ValueError("form_dw=False takes no grad_w")
+    if form_dw and grad_w is None:
         grad_w = torch.empty(d, dtype=torch.float32, device=dev)
-    if workspace is None:
+    if form_dw and workspace is None:
         nbytes = backward_workspace_bytes(T, d, sources.dtype)
         workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=dev)
-    checks = (("w", w, torch.float32, d), ("grad_out", grad_out, sources.dtype, T * d),
-              ("grad_w", grad_w, torch.float32, d))
+    checks = (("w", w, torch.float32, d), ("grad_out", grad_out, sources.dtype, T * d))
+    if form_dw:
+        checks += (("grad_w", grad_w, torch.float32, d),)
     if grad_last is not None:
         checks += (("grad_last", grad_last, sources.dtype, T * d),)
     for name, t, dt, n in checks:
         if t.device != dev or not t.is_contiguous() or t.dtype != dt or t.numel() != n:
             raise ValueError(f"{name} must be a contiguous {dt} tensor with {n} elements on {dev}")
-    if not workspace.is_contiguous() or workspace.device != dev:
+    if workspace is not None and (not workspace.is_contiguous() or workspace.device != dev):
         raise ValueError("workspace must be a contiguous device tensor")
     mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
-    if defer and (coef is None or coef.dtype != torch.float32 or coef.device != dev):
-        raise ValueError("deferred sources need a float32 coef buffer on the device")
+    if (defer or not form_dw) and (coef is None or coef.dtype != torch.float32 or coef.device != dev):
+        raise ValueError("deferred sources (and form_dw=False) need a float32 coef buffer on the device")
     src_stride = sources.stride(0) if sources.shape[0] > 1 else T * d
     grad_stride = grad_sources.stride(0) if S > 1 else T * d
     src_ptr = sources.data_ptr() if sources.shape[0] > 0 else None
     rc = lib().attnres_aggregate_backward(
         src_ptr, S, T, d, src_stride, last_source.data_ptr() if last_source is not None else None, w.data_ptr(),
         grad_out.data_ptr(), grad_sources.data_ptr(),
-        grad_stride, mask & 0xFFFFFFFF, defer & 0xFFFFFFFF, coef.data_ptr() if defer else None, int(coef_stride),
-        grad_last.data_ptr() if grad_last is not None else None, grad_w.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), float(eps), _dtype_code(sources),
-        _stream(dev, stream))
+        grad_stride, mask & 0xFFFFFFFF, defer & 0xFFFFFFFF, coef.data_ptr() if (defer or not form_dw) else None,
+        int(coef_stride), grad_last.data_ptr() if grad_last is not None else None,
+        grad_w.data_ptr() if form_dw else None, workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, float(eps),
+        _dtype_code(sources), _stream(dev, stream))
     _check("attnres_aggregate_backward", rc)
     return grad_w
 
@@ -331,13 +344,15 @@ def partial_sums(layer_outs, out: torch.Tensor, stream=None) -> torch.Tensor:
 
 
 def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor, grad_sources: torch.Tensor,
-                   grad_ws, *, accumulate=0, grad_last: torch.Tensor | None = None,
+                   grad_ws, *, accumulate=0, grad_last: torch.Tensor | None = None, coef_layer_stride: int = 0,
                    workspace: torch.Tensor | None = None, stream=None) -> None:
     """``attnres_block_backward``: add the B layers' deferred contributions into
     the n inter-block gradient rows ``grad_sources`` ``[n, T, d]`` float32, and
     the deferred sources' share of each layer's dL/dw into ``grad_ws[l]``
     (float32 ``[d]``).  ``sources`` ``[n, T, d]``; ``grad_outs`` / ``queries``:
-    B tensors ``[T, d]`` / ``[d]``; ``coef`` float32 ``[T, B, n, 3]``."""
+    B tensors ``[T, d]`` / ``[d]``; ``coef`` contiguous float32 with
+    ``T * B * m`` elements, ``[T, B, m]``, layer l's n triples first in its m
+    floats, m = ``coef_layer_stride`` (0: m = 3n, ``[T, B, n, 3]``)."""
     n, T, d = grad_sources.shape
     Bl = len(grad_outs)
     if sources.shape != grad_sources.shape or len(queries) != Bl or len(grad_ws) != Bl:
@@ -348,8 +363,9 @@ def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor
     for name, t in (("sources", sources), ("grad_sources", grad_sources)):
         if T > 0 and (t.stride(2) != 1 or t.stride(1) != d):
             raise ValueError(f"each row of {name} must be a contiguous [T, d] block")
-    if coef.dtype != torch.float32 or not coef.is_contiguous() or coef.numel() != T * Bl * n * 3:
-        raise ValueError("coef must be a contiguous float32 [T, B, n, 3] tensor")
+    m = coef_layer_stride or 3 * n
+    if coef.dtype != torch.float32 or not coef.is_contiguous() or coef.numel() != T * Bl * m:
+        raise ValueError(f"coef must be a contiguous float32 tensor of T * B * {m} elements")
     for g in grad_outs:
         if g.dtype != sources.dtype or not g.is_contiguous() or g.numel() != T * d:
             raise ValueError("each upstream gradient must be a contiguous [T, d] tensor like the sources")
@@ -368,9 +384,56 @@ def block_backward(sources: torch.Tensor, grad_outs, queries, coef: torch.Tensor
     mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
     _check("attnres_block_backward", lib().attnres_block_backward(
         sources.data_ptr(), n, T, d, sources.stride(0) if n > 1 else T * d, Bl, garr, warr, coef.data_ptr(),
-        grad_sources.data_ptr(), grad_sources.stride(0) if n > 1 else T * d, mask & 0xFFFFFFFF,
+        int(coef_layer_stride), grad_sources.data_ptr(), grad_sources.stride(0) if n > 1 else T * d, mask & 0xFFFFFFFF,
         grad_last.data_ptr() if grad_last is not None else None, dwarr, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _dtype_code(sources), _stream(dev, stream)))
+
+
+def partial_dw_workspace_bytes(T: int, d: int, B: int, dtype=torch.bfloat16) -> int:
+    """``attnres_partial_dw_workspace`` on the current device."""
+    out = ctypes.c_int64(0)
+    _check("attnres_partial_dw_workspace",
+           lib().attnres_partial_dw_workspace(T, d, B, _DTYPE_CODE[dtype], ctypes.byref(out)))
+    return int(out.value)
+
+
+def partial_dw(rows, coef: torch.Tensor | None, coef_stride: int, coef_layer_stride: int, grad_ws, *,
+               workspace: torch.Tensor | None = None, stream=None) -> None:
+    """``attnres_partial_dw``: ``grad_ws[l]`` (float32 ``[d]``) is overwritten
+    with the sum over tokens t of ``coef[t * coef_stride + l * coef_layer_stride]
+    * rows[l][t]``; ``rows`` are B tensors ``[T, d]`` (or None: that layer's row
+    is zeroed); ``coef`` a float32 device tensor whose first element is layer
+    0's coefficient for token 0 (a view may start mid-row)."""
+    Bl = len(grad_ws)
+    if len(rows) != Bl or Bl == 0:
+        raise ValueError("one row (or None) per dL/dw row")
+    d = grad_ws[0].numel()
+    given = [r for r in rows if r is not None]
+    dev = grad_ws[0].device
+    _same_gpu(dev, ("rows", given), ("coef", coef), ("grad_ws", list(grad_ws)), ("workspace", workspace))
+    T = given[0].shape[0] if given else 0
+    dt = given[0].dtype if given else torch.float32
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}; use bfloat16 or float32")
+    for r in given:
+        if r.dtype != dt or not r.is_contiguous() or tuple(r.shape) != (T, d):
+            raise ValueError("each row must be a contiguous [T, d] tensor, all of one dtype")
+    for w in grad_ws:
+        if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != d:
+            raise ValueError(f"each dL/dw row must be a contiguous float32 [d] tensor on {dev}")
+    if given and T > 0 and (coef is None or coef.dtype != torch.float32):
+        raise ValueError("rows need a float32 coef tensor")
+    if workspace is None:
+        nbytes = partial_dw_workspace_bytes(T, d, Bl, dt)
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=dev)
+    if not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous device tensor")
+    rarr = (ctypes.c_void_p * Bl)(*[r.data_ptr() if r is not None else None for r in rows])
+    dwarr = (ctypes.c_void_p * Bl)(*[w.data_ptr() for w in grad_ws])
+    _check("attnres_partial_dw", lib().attnres_partial_dw(
+        rarr, Bl, T, d, coef.data_ptr() if coef is not None else None, int(coef_stride), int(coef_layer_stride),
+        dwarr, workspace.data_ptr(), workspace.numel() * workspace.element_size(), _DTYPE_CODE[dt],
+        _stream(dev, stream)))
 
 
 def prepared_query_shape(n: int, d: int):

@@ -113,7 +113,10 @@ __device__ __forceinline__ void add_token_dw(f32x4 (*dw4)[64 * kMaxWaves], int t
     }
 }
 
-template <bool kBf16, int kV>
+// kDw: dL/dw is formed here (per-lane sums over the workgroup's tokens, one
+// row per workgroup); without it every source's coefficients are written
+// instead and the grid is one workgroup per token.
+template <bool kBf16, int kV, bool kDw>
 __global__ void __launch_bounds__(64 * kMaxWaves)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd_bwd<kV>())))
 aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
@@ -127,7 +130,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
   // [buffer][wave][sum of squares | w.x | g.x][source]
   __shared__ float red[2][kMaxWaves][3][16];
   // this lane's running dL/dw, [vector][lane] (each lane touches only its own)
-  __shared__ f32x4 dw4[kV * kGv][64 * kMaxWaves];
+  __shared__ f32x4 dw4[kDw ? kV * kGv : 1][64 * kMaxWaves];
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -138,8 +141,10 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
 
   Query<kBf16, kV> q;
   load_query<kBf16, kV>(q, w, nvec, tid, nthr);
+  if constexpr (kDw) {
 #pragma unroll
-  for (int k = 0; k < kV * kGv; ++k) dw4[k][tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kV * kGv; ++k) dw4[k][tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
@@ -225,8 +230,9 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
     const float delta = a * (ug - ubar);             // dL/dz_s
     const float c1 = delta / rho;                    // coefficient of w (and of H_s in dL/dw)
     const float c3 = c1 * z * inv_d / rho;           // coefficient of H_s in dL/dH_s
-    // deferred sources: their three coefficients go out instead of a gradient row
-    if (wave == 0 && lane < S && ((defer_mask >> lane) & 1u)) {
+    // deferred sources: their three coefficients go out instead of a gradient
+    // row (every source's, when dL/dw is formed by the caller)
+    if (wave == 0 && lane < S && (!kDw || ((defer_mask >> lane) & 1u))) {
       float* cf = coef + t * coef_stride + 3 * lane;
       cf[0] = a;
       cf[1] = c1;
@@ -287,7 +293,7 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
           for (int e = 0; e < kE; ++e) r[e] = fmaf(as[s], ge[e], fmaf(c1s[s], wf[e], -c3s[s] * xe[e]));
           // this token's share of dL/dw: sum_s c1_s H_s for this lane's elements,
           // over the sources not deferred (the block pass adds the others')
-          if (!((defer_mask >> s) & 1u)) {
+          if (kDw && !((defer_mask >> s) & 1u)) {
 #pragma unroll
             for (int e = 0; e < kE; ++e) dtok[v][e] = fmaf(c1s[s], xe[e], dtok[v][e]);
           }
@@ -321,17 +327,19 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
         __builtin_amdgcn_sched_barrier(0);  // one source's rows in registers at a time
       }
     }
-    add_token_dw<kV, kGv>(dw4, tid, dtok);
+    if constexpr (kDw) add_token_dw<kV, kGv>(dw4, tid, dtok);
   }
 
   // 6. this workgroup's dL/dw row
-  float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
+  if constexpr (kDw) {
+    float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
 #pragma unroll
-  for (int v = 0; v < kV; ++v) {
-    const int idx = v * nthr + tid;
-    if (idx < nvec) {
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      if (idx < nvec) {
 #pragma unroll
-      for (int h = 0; h < kGv; ++h) reinterpret_cast<f32x4*>(row)[idx * kGv + h] = dw4[v * kGv + h][tid];
+        for (int h = 0; h < kGv; ++h) reinterpret_cast<f32x4*>(row)[idx * kGv + h] = dw4[v * kGv + h][tid];
+      }
     }
   }
 }
@@ -342,8 +350,9 @@ aggregate_backward_kernel(const u32x4* __restrict__ src, int S, int64_t T, int n
 // shares are summed with their gradient rows in the block pass.  So after the
 // statistics nothing but the last row is needed: the rows stream once through
 // a three-row register ring, the last one is kept, and the kernel fits two
-// workgroups per CU.
-template <bool kBf16, int kV>
+// workgroups per CU.  kDw as in aggregate_backward_kernel: without it the
+// last source's coefficients are written too and nothing is summed over tokens.
+template <bool kBf16, int kV, bool kDw>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(kV <= 2 ? 4 : 2)))
 aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, int nvec, int64_t src_stride_v,
                                const u32x4* __restrict__ last_src, const float* __restrict__ w,
@@ -473,7 +482,7 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
     const float delta = a * (ug - ubar);
     const float c1 = delta / rho;
     const float c3 = c1 * z * inv_d / rho;
-    if (wave == 0 && lane < S && ((defer_mask >> lane) & 1u)) {
+    if (wave == 0 && lane < S && (!kDw || ((defer_mask >> lane) & 1u))) {
       float* cf = coef + t * coef_stride + 3 * lane;
       cf[0] = a;
       cf[1] = c1;
@@ -499,8 +508,10 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
 #pragma unroll
           for (int e = 0; e < kE; ++e) wf[e] = q.f[v][e];
         }
+        if constexpr (kDw) {
 #pragma unroll
-        for (int e = 0; e < kE; ++e) dw[v][e] = fmaf(c1L, xe[e], dw[v][e]);
+          for (int e = 0; e < kE; ++e) dw[v][e] = fmaf(c1L, xe[e], dw[v][e]);
+        }
         f32x4 o[kGv];
 #pragma unroll
         for (int h = 0; h < kGv; ++h) {
@@ -526,15 +537,17 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
     }
   }
 
-  float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
+  if constexpr (kDw) {
+    float* row = dw_rows + (int64_t)blockIdx.x * nvec * kE;
 #pragma unroll
-  for (int v = 0; v < kV; ++v) {
-    const int idx = v * nthr + tid;
-    if (idx < nvec) {
+    for (int v = 0; v < kV; ++v) {
+      const int idx = v * nthr + tid;
+      if (idx < nvec) {
 #pragma unroll
-      for (int h = 0; h < kGv; ++h)
-        reinterpret_cast<f32x4*>(row)[idx * kGv + h] =
-            f32x4{dw[v][4 * h], dw[v][4 * h + 1], dw[v][4 * h + 2], dw[v][4 * h + 3]};
+        for (int h = 0; h < kGv; ++h)
+          reinterpret_cast<f32x4*>(row)[idx * kGv + h] =
+              f32x4{dw[v][4 * h], dw[v][4 * h + 1], dw[v][4 * h + 2], dw[v][4 * h + 3]};
+      }
     }
   }
 }
@@ -545,11 +558,13 @@ aggregate_backward_last_kernel(const u32x4* __restrict__ src, int S, int64_t T, 
 // delta z/(d rho^2); here, per token and source,
 //     G_s += sum_l (a_{l,s} g_l + c1_{l,s} w_l) - (sum_l c3_{l,s}) H_s,
 // one read-modify-write of each gradient row per block instead of one per
-// layer.  The coefficients of a token are staged in LDS and read as broadcasts.
+// layer.  The coefficients of a token are staged in LDS and read as broadcasts;
+// in memory layer l's triples start cls floats after layer l-1's (cls >= 3n:
+// a layer's own last source may have its triple there too).
 template <bool kBf16, int kV>
 __global__ void __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(kV <= 2 ? 4 : 2)))
 block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec, int64_t src_stride_v,
-                      BlockRows rows, int B, const float* __restrict__ coef, f32x4* __restrict__ grad,
+                      BlockRows rows, int B, const float* __restrict__ coef, int cls, f32x4* __restrict__ grad,
                       int64_t grad_stride_v, unsigned acc_mask, u32x4* __restrict__ grad_last) {
   using El = Elems<kBf16>;
   constexpr int kE = El::kE, kGv = El::kG;
@@ -558,11 +573,16 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  const int per_tok = B * n * 3;
+  const int per_layer = n * 3;
+  const int per_tok = B * per_layer;
 
   int buf = 0;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x, buf ^= 1) {
-    for (int k = tid; k < per_tok; k += nthr) cf[buf][k] = coef[t * per_tok + k];
+    const float* ct = coef + t * (int64_t)(B * cls);
+    for (int k = tid; k < per_tok; k += nthr) {
+      const int l = k / per_layer;
+      cf[buf][k] = ct[l * cls + (k - l * per_layer)];
+    }
     __syncthreads();
     if (tid < n) {
       float c3 = 0.f;
@@ -654,7 +674,8 @@ block_backward_kernel(const u32x4* __restrict__ src, int n, int64_t T, int nvec,
 // source is fixed -- or alternates between two, for kNp = 8 -- and only the
 // token advances, by a uniform stride.  A workgroup of kDwWaves waves covers
 // kDwWaves * 128 columns for one group of strided tokens (tg of ntg) and
-// writes its partial rows to dw_part[tg][l][d] for a fixed-order sum.
+// writes its partial rows to dw_part[tg][l][d] for a fixed-order sum.  A
+// token's coefficients for layer l start at l * cls (cls >= 3 kN floats).
 // Coefficients past the group's tokens or of layer slots past B come from a
 // buffer load out of range (zero); rows are clamped to valid ones.  Every load
 // is unconditional, so a ring of kDwRing steps stays in flight.
@@ -665,7 +686,7 @@ constexpr int kDwRing = 4;
 template <bool kBf16, int kN>
 __global__ void __launch_bounds__(64 * kDwWaves)
 block_dw_kernel(const void* __restrict__ src, int64_t T, int d, int64_t src_stride, int B,
-                const float* __restrict__ coef, float* __restrict__ dw_part, int ncolblocks) {
+                const float* __restrict__ coef, int cls, float* __restrict__ dw_part, int ncolblocks) {
   constexpr int kNp = kN == 1 ? 1 : kN == 2 ? 2 : kN <= 4 ? 4 : 8;   // source slots per token
   constexpr int kTokPerStep = kNp <= 4 ? 4 / kNp : 1;
   constexpr int kStepsPerTok = kNp == 8 ? 2 : 1;
@@ -680,7 +701,7 @@ block_dw_kernel(const void* __restrict__ src, int64_t T, int d, int64_t src_stri
   const bool col_ok = col0 + 8 * j < d;
   const int e = col_ok ? col0 + 8 * j : d - 8;          // clamped: such lanes write nothing
   const unsigned ntok = (unsigned)((T - tg + ntg - 1) / ntg);   // tokens of this group (tg < T)
-  const unsigned per_tok = (unsigned)B * kN * 3;
+  const unsigned per_tok = (unsigned)(B * cls);
   const unsigned tsub = kNp <= 4 ? kq / kNp : 0;        // token within a step
   const int slot = kNp <= 4 ? kq % kNp : kq;            // source slot (+4 on odd steps for kNp = 8)
   int64_t hbase[kStepsPerTok];
@@ -690,7 +711,7 @@ block_dw_kernel(const void* __restrict__ src, int64_t T, int d, int64_t src_stri
   for (int p = 0; p < kStepsPerTok; ++p) {
     const int sp = slot + 4 * p;
     hbase[p] = (int64_t)(sp < kN ? sp : kN - 1) * src_stride + e;
-    cbase[p] = (unsigned)((j * kN + sp) * 3 + 1);
+    cbase[p] = (unsigned)(j * cls + sp * 3 + 1);
     cval[p] = sp < kN && j < B;
   }
   const unsigned steps =
@@ -790,6 +811,65 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
   }
 }
 
+// A layer's dL/dw share from a row of its own -- in the Block AttnRes backward
+// the partial block sum that was the layer's last source, whose coefficient
+// c1 = delta/rho the layer's backward wrote per token instead of summing it:
+//     dw_part[tg][l][j] = sum over the tokens t = tg, tg + ntg, ... of c_l[t] X_l[t][j],
+// tokens in increasing order, then reduce_rows_kernel sums the groups in a
+// fixed order.  A workgroup covers kPartialDwThreads 16-byte vectors of one
+// layer's row for one token group, kPdAhead tokens' vectors loading at once.
+// A layer without a row gets zeros.
+constexpr int kPdAhead = 8;
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kPartialDwThreads)
+partial_dw_kernel(DwRows rows, int64_t coef_stride, int64_t T, int nvec, int ncolblocks, int B,
+                  float* __restrict__ dw_part) {
+  using El = Elems<kBf16>;
+  constexpr int kE = El::kE;
+  const int l = blockIdx.y;
+  const int cb = blockIdx.x % ncolblocks;
+  const int64_t tg = blockIdx.x / ncolblocks;
+  const int64_t ntg = gridDim.x / ncolblocks;
+  const int idx = cb * kPartialDwThreads + threadIdx.x;
+  const u32x4* __restrict__ x = static_cast<const u32x4*>(rows.x[l]);
+  const float* __restrict__ c = rows.c[l];
+  float acc[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+  if (x != nullptr && idx < nvec) {
+    int64_t t = tg;
+    for (; t + (kPdAhead - 1) * ntg < T; t += kPdAhead * ntg) {
+      u32x4 xv[kPdAhead];
+      float cv[kPdAhead];
+#pragma unroll
+      for (int k = 0; k < kPdAhead; ++k) {
+        xv[k] = __builtin_nontemporal_load(x + (t + k * ntg) * (int64_t)nvec + idx);
+        cv[k] = c[(t + k * ntg) * coef_stride];
+      }
+#pragma unroll
+      for (int k = 0; k < kPdAhead; ++k) {
+        float xe[kE];
+        unpack<kBf16>(xv[k], xe);
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[e] = fmaf(cv[k], xe[e], acc[e]);
+      }
+    }
+    for (; t < T; t += ntg) {
+      float xe[kE];
+      unpack<kBf16>(__builtin_nontemporal_load(x + t * (int64_t)nvec + idx), xe);
+      const float cv = c[t * coef_stride];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[e] = fmaf(cv, xe[e], acc[e]);
+    }
+  }
+  if (idx < nvec) {
+    f32x4* out = reinterpret_cast<f32x4*>(dw_part + ((int64_t)tg * B + l) * nvec * kE) + (int64_t)idx * (kE / 4);
+#pragma unroll
+    for (int h = 0; h < kE / 4; ++h) out[h] = f32x4{acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]};
+  }
+}
+
 // The running partial sums of a block's layer outputs, formed exactly as the
 // store forms them (each step one float32 addition, then for bf16 one rounding
 // to nearest even): out[0] = F_0, out[k] = out[k-1] + F_k.  One pass: every
@@ -818,7 +898,10 @@ template <bool kBf16, int kV>
 hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
   const int nvec = a.d / (kBf16 ? 8 : 4);
   if (a.T > 0) {
-    auto kernel = a.last_only ? aggregate_backward_last_kernel<kBf16, kV> : aggregate_backward_kernel<kBf16, kV>;
+    auto kernel = a.form_dw ? (a.last_only ? aggregate_backward_last_kernel<kBf16, kV, true>
+                                           : aggregate_backward_kernel<kBf16, kV, true>)
+                            : (a.last_only ? aggregate_backward_last_kernel<kBf16, kV, false>
+                                           : aggregate_backward_kernel<kBf16, kV, false>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
                        static_cast<const u32x4*>(a.sources), a.S, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4),
                        static_cast<const u32x4*>(a.last_source), a.w,
@@ -828,6 +911,7 @@ hipError_t launch_bwd_v(const BackwardArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!a.form_dw) return hipSuccess;
   OutRows out{};
   out.p[0] = a.grad_w;
   hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((a.d + 31) / 32)), dim3(256), 0, stream, a.workspace,
@@ -851,8 +935,8 @@ hipError_t launch_block_v(const BlockBackwardArgs& a, hipStream_t stream) {
   const int nvec = a.d / (kBf16 ? 8 : 4);
   hipLaunchKernelGGL((block_backward_kernel<kBf16, kV>), dim3((unsigned)a.grid), dim3(a.threads), 0, stream,
                      static_cast<const u32x4*>(a.sources), a.n, a.T, nvec, a.src_stride / (kBf16 ? 8 : 4), a.rows,
-                     a.B, a.coef, reinterpret_cast<f32x4*>(a.grad_sources), a.grad_stride / 4, a.acc_mask,
-                     static_cast<u32x4*>(a.grad_last));
+                     a.B, a.coef, a.coef_layer, reinterpret_cast<f32x4*>(a.grad_sources), a.grad_stride / 4,
+                     a.acc_mask, static_cast<u32x4*>(a.grad_last));
   return hipGetLastError();
 }
 
@@ -873,7 +957,7 @@ hipError_t launch_block(const BlockBackwardArgs& a, hipStream_t stream) {
 #define ATTNRES_DW_CASE(N)                                                                                      \
   case N:                                                                                                       \
     hipLaunchKernelGGL((block_dw_kernel<kBf16, N>), grid, block, 0, stream, a.sources, a.T, a.d, a.src_stride, \
-                       a.B, a.coef, a.workspace, a.dw_colblocks);                                              \
+                       a.B, a.coef, a.coef_layer, a.workspace, a.dw_colblocks);                                \
     break;
     ATTNRES_DW_CASE(1) ATTNRES_DW_CASE(2) ATTNRES_DW_CASE(3) ATTNRES_DW_CASE(4)
     ATTNRES_DW_CASE(5) ATTNRES_DW_CASE(6) ATTNRES_DW_CASE(7) ATTNRES_DW_CASE(8)
@@ -931,6 +1015,25 @@ hipError_t static_scratch(void** ptr) {
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   return a.bf16 ? launch_block<true>(a, stream) : launch_block<false>(a, stream);
+}
+
+hipError_t launch_partial_dw(const PartialDwArgs& a, hipStream_t stream) {
+  // T = 0: no groups, and the sum of no rows writes zeros
+  if (a.T > 0) {
+    const int nvec = a.d / (a.bf16 ? 8 : 4);
+    const dim3 grid((unsigned)(a.colblocks * a.groups), (unsigned)a.B);
+    if (a.bf16)
+      hipLaunchKernelGGL((partial_dw_kernel<true>), grid, dim3(kPartialDwThreads), 0, stream, a.rows,
+                         a.coef_stride, a.T, nvec, a.colblocks, a.B, a.workspace);
+    else
+      hipLaunchKernelGGL((partial_dw_kernel<false>), grid, dim3(kPartialDwThreads), 0, stream, a.rows,
+                         a.coef_stride, a.T, nvec, a.colblocks, a.B, a.workspace);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)((a.d + 31) / 32), (unsigned)a.B), dim3(256), 0, stream,
+                     a.workspace, a.groups, (int64_t)a.B * a.d, (int64_t)a.d, a.d, a.out, false);
+  return hipGetLastError();
 }
 
 hipError_t launch_partial_sums(const PartialSumsArgs& a, hipStream_t stream) {

@@ -217,19 +217,28 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
     return ATTNRES_EINVAL;
   if (S > 1 && (src_stride < row || grad_stride < row)) return ATTNRES_EINVAL;
   if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
-  if (grad_w == nullptr) return ATTNRES_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(grad_w) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+  // without grad_w, dL/dw is left to the caller: every source's coefficients
+  // are written, no workspace is used, and the grid is one workgroup per token
+  const bool form_dw = grad_w != nullptr;
+  if (form_dw && (reinterpret_cast<uintptr_t>(grad_w) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
   defer_mask &= (S >= 32) ? 0xFFFFFFFFu : ((1u << S) - 1u);
-  if (defer_mask != 0) {
-    if (coef == nullptr || coef_stride < 3 * (int64_t)S) return ATTNRES_EINVAL;
+  if (defer_mask != 0 || !form_dw) {
+    // every coefficient offset stays far inside int64 (as the element offsets do)
+    if (coef == nullptr || coef_stride < 3 * (int64_t)S || coef_stride > (INT64_C(1) << 40) / (T > 0 ? T : 1))
+      return ATTNRES_EINVAL;
     if ((reinterpret_cast<uintptr_t>(coef) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
     if (grad_last != nullptr && ((defer_mask >> (S - 1)) & 1u)) return ATTNRES_EINVAL;  // nothing to hand out
   }
+  if (!form_dw) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+    use_static = false;
+  }
   const int es = elem_bytes(dtype);
-  const Range r_gw = range(grad_w, (int64_t)d * 4);
+  const Range r_gw = form_dw ? range(grad_w, (int64_t)d * 4) : Range{0, 0};
   if (T > 0) {
     if ((sources == nullptr && !(S == 1 && last_source != nullptr)) || w == nullptr || grad_out == nullptr ||
-        grad_sources == nullptr || (!use_static && (workspace == nullptr || workspace_bytes <= 0)))
+        grad_sources == nullptr || (form_dw && !use_static && (workspace == nullptr || workspace_bytes <= 0)))
       return ATTNRES_EINVAL;
     if (!aligned16(sources) || !aligned16(w) || !aligned16(grad_out) || !aligned16(grad_sources) ||
         !aligned16(workspace) || (grad_last != nullptr && !aligned16(grad_last)) ||
@@ -243,10 +252,11 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
     const Range r_g = range(grad_out, row * es);
     const Range r_gs = range(grad_sources, ((int64_t)(S - 1) * grad_stride + row) * 4);
     const Range r_gl = grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0};
-    const Range r_ws = range(workspace, workspace_bytes);
-    // coefficients are written for the deferred sources only, up to the highest one
-    const int top = defer_mask != 0 ? 32 - __builtin_clz(defer_mask) : 0;
-    const Range r_cf = defer_mask != 0 ? range(coef, ((T - 1) * coef_stride + 3 * (int64_t)top) * 4) : Range{0, 0};
+    const Range r_ws = form_dw ? range(workspace, workspace_bytes) : Range{0, 0};
+    // coefficients are written for the deferred sources, up to the highest one
+    // (for all S sources when dL/dw is left to the caller)
+    const int top = !form_dw ? S : defer_mask != 0 ? 32 - __builtin_clz(defer_mask) : 0;
+    const Range r_cf = top > 0 ? range(coef, ((T - 1) * coef_stride + 3 * (int64_t)top) * 4) : Range{0, 0};
     const Range outs[5] = {r_gs, r_gl, r_gw, r_ws, r_cf};
     const Range ins[4] = {r_src, r_w, r_g, r_last};
     for (int i = 0; i < 5; ++i) {
@@ -256,6 +266,7 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
         if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
     }
   }
+  if (!form_dw && T == 0) return ATTNRES_OK;  // no dL/dw to zero: nothing to launch
   const int64_t row_bytes = (int64_t)d * 4;
   if (use_static && row_bytes > attnres::kStaticScratchBytes) return ATTNRES_EINVAL;  // beyond the static array
   int cus = 0;
@@ -266,7 +277,11 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
   if (rc != ATTNRES_OK) return rc;
   const unsigned all = S >= 32 ? 0xFFFFFFFFu : ((1u << S) - 1u);
   const bool last_only = ((~defer_mask & all) & ~(1u << (S - 1))) == 0;
-  int64_t grid = backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, last_only));
+  // with dL/dw formed here each workgroup sums it over the tokens it loops
+  // over; without, a workgroup takes one token (a looping workgroup's loads
+  // queue behind its previous token's stores: 9-13% slower per launch)
+  int64_t grid = form_dw ? backward_grid(T, cus, backward_per_cu(cfg.vecs_per_lane, last_only))
+                         : (T < INT64_C(0x7fffffff) ? T : INT64_C(0x7fffffff));
   if (use_static) {
     // the static array, resolved once per device, and no more rows than it holds
     if (attnres::static_scratch(&workspace) != hipSuccess) return ATTNRES_ELAUNCH;
@@ -274,7 +289,7 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
     const int64_t rows = workspace_bytes / row_bytes;
     if (grid > rows) grid = rows;
   }
-  if (T > 0 && workspace_bytes < grid * row_bytes) return ATTNRES_EINVAL;
+  if (form_dw && T > 0 && workspace_bytes < grid * row_bytes) return ATTNRES_EINVAL;
   attnres::BackwardArgs a;
   a.sources = sources;
   a.S = S;
@@ -296,6 +311,7 @@ int aggregate_backward_impl(const void* sources, int32_t S, int64_t T, int32_t d
   a.eps = eps;
   a.bf16 = dtype == ATTNRES_BF16;
   a.last_only = last_only;
+  a.form_dw = form_dw;
   a.threads = cfg.threads;
   a.vecs_per_lane = cfg.vecs_per_lane;
   a.grid = grid;
@@ -357,10 +373,13 @@ ATTNRES_API int attnres_block_backward_workspace(int64_t T, int32_t d, int32_t B
 
 ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
                                        int32_t B, const void* const* grad_outs, const float* const* queries,
-                                       const float* coef, float* grad_sources, int64_t grad_stride,
-                                       uint32_t accumulate_mask, void* grad_last, float* const* grad_ws,
-                                       void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream) {
+                                       const float* coef, int64_t coef_layer_stride, float* grad_sources,
+                                       int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                       float* const* grad_ws, void* workspace, int64_t workspace_bytes,
+                                       int32_t dtype, void* stream) {
   if (n < 1 || n > attnres::kMaxInterSources || B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  const int64_t cls = coef_layer_stride == 0 ? 3 * (int64_t)n : coef_layer_stride;
+  if (cls < 3 * (int64_t)n) return ATTNRES_EINVAL;
   int rc = check_shape(T, d, dtype);
   if (rc != ATTNRES_OK) return rc;
   const int64_t row = T * (int64_t)d;
@@ -371,8 +390,8 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
   if (n > 1 && (src_stride < row || grad_stride < row)) return ATTNRES_EINVAL;
   if (src_stride % elems_per_vec(dtype) != 0 || grad_stride % 4 != 0) return ATTNRES_EUNSUPPORTED;
   // the dL/dw contraction takes 8 columns per lane and addresses the
-  // coefficients with 32-bit byte offsets
-  if (d % 8 != 0 || T * B * n * 12 >= (INT64_C(1) << 31)) return ATTNRES_EUNSUPPORTED;
+  // coefficients with 32-bit byte offsets: T * B * cls * 4 < 2^31
+  if (d % 8 != 0 || (T > 0 && cls > ((INT64_C(1) << 31) - 1) / (4 * (int64_t)B * T))) return ATTNRES_EUNSUPPORTED;
   if (T == 0) return ATTNRES_OK;
   if (sources == nullptr || grad_outs == nullptr || queries == nullptr || coef == nullptr ||
       grad_sources == nullptr || grad_ws == nullptr || workspace == nullptr)
@@ -382,7 +401,7 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
       (grad_last != nullptr && !aligned16(grad_last)) || (reinterpret_cast<uintptr_t>(coef) & 3u) != 0)
     return ATTNRES_EUNSUPPORTED;
   std::vector<Range> ins = {range(sources, ((int64_t)(n - 1) * src_stride + row) * es),
-                            range(coef, (int64_t)T * B * n * 3 * 4)};
+                            range(coef, (int64_t)T * B * cls * 4)};
   std::vector<Range> outs = {range(grad_sources, ((int64_t)(n - 1) * grad_stride + row) * 4),
                              grad_last != nullptr ? range(grad_last, row * es) : Range{0, 0},
                              range(workspace, workspace_bytes)};
@@ -423,6 +442,7 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
   a.src_stride = src_stride;
   a.B = B;
   a.coef = coef;
+  a.coef_layer = (int)cls;
   a.grad_sources = grad_sources;
   a.grad_stride = grad_stride;
   a.acc_mask = accumulate_mask;
@@ -437,6 +457,100 @@ ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T
   (void)hipGetLastError();
   return attnres::launch_block_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
                                                                                            : ATTNRES_ELAUNCH;
+}
+
+// Token groups of attnres_partial_dw: about 16 workgroups of two waves per CU
+// over the B layers' column blocks, at most one group per token.
+int64_t partial_dw_groups(int64_t T, int d, int32_t dtype, int B, int cus, int* colblocks) {
+  const int64_t nvec = d / elems_per_vec(dtype);
+  *colblocks = (int)((nvec + attnres::kPartialDwThreads - 1) / attnres::kPartialDwThreads);
+  const int64_t per = (int64_t)*colblocks * B;
+  const int64_t want = ((int64_t)cus * 16 + per - 1) / per;
+  return T < want ? (T > 0 ? T : 1) : want;
+}
+
+ATTNRES_API int attnres_partial_dw_workspace(int64_t T, int32_t d, int32_t B, int32_t dtype, int64_t* bytes) {
+  if (bytes == nullptr || B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (T == 0) {
+    *bytes = 0;
+    return ATTNRES_OK;
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  int colblocks = 0;
+  *bytes = partial_dw_groups(T, d, dtype, B, cus, &colblocks) * B * (int64_t)d * 4;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_partial_dw(const void* const* rows, int32_t B, int64_t T, int32_t d, const float* coef,
+                                   int64_t coef_stride, int64_t coef_layer_stride, float* const* grad_ws,
+                                   void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream) {
+  if (B < 1 || B > attnres::kMaxBlockLayers) return ATTNRES_EINVAL;
+  int rc = check_shape(T, d, dtype);
+  if (rc != ATTNRES_OK) return rc;
+  if (rows == nullptr || grad_ws == nullptr) return ATTNRES_EINVAL;
+  // every coefficient offset t * coef_stride + l * coef_layer_stride far inside int64
+  const int64_t lim = (INT64_C(1) << 40) / (T > 0 ? T : 1);
+  if (coef_stride < 0 || coef_stride > lim || coef_layer_stride < 0 || coef_layer_stride > (INT64_C(1) << 40))
+    return ATTNRES_EINVAL;
+  const int64_t row = T * (int64_t)d;
+  const int es = elem_bytes(dtype);
+  bool any = false;  // a row to read (none for T = 0: the rows are only zeroed)
+  for (int l = 0; l < B; ++l) any = any || (rows[l] != nullptr && T > 0);
+  if (any) {
+    if (coef == nullptr) return ATTNRES_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(coef) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+  }
+  std::vector<Range> ins, outs;
+  if (any) ins.push_back(range(coef, ((T - 1) * coef_stride + (int64_t)(B - 1) * coef_layer_stride + 1) * 4));
+  attnres::PartialDwArgs a;
+  for (int l = 0; l < attnres::kMaxBlockLayers; ++l) {
+    a.rows.x[l] = nullptr;
+    a.rows.c[l] = nullptr;
+    a.out.p[l] = nullptr;
+  }
+  for (int l = 0; l < B; ++l) {
+    if (grad_ws[l] == nullptr) return ATTNRES_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(grad_ws[l]) & 3u) != 0) return ATTNRES_EUNSUPPORTED;
+    outs.push_back(range(grad_ws[l], (int64_t)d * 4));
+    a.out.p[l] = grad_ws[l];
+    if (rows[l] == nullptr || T == 0) continue;
+    if (!aligned16(rows[l])) return ATTNRES_EUNSUPPORTED;
+    ins.push_back(range(rows[l], row * es));
+    a.rows.x[l] = rows[l];
+    a.rows.c[l] = coef + l * coef_layer_stride;
+  }
+  if (T > 0) {
+    if (workspace == nullptr) return ATTNRES_EINVAL;
+    if (!aligned16(workspace)) return ATTNRES_EUNSUPPORTED;
+    outs.push_back(range(workspace, workspace_bytes));
+  }
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTNRES_EALIAS;
+    for (size_t k = i + 1; k < outs.size(); ++k)
+      if (overlap(outs[i], outs[k])) return ATTNRES_EALIAS;
+  }
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc != ATTNRES_OK) return rc;
+  int colblocks = 0;
+  const int64_t groups = T > 0 ? partial_dw_groups(T, d, dtype, B, cus, &colblocks) : 0;
+  if (workspace_bytes < groups * B * (int64_t)d * 4) return ATTNRES_EINVAL;
+  a.B = B;
+  a.T = T;
+  a.d = d;
+  a.coef_stride = coef_stride;
+  a.workspace = static_cast<float*>(workspace);
+  a.bf16 = dtype == ATTNRES_BF16;
+  a.colblocks = colblocks;
+  a.groups = groups;
+  (void)hipGetLastError();
+  return attnres::launch_partial_dw(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTNRES_OK
+                                                                                      : ATTNRES_ELAUNCH;
 }
 
 ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t count, int64_t T, int32_t d, void* out,

@@ -18,6 +18,7 @@ hipError_t launch_block_merge(const MergeArgs&, hipStream_t) { return hipErrorNo
 hipError_t launch_aggregate_backward(const BackwardArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_block_backward(const BlockBackwardArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_partial_sums(const PartialSumsArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_partial_dw(const PartialDwArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t static_scratch(void**) { return hipErrorNoDevice; }
 
 }  // namespace attnres

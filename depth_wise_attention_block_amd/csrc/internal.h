@@ -128,6 +128,8 @@ struct BackwardArgs {
   float eps;
   bool bf16;
   bool last_only;         // every row but the last deferred: the streaming kernel
+  bool form_dw;           // dL/dw summed here; else every source's coefficients
+                          // are written and the grid is one workgroup per token
   int threads, vecs_per_lane;
   int64_t grid;
 };
@@ -164,7 +166,8 @@ struct BlockBackwardArgs {
   int64_t src_stride;
   BlockRows rows;
   int B;
-  const float* coef;      // [T][B][n][3]
+  const float* coef;      // [T][B][coef_layer]: layer l's n triples at l * coef_layer
+  int coef_layer;         // floats per layer and token, >= 3n
   float* grad_sources;    // n rows of [T][d] float32 at grad_stride floats
   int64_t grad_stride;
   unsigned acc_mask;
@@ -179,6 +182,29 @@ struct BlockBackwardArgs {
 };
 
 hipError_t launch_block_backward(const BlockBackwardArgs& a, hipStream_t stream);
+
+// Each layer's dL/dw share from a row of its own: x[l] ([T][d] source dtype, or
+// nullptr for none) weighted per token by c[l][t * coef_stride].
+struct DwRows {
+  const void* x[kMaxBlockLayers];
+  const float* c[kMaxBlockLayers];
+};
+// threads of a partial_dw workgroup: its column block is this many 16-byte vectors
+constexpr int kPartialDwThreads = 128;
+struct PartialDwArgs {
+  DwRows rows;
+  int B;
+  int64_t T;
+  int d;
+  int64_t coef_stride;    // floats between consecutive tokens' coefficients
+  OutRows out;            // B rows [d] float32, overwritten
+  float* workspace;       // [groups][B][d] float32
+  bool bf16;
+  int colblocks;          // ceil(vectors per row / kPartialDwThreads)
+  int64_t groups;         // strided token groups
+};
+
+hipError_t launch_partial_dw(const PartialDwArgs& a, hipStream_t stream);
 
 
 // Running partial sums of up to kMaxBlockLayers rows (rows.g holds the inputs).

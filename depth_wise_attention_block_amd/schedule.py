@@ -229,12 +229,16 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     each layer's backward writes three coefficients per token and source, and
     one ``attnres_block_backward`` per block applies them -- one
     read-modify-write of those rows per block instead of one per layer -- and
-    adds those sources' share of each layer's dL/dw.  The final aggregation's
-    sources h_0 .. b_{N-1} are the last block's inter-block sources, so it joins
-    that block's pass as one more layer.
+    adds those sources' share of each layer's dL/dw.  The layers' backwards
+    form no dL/dw themselves (one workgroup per token, nothing summed over
+    tokens): they also write the coefficients of their partial sum, whose
+    share of each layer's dL/dw one ``attnres_partial_dw`` per block forms
+    from the block's recomputed partial sums.  The final aggregation's sources
+    h_0 .. b_{N-1} are the last block's inter-block sources, so it joins that
+    block's pass as one more layer.
     Returns ``(grad_store, grad_w, grad_w_final)``.
     """
-    from .binding import aggregate_backward, block_backward, partial_sums
+    from .binding import aggregate_backward, block_backward, partial_dw, partial_sums
 
     L = len(layer_outputs)
     T, d = store.T, store.d
@@ -251,7 +255,9 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
     slots = store.slots
     dF = torch.empty((T, d), dtype=dt, device=dev)
     partials = torch.empty((block_size, T, d), dtype=dt, device=dev)  # partials[i-2]: before position i
-    coef_all = (torch.empty(T * (block_size + 1) * nblocks * 3, dtype=torch.float32, device=dev)
+    # per token of block n: Bc layer slots of n + 1 triples (the n inter-block
+    # sources, then the layer's own last source)
+    coef_all = (torch.empty(T * (block_size + 1) * (nblocks + 1) * 3, dtype=torch.float32, device=dev)
                 if defer else None)
     holds = [False] * (1 + nblocks)   # which gradient rows already hold a gradient
     final_in_block = defer and final_query is not None
@@ -267,7 +273,7 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
 
     def block_coef(n):
         Bc = block_layers(n)
-        return coef_all[:T * Bc * n * 3].view(T, Bc, n, 3)
+        return coef_all[:T * Bc * (n + 1) * 3].view(T, Bc, n + 1, 3)
 
     with markers.span("output layer backward"):
         if final_query is not None:
@@ -276,9 +282,10 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
                 # h_0 .. b_{N-1} deferred to the last block's pass (its last layer
                 # slot); only b_N's gradient row is written here
                 N, Bc = nblocks, block_layers(nblocks)
+                m = 3 * (N + 1)
                 aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=0,
-                                   defer=(1 << N) - 1, coef=block_coef(N).view(-1)[3 * N * (Bc - 1):],
-                                   coef_stride=3 * N * Bc, grad_w=grad_w_final, grad_last=dF, eps=eps)
+                                   defer=(1 << N) - 1, coef=block_coef(N).view(-1)[m * (Bc - 1):],
+                                   coef_stride=m * Bc, form_dw=False, grad_last=dF, eps=eps)
                 holds[N] = True
             else:
                 aggregate_backward(slots[:S], final_query, grad_final, grad_store[:S], accumulate=acc_mask(range(S)),
@@ -298,22 +305,25 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
                 partial_sums([layer_outputs[j - 1] for j in range(first, last)], partials)
         coef = block_coef(n) if defer else None
         Bc = coef.shape[1] if defer else B
+        m = 3 * (n + 1)    # coefficient floats per layer slot and token
         block_g = [None] * B
         for l in range(last, first - 1, -1):
             i = l - first + 1
             g = dr(l)
             block_g[i - 1] = g
-            cf = dict(defer=(1 << n) - 1, coef=coef.view(-1)[3 * n * (i - 1):], coef_stride=3 * n * Bc) if defer else {}
+            # deferred: coefficients of every source out, dL/dw formed per block
+            cf = (dict(defer=(1 << n) - 1, coef=coef.view(-1)[m * (i - 1):], coef_stride=m * Bc, form_dw=False)
+                  if defer else dict(grad_w=grad_w[l - 1]))
             with markers.span("layer backward", l):
                 if i >= 2:
                     rows = list(range(n + 1))
                     aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n + 1], last_source=partials[i - 2],
-                                       accumulate=acc_mask(rows), grad_w=grad_w[l - 1], grad_last=dF, eps=eps, **cf)
+                                       accumulate=acc_mask(rows), grad_last=dF, eps=eps, **cf)
                     touched = rows if not defer else [n]
                 else:
                     rows = list(range(n))
                     aggregate_backward(slots[:n], queries[l - 1], g, grad_store[:n], accumulate=acc_mask(rows),
-                                       grad_w=grad_w[l - 1], grad_last=None if defer else dF, eps=eps, **cf)
+                                       grad_last=None if defer else dF, eps=eps, **cf)
                     touched = [] if defer else rows
             for r in touched:
                 holds[r] = True
@@ -322,11 +332,16 @@ def run_schedule_backward(store: SourceStore, layer_outputs: Sequence[torch.Tens
         if defer:
             qs = [queries[j - 1] for j in range(first, last + 1)]
             dws = [grad_w[j - 1] for j in range(first, last + 1)]
-            if Bc > B:   # the final aggregation, in the last slot
+            # each layer's own last source: its partial sum (none for the block's first layer)
+            own = [None] + [partials[i - 2] for i in range(2, B + 1)]
+            if Bc > B:   # the final aggregation, in the last slot; its own last source is b_N
                 block_g, qs, dws = block_g + [grad_final], qs + [final_query], dws + [grad_w_final]
+                own = own + [slots[n]]
             with markers.span("gradient rows of block", n):
+                # the partials' share of dL/dw (written), then the inter-block sources' (added)
+                partial_dw(own, coef.view(-1)[3 * n + 1:], m * Bc, m, dws)
                 block_backward(slots[:n], block_g, qs, coef, grad_store[:n], dws, accumulate=acc_mask(range(n)),
-                               grad_last=dF)
+                               grad_last=dF, coef_layer_stride=m)
             holds[:n] = [True] * n
             if on_grad is not None:
                 on_grad(first - 1, dF)

@@ -272,37 +272,42 @@ class ScheduleBackward:
         """Algorithmic bytes of one backward pass.  Every layer reads its
         sources and dL/dr and hands out a gradient; with ``defer`` a layer
         updates only its partial's gradient row and writes 3 coefficients per
-        token and inter-block source, and one pass per block reads the block's
-        inter-block sources, its dL/dr rows and coefficients and writes each
-        inter-block gradient row once (read-modify-write, except in the last
-        block, whose rows the deferred output layer leaves untouched); the
-        output layer is one more layer of the last block's pass.  Without
-        ``defer`` every layer read-modify-writes all its sources' gradient rows.
-        Not counted: the second read of a block's inter-block sources by the
-        dL/dw contraction (an implementation choice, n rows per block)."""
+        token and source (its dL/dw is formed per block), and one pass per
+        block reads the block's inter-block sources, its dL/dr rows and
+        coefficients and writes each inter-block gradient row once
+        (read-modify-write, except in the last block, whose rows the deferred
+        output layer leaves untouched); the output layer is one more layer of
+        the last block's pass.  Without ``defer`` every layer
+        read-modify-writes all its sources' gradient rows and writes its dL/dw.
+        Not counted: the second reads of rows by the dL/dw contractions (an
+        implementation choice: a block's n inter-block sources and the B - 1
+        partial sums, once more per block)."""
         T, d, L, bs = self.T, self.d, self.layers, self.block_size
         row2, row4 = 2 * T * d, 4 * T * d
         nblocks = (L + bs - 1) // bs
         # output layer: sources and g in, dF out; gradient rows written first touch
         # (only b_N's when the other sources are deferred to the last block's pass)
         S = 1 + nblocks
-        total = S * row2 + row2 + row2 + 8 * d
-        total += (row4 + 12 * nblocks * T) if defer else S * row4
+        total = S * row2 + row2 + row2 + 4 * d          # sources, g, dF out; query in
+        total += (row4 + 12 * S * T) if defer else (S * row4 + 4 * d)   # (+ dL/dw out when formed here)
         for n in range(1, nblocks + 1):
             B = min(n * bs, L) - (n - 1) * bs
             if B >= 2:                                   # partial sums recomputed in one pass
                 total += 2 * (B - 1) * row2
             for i in range(1, B + 1):
                 S = n + (1 if i >= 2 else 0)
-                total += S * row2 + row2 + 8 * d             # sources, g; query in, dL/dw out
+                total += S * row2 + row2 + 4 * d             # sources, g; query in
                 if defer:
-                    total += 12 * n * T                      # coefficients of the inter-block sources
+                    total += 12 * S * T                      # coefficients of every source
                     if i >= 2:
                         total += 2 * row4 + row2             # the partial's gradient row, dF out
                 else:
-                    total += 2 * S * row4 + row2             # every gradient row, dF out
+                    total += 2 * S * row4 + row2 + 4 * d     # every gradient row, dF out, dL/dw out
             if defer:                                        # one pass per block (+ the output layer in the last)
                 Bc = B + (1 if n == nblocks else 0)
                 rows = n * row4 if n == nblocks else 2 * n * row4
                 total += n * row2 + Bc * row2 + 12 * n * Bc * T + rows + row2 + 12 * d * Bc
+                # the partial sums' share of dL/dw: each layer's own last source's
+                # c1 in, every layer's dL/dw row written (its row re-read: not counted)
+                total += 4 * T * (Bc - 1) + 4 * d * Bc
         return total

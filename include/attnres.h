@@ -322,12 +322,19 @@ ATTNRES_API int attnres_partial_sums(const void* const* layer_outs, int32_t coun
  *                   sources not in defer_mask (zero for T = 0); a deferred
  *                   source's share, sum over tokens of (delta_s/rho_s) H_s, is
  *                   added by attnres_block_backward with its gradient row.
+ *                   Or NULL: dL/dw is left to the caller -- the three
+ *                   coefficients of EVERY source are written to coef (coef
+ *                   required, coef_stride >= 3S), gradient rows are formed as
+ *                   usual, no workspace is used (it may be NULL), and each
+ *                   workgroup takes one token; attnres_block_backward and
+ *                   attnres_partial_dw then form dL/dw from the coefficients.
  *   workspace       device, at least attnres_aggregate_backward_workspace()
  *                   bytes, 16-byte aligned (NULL allowed for T = 0): one
  *                   float32 row of dL/dw per workgroup, summed in a fixed order,
  *                   so results are bitwise reproducible on one device.
  * Outputs may not overlap the inputs or each other (ATTNRES_EALIAS).  Unlike
- * the forward, T = 0 still launches (to zero grad_w).
+ * the forward, T = 0 still launches (to zero grad_w; with grad_w NULL it
+ * launches nothing).  coef_stride * T must stay below 2^40 (ATTNRES_EINVAL).
  */
 ATTNRES_API int attnres_aggregate_backward(const void* sources, int32_t S, int64_t T, int32_t d, int64_t src_stride,
                                            const void* last_source, const float* w, const void* grad_out,
@@ -377,8 +384,14 @@ ATTNRES_API int attnres_aggregate_backward_static(const void* sources, int32_t S
  *                 float32, added to) are HOST arrays of B pointers.  A "layer"
  *                 may be any aggregation over these sources (e.g. the final
  *                 one of the network).
- *   coef          device float32 [T][B][n][3]: layer l's coefficients, as its
- *                 backward wrote them with coef = coef + 3 n l, coef_stride 3 n B.
+ *   coef          device float32 [T][B][m]: layer l's coefficients, as its
+ *                 backward wrote them with coef = coef + m l, coef_stride m B;
+ *                 its n triples (a, c1, c3) of the inter-block sources come
+ *                 first, m = coef_layer_stride floats apart.
+ *   coef_layer_stride  m >= 3n, or 0 for m = 3n.  A layer whose backward left
+ *                 dL/dw to the caller also wrote the triple of its own last
+ *                 source (its partial block sum) at 3n: m = 3(n + 1) keeps it
+ *                 for attnres_partial_dw.
  *   grad_sources  device, n rows [T][d] float32 at grad_stride floats; rows whose
  *                 bit is set in accumulate_mask are added into, others written.
  *   grad_last     device [T][d] dtype, or NULL: the new gradient row n-1 (the
@@ -387,13 +400,47 @@ ATTNRES_API int attnres_aggregate_backward_static(const void* sources, int32_t S
  *                 16-byte aligned: partial dL/dw rows, summed in a fixed order
  *                 (bitwise reproducible on one device).
  * Outputs may not overlap the inputs or each other (ATTNRES_EALIAS).  Needs d a
- * multiple of 8 and T*B*n*12 < 2^31 (else ATTNRES_EUNSUPPORTED).
+ * multiple of 8 and T*B*m*4 < 2^31 (else ATTNRES_EUNSUPPORTED).
  */
 ATTNRES_API int attnres_block_backward(const void* sources, int32_t n, int64_t T, int32_t d, int64_t src_stride,
                                        int32_t B, const void* const* grad_outs, const float* const* queries,
-                                       const float* coef, float* grad_sources, int64_t grad_stride,
-                                       uint32_t accumulate_mask, void* grad_last, float* const* grad_ws,
-                                       void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
+                                       const float* coef, int64_t coef_layer_stride, float* grad_sources,
+                                       int64_t grad_stride, uint32_t accumulate_mask, void* grad_last,
+                                       float* const* grad_ws, void* workspace, int64_t workspace_bytes,
+                                       int32_t dtype, void* stream);
+
+/*
+ * attnres_partial_dw -- each layer's dL/dw share from a source row of its own.
+ * In Block AttnRes the last source of layer l's aggregation is the partial sum
+ * of its block (kimi.papertok.ai §4.3), read by that layer only; when its
+ * backward left dL/dw to the caller (attnres_aggregate_backward with grad_w
+ * NULL), that source's share, sum over tokens of (delta/rho) H, is formed here
+ * for up to 16 layers in one pass:
+ *   grad_ws[l] = sum over tokens t of coef[t * coef_stride + l * coef_layer_stride] * rows[l][t]
+ * (float32, summed in a fixed order: bitwise reproducible on one device).
+ *   rows          HOST array of B pointers: device [T][d] in dtype, 16-byte
+ *                 aligned, or NULL for a layer without such a row (its
+ *                 grad_ws row is set to zero).
+ *   coef          device float32; for layers written by
+ *                 attnres_aggregate_backward with coef = base + m l and
+ *                 coef_stride m B, pass base + 3 (S-1) + 1 (the c1 of the
+ *                 last source), coef_stride m B and coef_layer_stride m.  May
+ *                 be NULL when no row is given or T = 0.
+ *   grad_ws       HOST array of B pointers: device [d] float32, overwritten
+ *                 (zero for T = 0).
+ *   workspace     device, at least attnres_partial_dw_workspace() bytes,
+ *                 16-byte aligned (NULL allowed for T = 0).
+ * Outputs may not overlap the inputs or each other (ATTNRES_EALIAS); strides
+ * are non-negative with coef_stride * T and coef_layer_stride below 2^40
+ * (ATTNRES_EINVAL).
+ */
+ATTNRES_API int attnres_partial_dw(const void* const* rows, int32_t B, int64_t T, int32_t d, const float* coef,
+                                   int64_t coef_stride, int64_t coef_layer_stride, float* const* grad_ws,
+                                   void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
+
+/* Workspace bytes attnres_partial_dw needs for T tokens of width d and B layers
+ * on the current device (host only apart from a device-attribute query). */
+ATTNRES_API int attnres_partial_dw_workspace(int64_t T, int32_t d, int32_t B, int32_t dtype, int64_t* bytes);
 
 /* Workspace bytes attnres_block_backward needs for T tokens of width d and B
  * layers on the current device (host only apart from a device-attribute query). */

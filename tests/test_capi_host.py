@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B._SIGNATURES)
@@ -329,14 +329,22 @@ def test_backward_host_checks(lib):
     assert bwd(defer=0b011, cf=CF + 2, cfs=9) == B.EUNSUPPORTED
     assert bwd(defer=0b100, cf=CF, cfs=9, gl=GL) == B.EINVAL          # the last source is deferred
     assert bwd(defer=0b011, cf=GS + 4, cfs=9) == B.EALIAS and bwd(defer=0b011, cf=SRC, cfs=9) == B.EALIAS
+    assert bwd(defer=0b011, cf=CF, cfs=1 << 40) == B.EINVAL           # coefficient offsets beyond 2^40
+    # no grad_w: dL/dw left to the caller, every source's coefficients written, no workspace
+    assert bwd(gw=None, cf=CF, cfs=8) == B.EINVAL and bwd(gw=None, cf=CF + 2, cfs=9) == B.EUNSUPPORTED
+    assert bwd(gw=None, cf=GS + 4, cfs=9) == B.EALIAS                  # coefficients of all three sources
+    assert bwd(gw=None, cf=CF + 64, cfs=9, gs=CF) == B.EALIAS
+    assert bwd(gw=None, cf=CF, cfs=9, ws=None, wsb=0) == B.ELAUNCH     # checks pass: the device query fails
+    assert bwd(T=0, gw=None, cf=CF, cfs=9, ws=None, wsb=0) == B.OK     # nothing to launch
+    assert bwd(T=0, gw=None, cf=None, cfs=9) == B.EINVAL
 
     Arr = ctypes.c_void_p * 2
     G2, W2, DW2 = Arr(OUT, OUT + 4096), Arr(W, W + 4096), Arr(GW, GW + 4096)
 
-    def blk(n=3, T=4, d=8, src=SRC, Bl=2, gs_=G2, ws_=W2, cf=CF, grads=GS, gl=None, dtype=B.BF16, gstride=0,
-            dws=DW2, wk=WS, wkb=1 << 20):
-        return B.lib().attnres_block_backward(src, n, T, d, 0, Bl, gs_, ws_, cf, grads, gstride, 0, gl, dws, wk,
-                                              wkb, dtype, None)
+    def blk(n=3, T=4, d=8, src=SRC, Bl=2, gs_=G2, ws_=W2, cf=CF, cls=0, grads=GS, gl=None, dtype=B.BF16,
+            gstride=0, dws=DW2, wk=WS, wkb=1 << 20):
+        return B.lib().attnres_block_backward(src, n, T, d, 0, Bl, gs_, ws_, cf, cls, grads, gstride, 0, gl, dws,
+                                              wk, wkb, dtype, None)
 
     assert blk(n=0) == B.EINVAL and blk(n=9) == B.EINVAL and blk(Bl=0) == B.EINVAL and blk(Bl=17) == B.EINVAL
     assert blk(T=0) == B.OK and blk(d=12) == B.EUNSUPPORTED and blk(gstride=8) == B.EINVAL
@@ -348,6 +356,10 @@ def test_backward_host_checks(lib):
     assert blk(grads=SRC) == B.EALIAS and blk(gl=OUT + 4096) == B.EALIAS and blk(grads=CF) == B.EALIAS
     assert blk(dws=Arr(GW, W)) == B.EALIAS and blk(dws=Arr(GW, GW)) == B.EALIAS and blk(wk=GS) == B.EALIAS
     assert blk(dws=Arr(GW, WS + 64)) == B.EALIAS
+    assert blk(cls=8) == B.EINVAL and blk(cls=-9) == B.EINVAL          # fewer floats per layer than 3n
+    assert blk(cls=1 << 40) == B.EUNSUPPORTED                          # T * B * m * 4 beyond 32-bit offsets
+    assert blk(cls=12, grads=CF + 4 * 2 * 12 * 4 - 16) == B.EALIAS     # the coefficients span T * B * m floats
+    assert blk(cls=12, grads=CF + 4 * 2 * 12 * 4) == B.ELAUNCH and blk(cls=12) == B.ELAUNCH
 
     add = B.lib().attnres_add_rows
     assert add(None, None, W, 4, 8, B.BF16, None) == B.EINVAL and add(None, OUT, None, 4, 8, B.BF16, None) == B.EINVAL
@@ -360,6 +372,35 @@ def test_backward_host_checks(lib):
     assert wsb(0, 8, 3, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
     assert wsb(4, 8, 0, B.BF16, ctypes.byref(out)) == B.EINVAL and wsb(4, 8, 17, B.BF16, ctypes.byref(out)) == B.EINVAL
     assert wsb(4, 12, 3, B.BF16, ctypes.byref(out)) == B.EUNSUPPORTED and wsb(4, 8, 3, B.BF16, None) == B.EINVAL
+
+
+def test_partial_dw_host_checks(lib):
+    """attnres_partial_dw rejects bad arguments before touching the GPU."""
+    Arr = ctypes.c_void_p * 3
+    R0, R1, CF, DW, WS = 0x60000000, 0x61000000, 0x62000000, 0x63000000, 0x64000000
+    ROWS, DWS = Arr(None, R0, R1), Arr(DW, DW + 4096, DW + 8192)
+
+    def pdw(rows=ROWS, Bl=3, T=4, d=8, cf=CF, cs=6, cls=3, dws=DWS, ws=WS, wsb=1 << 20, dtype=B.BF16):
+        return B.lib().attnres_partial_dw(rows, Bl, T, d, cf, cs, cls, dws, ws, wsb, dtype, None)
+
+    assert pdw(Bl=0) == B.EINVAL and pdw(Bl=17) == B.EINVAL and pdw(T=-1) == B.EINVAL
+    assert pdw(d=12) == B.EUNSUPPORTED and pdw(dtype=2) == B.EUNSUPPORTED
+    assert pdw(rows=None) == B.EINVAL and pdw(dws=None) == B.EINVAL and pdw(dws=Arr(DW, None, DW + 64)) == B.EINVAL
+    assert pdw(cs=-1) == B.EINVAL and pdw(cls=-1) == B.EINVAL and pdw(cs=1 << 40) == B.EINVAL
+    assert pdw(cls=(1 << 40) + 1) == B.EINVAL
+    assert pdw(cf=None) == B.EINVAL and pdw(cf=CF + 2) == B.EUNSUPPORTED          # rows need coefficients
+    assert pdw(rows=Arr(None, R0 + 8, R1)) == B.EUNSUPPORTED and pdw(dws=Arr(DW, DW + 2, DW + 64)) == B.EUNSUPPORTED
+    assert pdw(ws=None) == B.EINVAL and pdw(ws=WS + 8) == B.EUNSUPPORTED
+    assert pdw(dws=Arr(DW, R0 + 16, DW + 64)) == B.EALIAS and pdw(dws=Arr(DW, CF + 8, DW + 64)) == B.EALIAS
+    assert pdw(dws=Arr(DW, DW + 16, DW + 64)) == B.EALIAS and pdw(ws=R1) == B.EALIAS and pdw(ws=DW) == B.EALIAS
+    assert pdw(dws=Arr(DW, CF + 4 * (3 * 6 + 2 * 3) + 4, DW + 64)) == B.ELAUNCH   # past the last coefficient
+    assert pdw(rows=Arr(None, None, None), cf=None) == B.ELAUNCH    # nothing to read: checks pass
+    assert pdw(T=0, cf=None, ws=None) == B.ELAUNCH                  # zeroes the rows: checks pass
+    out = ctypes.c_int64()
+    wsq = B.lib().attnres_partial_dw_workspace
+    assert wsq(0, 8, 3, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
+    assert wsq(4, 8, 0, B.BF16, ctypes.byref(out)) == B.EINVAL and wsq(4, 8, 17, B.BF16, ctypes.byref(out)) == B.EINVAL
+    assert wsq(4, 12, 3, B.BF16, ctypes.byref(out)) == B.EUNSUPPORTED and wsq(4, 8, 3, B.BF16, None) == B.EINVAL
 
 
 def test_backward_static_checks_like_the_workspace_entry_point(lib):
@@ -378,6 +419,7 @@ def test_backward_static_checks_like_the_workspace_entry_point(lib):
     assert bs(src=SRC + 8) == B.EUNSUPPORTED and bs(gw=GW + 2) == B.EUNSUPPORTED
     assert bs(gs=SRC + 32) == B.EALIAS and bs(gl=G) == B.EALIAS and bs(gw=W) == B.EALIAS
     assert bs(defer=1) == B.EINVAL                                 # deferred sources need coef
+    assert bs(gw=None, cf=None) == B.EINVAL and bs(gw=None, cf=0xB0000000, cs=9) == B.ELAUNCH
     assert bs() == B.ELAUNCH                                       # checks passed: the device query fails here
 
 

@@ -470,6 +470,149 @@ def test_block_backward_matches_oracle(dtype, n, Bl, T, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("S,defer,T,d,acc", [(9, 0xFF, 37, 7168, 0x100), (9, 0, 37, 7168, 0x1FF),
+                                             (4, 0b0101, 45, 1032, 0b1010), (3, 0b111, 20, 264, 0),
+                                             (2, 0b01, 300, 7176, 0b10), (1, 0b0, 9, 7168, 1)])
+def test_backward_without_dw_matches_oracle_and_the_dw_form(dtype, S, defer, T, d, acc):
+    """grad_w NULL (dL/dw left to the caller, one workgroup per token): the
+    gradient rows, the handed-out copy and the deferred sources' coefficients
+    are those of the dL/dw form bit for bit; every source's coefficients are
+    written, the non-deferred ones recombine to the oracle's dH_s, and their
+    c1 summed over tokens with the rows (float64, on the host) is the oracle's
+    dL/dw share of those sources."""
+    note(f"backward without dw dtype={dtype} S={S} defer={defer:#x} T={T} d={d} acc={acc:#x}")
+    H, w, g = inputs(S, T, d, dtype, seed=S * 5 + T)
+    dev = H.device
+    prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(8), device=dev)
+    last_deferred = (defer >> (S - 1)) & 1
+    runs = []
+    for form_dw in (True, False):
+        grads = prefill.clone()
+        coef = torch.full((T, 3 * S), float("nan"), dtype=torch.float32, device=dev)
+        hand = None if last_deferred else torch.empty((T, d), dtype=dtype, device=dev)
+        kw = dict(coef=coef, coef_stride=3 * S) if (defer or not form_dw) else {}
+        dw = B.aggregate_backward(H, w, g, grads, accumulate=acc, defer=defer, grad_last=hand, form_dw=form_dw, **kw)
+        runs.append((grads, coef, hand, dw))
+    torch.cuda.synchronize()
+    (ga, ca, ha, dwa), (gb, cb, hb, dwb) = runs
+    assert dwb is None
+    assert torch.equal(ga, gb), "gradient rows differ between the two forms"
+    if ha is not None:
+        assert torch.equal(ha, hb), "handed-out gradient differs"
+    cfa = host(ca).reshape(T, S, 3)
+    cf = host(cb).astype(np.float64).reshape(T, S, 3)
+    assert not np.any(np.isnan(cf)), "a source's coefficients were not written"
+    Hh, wh, gh = host(H), host(w), host(g)
+    dH_ref, _, dw_src = orc.depth_attention_backward(Hh, wh, gh, per_source=True)
+    bH, bw = bounds(Hh, wh, gh)
+    share = np.zeros(d)
+    for s in range(S):
+        if (defer >> s) & 1:
+            assert np.array_equal(cfa[:, s].view(np.int32), host(cb).reshape(T, S, 3)[:, s].view(np.int32)), \
+                f"coefficients of deferred source {s} differ"
+            continue
+        rec = cf[:, s, 0:1] * gh + cf[:, s, 1:2] * wh[None] - cf[:, s, 2:3] * Hh[s]
+        err = np.abs(rec - dH_ref[s])
+        lim = C_BWD * bH[s] + 2.0 ** -22 * np.abs(dH_ref[s])
+        assert np.all(err <= lim), f"coefficients of source {s}: ratio {np.max(err / lim):.3g}"
+        share += dw_src[s]
+    mine = sum(cf[:, s, 1] @ Hh[s] for s in range(S) if not (defer >> s) & 1) if defer != (1 << S) - 1 else 0.0
+    errw = np.abs(mine - share)
+    limw = C_BWD * bw + 2.0 ** -23 * np.abs(share) + np.finfo(np.float32).tiny
+    assert np.all(errw <= limw), f"dw share from the coefficients: ratio {np.max(errw / limw):.3g}"
+
+
+def test_backward_without_dw_empty_batch_launches_nothing():
+    dev = device()
+    H = torch.empty((3, 0, 264), dtype=torch.bfloat16, device=dev)
+    grads = torch.empty((3, 0, 264), dtype=torch.float32, device=dev)
+    coef = torch.empty(9, dtype=torch.float32, device=dev)
+    B.aggregate_backward(H, synth.query(264, device=dev), torch.empty((0, 264), dtype=torch.bfloat16, device=dev),
+                         grads, defer=0b011, coef=coef, coef_stride=9, form_dw=False)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("T,d,Bl", [(1, 8, 1), (37, 264, 3), (1000, 7168, 12), (4099, 520, 16), (32768, 7168, 2)])
+def test_partial_dw_matches_float64(dtype, T, d, Bl):
+    """attnres_partial_dw: grad_ws[l] = sum_t c_l[t] X_l[t] for the layers with a
+    row (layer 0 and every third have none and get zeros), coefficients read
+    at an odd layer stride from mid-buffer, against a float64 sum on the host
+    (all columns, or 256 sampled ones at T = 32,768); bitwise equal on a
+    second call.  The float32 sum runs over token groups and then the groups:
+    its error is far below 1e-4 of sum |c x|."""
+    dev = device()
+    note(f"partial dw dtype={dtype} T={T} d={d} B={Bl}")
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    rows = [None if (l % 3 == 0) else synth.layer_output(T, d, std=1.5, seed=T + l, tag=300 + l, device=dev,
+                                                          dtype=name) for l in range(Bl)]
+    m = 7
+    gen = torch.Generator(device=dev).manual_seed(T + Bl)
+    coef = torch.randn((T * Bl * m + 8,), generator=gen, device=dev) * torch.exp(
+        torch.randn((T * Bl * m + 8,), generator=gen, device=dev))
+    base = coef[4:]
+    outs = []
+    for _ in range(2):
+        dws = [torch.full((d,), float("nan"), dtype=torch.float32, device=dev) for _ in range(Bl)]
+        B.partial_dw(rows, base, Bl * m, m, dws)
+        outs.append(dws)
+    torch.cuda.synchronize()
+    cols = np.arange(d) if T * d <= 8 << 20 else np.sort(np.random.default_rng(T).choice(d, 256, replace=False))
+    c = host(base)[: T * Bl * m].astype(np.float64).reshape(T, Bl, m)[:, :, 0]
+    for l in range(Bl):
+        assert torch.equal(outs[0][l], outs[1][l]), f"layer {l}: not reproducible"
+        got = host(outs[0][l]).astype(np.float64)
+        if rows[l] is None:
+            assert np.all(got == 0.0), f"layer {l} has no row: its dL/dw share must be zero"
+            continue
+        X = host(rows[l][:, torch.as_tensor(cols, device=dev)]).astype(np.float64)
+        want = c[:, l] @ X
+        mag = np.abs(c[:, l]) @ np.abs(X)
+        err = np.abs(got[cols] - want)
+        assert np.all(err <= 1e-4 * mag + 1e-30), f"layer {l}: ratio {np.max(err / (1e-4 * mag + 1e-30)):.3g}"
+
+
+def test_partial_dw_empty_batch_zeroes_the_rows():
+    dev = device()
+    dws = [torch.full((264,), 3.0, dtype=torch.float32, device=dev) for _ in range(3)]
+    rows = [None, torch.empty((0, 264), dtype=torch.bfloat16, device=dev), None]
+    B.partial_dw(rows, None, 9, 3, dws)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, torch.zeros_like(x)) for x in dws)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("n,Bl,T,d", [(1, 3, 9, 8), (5, 12, 77, 1032), (8, 16, 33, 2056)])
+def test_block_backward_layer_stride_is_the_packed_layout(dtype, n, Bl, T, d):
+    """attnres_block_backward with m = 3(n + 1) floats per layer slot (a layer's
+    own last source's triple after the n inter-block ones, filled with
+    garbage here) gives the packed [T][B][n][3] layout's results bit for bit:
+    gradient rows, handed-out row and every layer's dL/dw."""
+    dev = device()
+    note(f"block backward layer stride dtype={dtype} n={n} B={Bl} T={T} d={d}")
+    H, _, _ = inputs(n, T, d, dtype, seed=n + Bl)
+    name = "bf16" if dtype == torch.bfloat16 else "f32"
+    Ws = [synth.query(d, seed=n, device=dev, tag=l) for l in range(Bl)]
+    Gs = [synth.layer_output(T, d, std=1.0, seed=n, tag=70 + l, device=dev, dtype=name) for l in range(Bl)]
+    gen = torch.Generator(device=dev).manual_seed(n * Bl)
+    wide = torch.randn((T, Bl, n + 1, 3), generator=gen, device=dev) * 1e-2
+    packed = wide[:, :, :n].contiguous()
+    wide[:, :, n] = 1e30                               # never read
+    prefill = torch.randn((n, T, d), generator=gen, device=dev)
+    res = []
+    for coef, m in ((packed, 0), (wide, 3 * (n + 1))):
+        grads = prefill.clone()
+        dws = [torch.full((d,), 0.25, dtype=torch.float32, device=dev) for _ in range(Bl)]
+        emit = torch.empty((T, d), dtype=dtype, device=dev)
+        B.block_backward(H, Gs, Ws, coef, grads, dws, accumulate=(1 << n) - 1, grad_last=emit, coef_layer_stride=m)
+        res.append((grads, dws, emit))
+    torch.cuda.synchronize()
+    (g0, w0, e0), (g1, w1, e1) = res
+    assert torch.equal(g0, g1) and torch.equal(e0, e1)
+    assert all(torch.equal(a, b) for a, b in zip(w0, w1))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("count", [1, 2, 11, 16])
 def test_partial_sums_are_the_store_updates(dtype, count):
     """attnres_partial_sums equals the oracle's update chain bit for bit."""

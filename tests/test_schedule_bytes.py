@@ -122,14 +122,15 @@ def _run_backward(T, d, defer, layers=93, block_size=12):
     total = [0]
 
     def count_aggregate_backward(sources, w, grad_out, grad_sources, *, last_source=None, accumulate=0, defer=0,
-                                 coef=None, coef_stride=0, grad_w=None, grad_last=None, workspace=None, eps=1e-5,
-                                 stream=None):
+                                 coef=None, coef_stride=0, grad_w=None, grad_last=None, workspace=None,
+                                 form_dw=True, eps=1e-5, stream=None):
         S = grad_sources.shape[0]
-        b = S * row2 + row2 + 4 * d + 4 * d                 # sources, dL/dr, query; dL/dw out
+        b = S * row2 + row2 + 4 * d                         # sources, dL/dr, query
+        b += 4 * d if form_dw else 0                        # dL/dw out
         for s in range(S):
-            if (defer >> s) & 1:
+            if (defer >> s) & 1 or not form_dw:
                 b += 12 * T                                    # three coefficients per token
-            else:
+            if not (defer >> s) & 1:
                 b += row4 + (row4 if (accumulate >> s) & 1 else 0)   # the gradient row written (and read)
         if grad_last is not None:
             b += row2
@@ -137,7 +138,7 @@ def _run_backward(T, d, defer, layers=93, block_size=12):
         return grad_w
 
     def count_block_backward(sources, grad_outs, queries, coef, grad_sources, grad_ws, *, accumulate=0,
-                             grad_last=None, workspace=None, stream=None):
+                             grad_last=None, coef_layer_stride=0, workspace=None, stream=None):
         n, B = sources.shape[0], len(grad_outs)
         b = n * row2 + B * row2 + 12 * n * B * T           # sources, dL/dr rows, coefficients
         b += sum(row4 + (row4 if (accumulate >> s) & 1 else 0) for s in range(n))   # gradient rows
@@ -150,9 +151,14 @@ def _run_backward(T, d, defer, layers=93, block_size=12):
         total[0] += 2 * len(layer_outs) * row2              # each layer output in, each partial sum out
         return out
 
-    saved = binding.aggregate_backward, binding.block_backward, binding.partial_sums
-    binding.aggregate_backward, binding.block_backward, binding.partial_sums = (
-        count_aggregate_backward, count_block_backward, count_partial_sums)
+    def count_partial_dw(rows, coef, coef_stride, coef_layer_stride, grad_ws, *, workspace=None, stream=None):
+        # one coefficient per token of each given row in (the row itself is a
+        # second read, as in the block's contraction), every dL/dw row out
+        total[0] += sum(4 * T for r in rows if r is not None) + 4 * d * len(grad_ws)
+
+    saved = binding.aggregate_backward, binding.block_backward, binding.partial_sums, binding.partial_dw
+    binding.aggregate_backward, binding.block_backward, binding.partial_sums, binding.partial_dw = (
+        count_aggregate_backward, count_block_backward, count_partial_sums, count_partial_dw)
     try:
         F = [torch.zeros((T, d), dtype=torch.bfloat16) for _ in range(layers)]
         W = [torch.zeros(d) for _ in range(layers)]
@@ -160,7 +166,7 @@ def _run_backward(T, d, defer, layers=93, block_size=12):
         schedule.run_schedule_backward(store, F, W, block_size, G, final_query=torch.zeros(d),
                                        grad_final=torch.zeros((T, d), dtype=torch.bfloat16), defer=defer)
     finally:
-        binding.aggregate_backward, binding.block_backward, binding.partial_sums = saved
+        binding.aggregate_backward, binding.block_backward, binding.partial_sums, binding.partial_dw = saved
     return total[0]
 
 
