@@ -3,7 +3,8 @@ d = 8192: four 16-byte vectors per lane) and at three vectors per lane (bf16
 d = 10000, float32 d = 5000), for every kernel family: the aggregation in each
 of its source-bound instances, plain and fused with the partial update, and
 over more than 9 sources; the two-phase pair; the backward (the general
-kernel, the last-source kernel and the block pass with its dL/dw contraction).
+kernel, the last-source kernel, with dL/dw formed or left to the caller, the
+block pass with its dL/dw contraction and the partial sums' dL/dw pass).
 These are the instances the other tests, at d <= 8192 bf16, do not reach.  A
 few tokens keep the oracle fast."""
 
@@ -117,19 +118,28 @@ def test_wide_two_phase(d, n_completed, close):
 
 @pytest.mark.parametrize("dtype,d", WIDE)
 @pytest.mark.parametrize("S,acc", [(3, 0b101), (9, 0x1FF)])
-def test_wide_backward(dtype, d, S, acc):
-    """The general backward kernel (every source's row written or added)."""
+@pytest.mark.parametrize("form_dw", [True, False], ids=["dw", "coef"])
+def test_wide_backward(dtype, d, S, acc, form_dw):
+    """The general backward kernel (every source's row written or added); with
+    dL/dw left to the caller, dL/dw summed on the host from the coefficients
+    it writes for every source."""
     T = 6
-    note(f"wide backward {dtype} d={d} S={S} acc={acc:#x}")
+    note(f"wide backward {dtype} d={d} S={S} acc={acc:#x} form_dw={form_dw}")
     H, w, g = inputs(S, T, d, TDT[dtype], seed=S + d)
     dev = H.device
     prefill = torch.randn((S, T, d), generator=torch.Generator(device=dev).manual_seed(3), device=dev)
     grads = prefill.clone()
     hand = torch.empty((T, d), dtype=TDT[dtype], device=dev)
-    dw = B.aggregate_backward(H, w, g, grads, accumulate=acc, grad_last=hand)
+    coef = torch.full((T, 3 * S), float("nan"), dtype=torch.float32, device=dev)
+    kw = {} if form_dw else dict(form_dw=False, coef=coef, coef_stride=3 * S)
+    dw = B.aggregate_backward(H, w, g, grads, accumulate=acc, grad_last=hand, **kw)
     torch.cuda.synchronize()
+    if not form_dw:
+        cf = host(coef).astype(np.float64).reshape(T, S, 3)
+        dw = sum(cf[:, s, 1] @ host(H[s]).astype(np.float64) for s in range(S))
     pre = np.stack([host(prefill[s]) if (acc >> s) & 1 else np.zeros((T, d)) for s in range(S)])
-    check(host(grads), host(dw), host(H), host(w), host(g), f"wide backward {dtype} d={d} S={S}", prefill=pre)
+    check(host(grads), host(dw) if form_dw else dw, host(H), host(w), host(g), f"wide backward {dtype} d={d} S={S}",
+          prefill=pre)
     assert torch.equal(hand, grads[S - 1].to(TDT[dtype])), "handed-out gradient is not the row's rounding"
 
 
@@ -194,6 +204,52 @@ def test_wide_block_backward(dtype, d):
         bH_tot += bH
         e = np.abs(host(dws[l]).astype(np.float64) - dw_ref)
         assert np.all(e <= C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref)), f"dL/dw layer {l}"
+    err = np.abs(host(grads) - ref)
+    lim = C_BWD * bH_tot + 2.0 ** -22 * np.abs(ref) + 2.0 ** -23 * np.abs(host(prefill))
+    assert np.all(err <= lim), f"gradient rows: ratio {np.max(err / lim):.3g}"
+
+
+@pytest.mark.parametrize("dtype,d", WIDE)
+def test_wide_block_with_dw_per_block(dtype, d):
+    """The schedule's deferred form at the widest rows: n = 3 inter-block
+    sources and 3 layers, each with a partial sum of its own as last source;
+    the layers form no dL/dw (one workgroup per token) and write n + 1 triples
+    per token, attnres_partial_dw forms the partials' share and the block pass
+    (at that wider coefficient stride) adds the rest: each partial's gradient
+    row, the inter-block rows and every layer's whole dL/dw against the oracle."""
+    n, Bl, T = 3, 3, 5
+    m = 3 * (n + 1)
+    note(f"wide block with dL/dw per block {dtype} d={d}")
+    H, _, _ = inputs(n, T, d, TDT[dtype], seed=d + 2)
+    dev = H.device
+    Ws = [synth.query(d, seed=d, device=dev, tag=10 + l) for l in range(Bl)]
+    Gs = [synth.layer_output(T, d, std=1.0, seed=d, tag=90 + l, device=dev, dtype=dtype) for l in range(Bl)]
+    Ps = [synth.layer_output(T, d, std=3.0, seed=d, tag=95 + l, device=dev, dtype=dtype) for l in range(Bl)]
+    prefill = torch.randn((n, T, d), generator=torch.Generator(device=dev).manual_seed(10), device=dev)
+    grads = prefill.clone()
+    coef = torch.full((T, Bl, n + 1, 3), float("nan"), dtype=torch.float32, device=dev)
+    own = [torch.zeros((n + 1, T, d), dtype=torch.float32, device=dev) for _ in range(Bl)]
+    for l in range(Bl):
+        B.aggregate_backward(H, Ws[l], Gs[l], own[l], last_source=Ps[l], defer=(1 << n) - 1,
+                             coef=coef.view(-1)[m * l:], coef_stride=m * Bl, form_dw=False)
+    dws = [torch.full((d,), float("nan"), dtype=torch.float32, device=dev) for _ in range(Bl)]
+    B.partial_dw(Ps, coef.view(-1)[3 * n + 1:], m * Bl, m, dws)
+    B.block_backward(H, Gs, Ws, coef, grads, dws, accumulate=(1 << n) - 1, coef_layer_stride=m)
+    torch.cuda.synchronize()
+    Hh = host(H)
+    ref = host(prefill).astype(np.float64)
+    bH_tot = np.zeros_like(ref)
+    tiny = np.finfo(np.float32).tiny
+    for l in range(Bl):
+        src = np.concatenate([Hh, host(Ps[l])[None]])
+        dH, dw_ref = orc.depth_attention_backward(src, host(Ws[l]), host(Gs[l]))
+        bH, bw = bounds(src, host(Ws[l]), host(Gs[l]))
+        ref += dH[:n]
+        bH_tot += bH[:n]
+        e = np.abs(host(own[l][n]) - dH[n])
+        assert np.all(e <= C_BWD * bH[n] + 2.0 ** -22 * np.abs(dH[n]) + tiny), f"partial row of layer {l}"
+        e = np.abs(host(dws[l]).astype(np.float64) - dw_ref)
+        assert np.all(e <= C_BWD * bw + 2.0 ** -23 * np.abs(dw_ref) + tiny), f"dL/dw layer {l}"
     err = np.abs(host(grads) - ref)
     lim = C_BWD * bH_tot + 2.0 ** -22 * np.abs(ref) + 2.0 ** -23 * np.abs(host(prefill))
     assert np.all(err <= lim), f"gradient rows: ratio {np.max(err / lim):.3g}"
