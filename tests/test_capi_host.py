@@ -1,7 +1,9 @@
 """The C ABI on a host without a GPU: the library loads, exports every symbol the
 header declares, and its host-side logic (argument checks, launch-shape policy,
 source-store state machine) behaves as documented.  No kernel is launched:
-every call here fails its checks before the first HIP call, or has T = 0."""
+every call here fails its checks before the first HIP call, or has T = 0 where
+that launches nothing, or passes its checks and stops at the device query --
+a call made only where no GPU is visible (``passes_host_checks``)."""
 
 import ctypes
 import math
@@ -9,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from depth_wise_attention_block_amd import binding as B
 
@@ -18,6 +21,18 @@ HEADER = os.path.join(REPO, "include", "attnres.h")
 # Fake, 16-byte aligned, non-overlapping device addresses: never dereferenced,
 # because every call below is rejected on the host (or has nothing to do).
 SRC, W, OUT, WTS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+# Counting devices initialises no GPU.  With one visible, a call that passes
+# every host check would launch on the fake addresses above.
+NO_GPU = torch.cuda.device_count() == 0
+
+
+def passes_host_checks(call):
+    """``call()`` passes every host check: on a host without a GPU it then stops
+    at the device query (ATTNRES_ELAUNCH).  Where a GPU is visible the call is
+    not made."""
+    if NO_GPU:
+        assert call() == B.ELAUNCH
 
 
 @pytest.fixture(scope="module")
@@ -334,7 +349,7 @@ def test_backward_host_checks(lib):
     assert bwd(gw=None, cf=CF, cfs=8) == B.EINVAL and bwd(gw=None, cf=CF + 2, cfs=9) == B.EUNSUPPORTED
     assert bwd(gw=None, cf=GS + 4, cfs=9) == B.EALIAS                  # coefficients of all three sources
     assert bwd(gw=None, cf=CF + 64, cfs=9, gs=CF) == B.EALIAS
-    assert bwd(gw=None, cf=CF, cfs=9, ws=None, wsb=0) == B.ELAUNCH     # checks pass: the device query fails
+    passes_host_checks(lambda: bwd(gw=None, cf=CF, cfs=9, ws=None, wsb=0))
     assert bwd(T=0, gw=None, cf=CF, cfs=9, ws=None, wsb=0) == B.OK     # nothing to launch
     assert bwd(T=0, gw=None, cf=None, cfs=9) == B.EINVAL
 
@@ -359,7 +374,8 @@ def test_backward_host_checks(lib):
     assert blk(cls=8) == B.EINVAL and blk(cls=-9) == B.EINVAL          # fewer floats per layer than 3n
     assert blk(cls=1 << 40) == B.EUNSUPPORTED                          # T * B * m * 4 beyond 32-bit offsets
     assert blk(cls=12, grads=CF + 4 * 2 * 12 * 4 - 16) == B.EALIAS     # the coefficients span T * B * m floats
-    assert blk(cls=12, grads=CF + 4 * 2 * 12 * 4) == B.ELAUNCH and blk(cls=12) == B.ELAUNCH
+    passes_host_checks(lambda: blk(cls=12, grads=CF + 4 * 2 * 12 * 4))
+    passes_host_checks(lambda: blk(cls=12))
 
     add = B.lib().attnres_add_rows
     assert add(None, None, W, 4, 8, B.BF16, None) == B.EINVAL and add(None, OUT, None, 4, 8, B.BF16, None) == B.EINVAL
@@ -393,9 +409,9 @@ def test_partial_dw_host_checks(lib):
     assert pdw(ws=None) == B.EINVAL and pdw(ws=WS + 8) == B.EUNSUPPORTED
     assert pdw(dws=Arr(DW, R0 + 16, DW + 64)) == B.EALIAS and pdw(dws=Arr(DW, CF + 8, DW + 64)) == B.EALIAS
     assert pdw(dws=Arr(DW, DW + 16, DW + 64)) == B.EALIAS and pdw(ws=R1) == B.EALIAS and pdw(ws=DW) == B.EALIAS
-    assert pdw(dws=Arr(DW, CF + 4 * (3 * 6 + 2 * 3) + 4, DW + 64)) == B.ELAUNCH   # past the last coefficient
-    assert pdw(rows=Arr(None, None, None), cf=None) == B.ELAUNCH    # nothing to read: checks pass
-    assert pdw(T=0, cf=None, ws=None) == B.ELAUNCH                  # zeroes the rows: checks pass
+    passes_host_checks(lambda: pdw(dws=Arr(DW, CF + 4 * (3 * 6 + 2 * 3) + 4, DW + 64)))  # past the last coefficient
+    passes_host_checks(lambda: pdw(rows=Arr(None, None, None), cf=None))    # nothing to read
+    passes_host_checks(lambda: pdw(T=0, cf=None, ws=None))                  # T = 0 still zeroes the rows
     out = ctypes.c_int64()
     wsq = B.lib().attnres_partial_dw_workspace
     assert wsq(0, 8, 3, B.BF16, ctypes.byref(out)) == B.OK and out.value == 0
@@ -419,8 +435,9 @@ def test_backward_static_checks_like_the_workspace_entry_point(lib):
     assert bs(src=SRC + 8) == B.EUNSUPPORTED and bs(gw=GW + 2) == B.EUNSUPPORTED
     assert bs(gs=SRC + 32) == B.EALIAS and bs(gl=G) == B.EALIAS and bs(gw=W) == B.EALIAS
     assert bs(defer=1) == B.EINVAL                                 # deferred sources need coef
-    assert bs(gw=None, cf=None) == B.EINVAL and bs(gw=None, cf=0xB0000000, cs=9) == B.ELAUNCH
-    assert bs() == B.ELAUNCH                                       # checks passed: the device query fails here
+    assert bs(gw=None, cf=None) == B.EINVAL
+    passes_host_checks(lambda: bs(gw=None, cf=0xB0000000, cs=9))
+    passes_host_checks(bs)
 
 
 def test_partial_sums_host_checks(lib):
@@ -581,3 +598,80 @@ def test_c_client_checks_its_input_before_any_gpu_call(tmp_path):
     bad.write_bytes(struct.pack("<4i", 0, 4, 16, 0))
     r = subprocess.run([client, str(bad), str(tmp_path / "out.bin")], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "bad header" in r.stderr
+
+
+# ---- property-based sweep of the argument checks ---------------------------
+# Random sizes, strides (from edge values: negative, zero, tiny, the largest
+# accepted, just past it, near int64's end) and fake pointers (aligned,
+# misaligned, overlapping each other, null): every call must return one of the
+# documented statuses, and -- in the sanitized child run of this file -- do so
+# without an out-of-bounds access or an integer overflow in the range and
+# alias arithmetic.  Calls that pass their checks stop at the device query, so
+# the sweep runs only where no GPU is visible.
+
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+STATUSES = {B.OK, B.EINVAL, B.EUNSUPPORTED, B.EALIAS, B.ELAUNCH}
+EDGE = [-(1 << 62), -1, 0, 1, 2, 3, 4, 7, 8, 9, 12, 16, 17, 27, 255, 256, 4096, 7168, 7176, 8192, 16384, 16392,
+        (1 << 31) - 1, 1 << 31, 1 << 37, (1 << 40) // 8, 1 << 40, (1 << 40) + 1, 1 << 62, (1 << 63) - 1]
+PTRS = [None, 0x10000000, 0x10000008, 0x10000010, 0x10000400, 0x20000000, 0x30000000, 0x30000004, 0x7FFFFFFFFFF0]
+ints = st.sampled_from(EDGE)
+small = st.integers(min_value=-2, max_value=18)
+ptrs = st.sampled_from(PTRS)
+FUZZ = settings(max_examples=300, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+no_gpu = pytest.mark.skipif(not NO_GPU, reason="a call that passes its checks would launch on fake addresses")
+
+
+def _arr(items):
+    return (ctypes.c_void_p * max(len(items), 1))(*items)
+
+
+@no_gpu
+@FUZZ
+@given(S=small, T=ints, d=ints, src_stride=ints, grad_stride=ints, coef_stride=ints, ws_bytes=ints,
+       acc=st.integers(0, 0x3FF), defer=st.integers(0, 0x3FF), dtype=st.sampled_from([0, 1, 2]),
+       p=st.lists(ptrs, min_size=9, max_size=9), static=st.booleans())
+def test_fuzz_aggregate_backward(lib, S, T, d, src_stride, grad_stride, coef_stride, ws_bytes, acc, defer, dtype, p,
+                                 static):
+    src, last, w, g, gs, cf, gl, gw, ws = p
+    if static:
+        rc = B.lib().attnres_aggregate_backward_static(src, S, T, d, src_stride, last, w, g, gs, grad_stride, acc,
+                                                       defer, cf, coef_stride, gl, gw, 1e-5, dtype, None)
+    else:
+        rc = B.lib().attnres_aggregate_backward(src, S, T, d, src_stride, last, w, g, gs, grad_stride, acc, defer,
+                                                cf, coef_stride, gl, gw, ws, ws_bytes, 1e-5, dtype, None)
+    assert rc in STATUSES
+
+
+@no_gpu
+@FUZZ
+@given(n=small, Bl=small, T=ints, d=ints, src_stride=ints, grad_stride=ints, cls=ints, ws_bytes=ints,
+       dtype=st.sampled_from([0, 1, 2]), p=st.lists(ptrs, min_size=5, max_size=5),
+       rows=st.lists(ptrs, min_size=16, max_size=16), qs=st.lists(ptrs, min_size=16, max_size=16),
+       dws=st.lists(ptrs, min_size=16, max_size=16))
+def test_fuzz_block_backward(lib, n, Bl, T, d, src_stride, grad_stride, cls, ws_bytes, dtype, p, rows, qs, dws):
+    src, cf, gs, gl, ws = p
+    rc = B.lib().attnres_block_backward(src, n, T, d, src_stride, Bl, _arr(rows), _arr(qs), cf, cls, gs, grad_stride,
+                                        0xFF, gl, _arr(dws), ws, ws_bytes, dtype, None)
+    assert rc in STATUSES
+
+
+@no_gpu
+@FUZZ
+@given(Bl=small, T=ints, d=ints, cs=ints, cls=ints, ws_bytes=ints, dtype=st.sampled_from([0, 1, 2]),
+       cf=ptrs, ws=ptrs, rows=st.lists(ptrs, min_size=16, max_size=16), dws=st.lists(ptrs, min_size=16, max_size=16))
+def test_fuzz_partial_dw(lib, Bl, T, d, cs, cls, ws_bytes, dtype, cf, ws, rows, dws):
+    rc = B.lib().attnres_partial_dw(_arr(rows), Bl, T, d, cf, cs, cls, _arr(dws), ws, ws_bytes, dtype, None)
+    assert rc in STATUSES
+
+
+@no_gpu
+@FUZZ
+@given(S=st.sampled_from([-1, 0, 1, 2, 9, 10, 94, 256, 257]), T=ints, d=ints, stride=ints,
+       dtype=st.sampled_from([0, 1, 2]), p=st.lists(ptrs, min_size=4, max_size=4),
+       count=small, outs=st.lists(ptrs, min_size=16, max_size=16), out=ptrs, out_stride=ints)
+def test_fuzz_aggregate_and_partial_sums(lib, S, T, d, stride, dtype, p, count, outs, out, out_stride):
+    src, w, o, wts = p
+    assert B.lib().attnres_aggregate(src, S, T, d, stride, w, o, wts, 1e-5, dtype, None) in STATUSES
+    assert B.lib().attnres_partial_sums(_arr(outs), count, T, d, out, out_stride, dtype, None) in STATUSES
