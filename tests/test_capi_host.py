@@ -675,3 +675,46 @@ def test_fuzz_aggregate_and_partial_sums(lib, S, T, d, stride, dtype, p, count, 
     src, w, o, wts = p
     assert B.lib().attnres_aggregate(src, S, T, d, stride, w, o, wts, 1e-5, dtype, None) in STATUSES
     assert B.lib().attnres_partial_sums(_arr(outs), count, T, d, out, out_stride, dtype, None) in STATUSES
+
+
+STORE_FIELDS = ("base", "T", "slot_stride", "d", "s_max", "dtype", "n_completed", "partial_valid", "reserved")
+
+
+@no_gpu
+@FUZZ
+@given(base=ptrs, T=ints, stride=ints, d=ints, s_max=small, dtype=st.sampled_from([0, 1, 2]),
+       n_done=small, pv=st.integers(-1, 2), which=st.integers(0, 4), fin=st.integers(-1, 2), nb=small,
+       inter_stride=ints, p=st.lists(ptrs, min_size=6, max_size=6))
+def test_fuzz_store_calls(lib, base, T, stride, d, s_max, dtype, n_done, pv, which, fin, nb, inter_stride, p):
+    """Any store, including one no attnres_store_init would produce: each call
+    returns a documented status, and a rejected call leaves the store as it was."""
+    s = B.attnres_store_t(base=base, T=T, slot_stride=stride, d=d, s_max=s_max, dtype=dtype, n_completed=n_done,
+                          partial_valid=pv, reserved=0)
+    before = tuple(getattr(s, f) for f in STORE_FIELDS)
+    f, w, inter, lg, out, wts = p
+    ref = ctypes.byref(s)
+    if which == 0:
+        rc = B.lib().attnres_accumulate(ref, f, fin, None)
+    elif which == 1:
+        rc = B.lib().attnres_accumulate_aggregate(ref, f, fin, w, out, wts, 1e-5, None)
+    elif which == 2:
+        rc = B.lib().attnres_block_prepare(ref, f, fin, w, nb, inter, inter_stride, lg, wts, 1e-5, None)
+    elif which == 3:
+        rc = B.lib().attnres_block_merge(ref, f, w, inter, lg, out, wts, 1e-5, None)
+    else:
+        rc = B.lib().attnres_store_sources(ref)
+        assert rc in STATUSES | {B.ESTATE} or 1 <= rc <= 9
+        rc = B.OK
+    assert rc in STATUSES | {B.ESTATE}
+    if rc not in (B.OK, B.ELAUNCH):
+        assert tuple(getattr(s, f) for f in STORE_FIELDS) == before, "a rejected call changed the store"
+
+
+@no_gpu
+@FUZZ
+@given(n=st.sampled_from([-1, 0, 1, 4, 5, 16, 17, 1 << 20]), T=ints, d=ints, dtype=st.sampled_from([0, 1, 2]),
+       p=st.lists(ptrs, min_size=3, max_size=3))
+def test_fuzz_split_queries_and_add_rows(lib, n, T, d, dtype, p):
+    a, b, out = p
+    assert B.lib().attnres_split_queries(a, n, d, out, None) in STATUSES
+    assert B.lib().attnres_add_rows(a, b, out, T, d, dtype, None) in STATUSES
