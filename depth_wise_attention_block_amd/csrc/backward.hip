@@ -22,7 +22,10 @@
 // time, the next source's old rows loading while the current one is formed.
 // dL/dw is accumulated per lane over the workgroup's tokens and written as one
 // float32 row per workgroup; reduce_rows_kernel sums those rows in a fixed
-// order, so the result is deterministic for a given grid.
+// order, so the result is deterministic for a given grid.  A caller that forms
+// dL/dw itself gets every source's coefficients instead, and the grid is then
+// one workgroup per token (no loop, so no token's loads wait behind the
+// previous token's stores).
 //
 // Deferred sources (the inter-block sources every layer of a block shares)
 // leave their gradient rows alone: the layer writes their coefficients
@@ -30,7 +33,9 @@
 // applies all the block's layers at once, while block_dw_kernel (MFMA) adds
 // their share of each layer's dL/dw.  When every source but the last is
 // deferred, aggregate_backward_last_kernel streams the rows once and keeps
-// only the last.
+// only the last; the last source's (the partial sum's) share of dL/dw is then
+// either summed there or formed per block by partial_dw_kernel from the
+// coefficients.
 //
 // HBM bytes per token at S sources, bf16, all gradients accumulated:
 //   2 S d (sources) + 2 d (g) + 8 S d (old and new float32 gradients)
