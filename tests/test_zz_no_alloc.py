@@ -2,7 +2,9 @@
 (its dL/dw rows in the library's static device array) -- against
 attnres_aggregate_backward with a caller workspace, through the C ABI: two
 calls in a row, the second on a smaller batch (the array still holds the first
-call's rows), for the general kernel and the last-source streaming kernel."""
+call's rows), for the general kernel and the last-source streaming kernel; and
+with dL/dw left to the caller (grad_w NULL), where neither entry point needs
+scratch and both write every source's coefficients."""
 
 import numpy as np
 import pytest
@@ -18,9 +20,10 @@ pytestmark = pytest.mark.gpu
 def _call(static, H, w, g, grads, gw, gl, defer, coef, ws=None):
     S, T, d = grads.shape
     stream = torch.cuda.current_stream().cuda_stream
+    use_coef = defer or gw is None
     args = (H.data_ptr(), S, T, d, H.stride(0), None, w.data_ptr(), g.data_ptr(), grads.data_ptr(),
-            grads.stride(0), 0, defer, coef.data_ptr() if defer else None, coef.shape[1] if defer else 0,
-            gl.data_ptr() if gl is not None else None, gw.data_ptr())
+            grads.stride(0), 0, defer, coef.data_ptr() if use_coef else None, coef.shape[1] if use_coef else 0,
+            gl.data_ptr() if gl is not None else None, gw.data_ptr() if gw is not None else None)
     if static:
         rc = B.lib().attnres_aggregate_backward_static(*args, 1e-5, B.BF16, stream)
     else:
@@ -29,7 +32,7 @@ def _call(static, H, w, g, grads, gw, gl, defer, coef, ws=None):
     assert rc == B.OK, B.strerror(rc)
 
 
-def _case(T, S, d, defer, seed):
+def _case(T, S, d, defer, seed, form_dw=True):
     dev = device()
     H = synth.sources(S, T, d, scale=(0.5, 50.0), seed=seed, device=dev)
     w = synth.query(d, seed=seed + 1, device=dev)
@@ -37,13 +40,15 @@ def _case(T, S, d, defer, seed):
     outs = []
     for static in (False, True):
         grads = torch.full((S, T, d), 7.0, dtype=torch.float32, device=dev)
-        gw = torch.full((d,), 7.0, dtype=torch.float32, device=dev)
+        gw = torch.full((d,), 7.0, dtype=torch.float32, device=dev) if form_dw else None
         last_deferred = (defer >> (S - 1)) & 1
         gl = None if last_deferred else torch.zeros((T, d), dtype=torch.bfloat16, device=dev)
         coef = torch.zeros((T, 3 * S), dtype=torch.float32, device=dev)
         ws = None
-        if not static:
+        if not static and form_dw:
             ws = torch.empty(max(B.backward_workspace_bytes(T, d) // 4, 4), dtype=torch.float32, device=dev)
+        elif not static:
+            ws = torch.empty(4, dtype=torch.float32, device=dev)     # passed, and unused without grad_w
         _call(static, H, w, g, grads, gw, gl, defer, coef, ws)
         torch.cuda.synchronize()
         outs.append((grads, gw, gl, coef))
@@ -77,3 +82,19 @@ def test_static_backward_matches_the_workspace_entry_point(defer):
         else:   # a device with more workgroups than static rows: dL/dw summed over a capped grid
             scale = float(w0.abs().max())
             assert float((w0 - w1).abs().max()) <= 1e-5 * scale, f"T={T} dL/dw"
+
+
+@pytest.mark.parametrize("defer", [0, 0xFF], ids=["general", "last_source"])
+def test_static_backward_without_dw_matches_the_workspace_entry_point(defer):
+    """grad_w NULL: every gradient row, the handed-out gradient and every
+    source's coefficients bitwise equal between the two entry points, two
+    calls in a row, the second smaller."""
+    S, d = 9, 7168
+    for T, seed in ((4096, 3), (300, 4)):
+        note(f"no-alloc backward without dw defer={defer:#x} T={T}")
+        (g0, _, l0, c0), (g1, _, l1, c1) = _case(T, S, d, defer, seed, form_dw=False)
+        for k in range(S):
+            if not (defer >> k) & 1:
+                assert _same(g0[k], g1[k]), f"T={T} grad row {k}"
+        assert _same(l0, l1) and _same(c0, c1), f"T={T} handed-out gradient or coefficients"
+        assert not torch.isnan(c0).any() and bool((c0 != 0).any()), "coefficients not written"
