@@ -307,6 +307,12 @@ def aggregate_backward(sources: torch.Tensor, w: torch.Tensor, grad_out: torch.T
     mask = accumulate if isinstance(accumulate, int) else sum(1 << i for i, a in enumerate(accumulate) if a)
     if (defer or not form_dw) and (coef is None or coef.dtype != torch.float32 or coef.device != dev):
         raise ValueError("deferred sources (and form_dw=False) need a float32 coef buffer on the device")
+    if (defer or not form_dw) and T > 0:
+        # the kernel writes (T - 1) * coef_stride + 3 S floats from coef's first element at most
+        top = S if not form_dw else (defer & ((1 << S) - 1)).bit_length()
+        need = (T - 1) * int(coef_stride) + 3 * top
+        if not coef.is_contiguous() or coef.numel() < need:
+            raise ValueError(f"coef must be a contiguous float32 tensor of at least {need} elements")
     src_stride = sources.stride(0) if sources.shape[0] > 1 else T * d
     grad_stride = grad_sources.stride(0) if S > 1 else T * d
     src_ptr = sources.data_ptr() if sources.shape[0] > 0 else None
@@ -421,8 +427,13 @@ def partial_dw(rows, coef: torch.Tensor | None, coef_stride: int, coef_layer_str
     for w in grad_ws:
         if w.dtype != torch.float32 or not w.is_contiguous() or w.numel() != d:
             raise ValueError(f"each dL/dw row must be a contiguous float32 [d] tensor on {dev}")
-    if given and T > 0 and (coef is None or coef.dtype != torch.float32):
-        raise ValueError("rows need a float32 coef tensor")
+    if given and T > 0:
+        if coef is None or coef.dtype != torch.float32 or not coef.is_contiguous():
+            raise ValueError("rows need a contiguous float32 coef tensor")
+        # the last layer's coefficient of the last token, counted from coef's first element
+        need = (T - 1) * int(coef_stride) + (Bl - 1) * int(coef_layer_stride) + 1
+        if coef.numel() < need:
+            raise ValueError(f"coef must hold at least {need} elements")
     if workspace is None:
         nbytes = partial_dw_workspace_bytes(T, d, Bl, dt)
         workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=dev)

@@ -556,6 +556,9 @@ def _mixed_calls():
             H, [g0, g1], [w0, w1], cf, gs, [dw0, dw1], grad_last=gl, workspace=ws))
     add("split_queries", [mk(Bq, d, dtype=f32), mk(*B.prepared_query_shape(Bq, d))],
         lambda w, o: B.split_queries(w, o))
+    add("partial_dw", [mk(T, d), mk(T, d), mk(T * Bq * 3, dtype=f32), mk(d, dtype=f32), mk(d, dtype=f32),
+                       mk(64, dtype=f32)],
+        lambda r0, r1, cf, dw0, dw1, ws: B.partial_dw([r0, r1], cf, Bq * 3, 3, [dw0, dw1], workspace=ws))
 
     def store(slots):
         st = B.SourceStore(T, d, s_max=4, slots=slots)
@@ -584,6 +587,42 @@ def test_binding_refuses_one_host_tensor_among_gpu_tensors(monkeypatch, label, k
     monkeypatch.setattr(B, "lib", lambda: _HostOnlyLib(real))
     with pytest.raises(ValueError, match="GPU|must be on"):
         call()
+
+
+def test_binding_refuses_a_short_coefficient_buffer(monkeypatch):
+    """The kernels write (backward) or read (partial_dw) coefficients at
+    t * coef_stride + ... from the buffer's first element, which the C ABI
+    cannot bound: the binding refuses a buffer one element short, and lets
+    the exact size through to the library."""
+    import torch
+    real = B.lib()
+    monkeypatch.setattr(B, "lib", lambda: _HostOnlyLib(real))
+    S, T, d = 3, 4, 16
+
+    def g(*shape, dtype=torch.bfloat16):
+        return _OnGpu(torch.zeros(shape, dtype=dtype))
+
+    def bwd(n, defer, form_dw):
+        kw = dict(grad_w=g(d, dtype=torch.float32), workspace=g(64, dtype=torch.float32)) if form_dw else {}
+        B.aggregate_backward(g(S, T, d), g(d, dtype=torch.float32), g(T, d), g(S, T, d, dtype=torch.float32),
+                             defer=defer, coef=g(n, dtype=torch.float32), coef_stride=9, form_dw=form_dw, **kw)
+
+    # every source's triple without dL/dw; up to the highest deferred source's with it
+    for defer, form_dw, need in ((0b011, False, 3 * 9 + 9), (0b011, True, 3 * 9 + 6), (0b001, True, 3 * 9 + 3)):
+        with pytest.raises(ValueError, match="coef"):
+            bwd(need - 1, defer, form_dw)
+        with pytest.raises(AssertionError, match="was called"):
+            bwd(need, defer, form_dw)
+
+    def pdw(n):
+        B.partial_dw([None, g(T, d), g(T, d)], g(n, dtype=torch.float32), 9, 3,
+                     [g(d, dtype=torch.float32) for _ in range(3)], workspace=g(64, dtype=torch.float32))
+
+    need = 3 * 9 + 2 * 3 + 1
+    with pytest.raises(ValueError, match="coef"):
+        pdw(need - 1)
+    with pytest.raises(AssertionError, match="was called"):
+        pdw(need)
 
 
 def test_c_client_checks_its_input_before_any_gpu_call(tmp_path):
